@@ -1,0 +1,265 @@
+"""fp64 CPU oracle of the DSpark semi-autoregressive draft-proposal hot path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+and the benchmark's CPU-baseline leg may import this module.  It shares no
+code with the HIP library; it receives the same input arrays (from ``synth``)
+and computes every step from its plain definition, in float64, on the CPU.
+
+Sources (the pages), cited by title and section:
+  [P1] "Qwen3.8-Flash-Next DSpark 训练实验" (xpengzhao.github.io dl-note):
+       评估口径/离线指标 (overlap a_i, tau_prob, validity rules, top-16 rule),
+       Baseline 架构/Markov 顺序修正 (m_i, b_i, l_i, greedy),
+       Confidence head 与训练目标 (s_i, sigmoid).
+  [P4] "DSpark 论文精读：置信度调度推测解码、半自回归生成与大模型推理加速"
+       (zzqdeco.github.io): §2.2 (U = W_lm h, corrected logits U~_j, chain vs
+       parallel factorisation), §2.3 (teacher-forced vs sequential Markov),
+       §3.1 (alpha identity, prefix survival cumprod and its 0.85^6 example).
+  [P5] "DeepSpec 训练全流程详解（以 Qwen3 + DSpark 为例）" (wangjunjian.com):
+       §4.3 propose (compute_logits, sample_draft_tokens with the anchor as
+       first previous token, predict_confidence_step).
+  Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+       Easy as 1, 2, 3", SC'11 (the pages name no sampler).
+
+Readings where the pages are silent or disagree (each is listed in the design
+notes as well):
+  * the Markov bias is linear, b = Bm^T A[prev] ([P1] Markov 顺序修正); the
+    SiLU variant shown in [P4] §2.3 is not used;
+  * every slot, including slot 0, is biased; slot 0 uses the anchor as its
+    previous token ([P1] m_1 = W_1[D]; [P5] §4.3 first_prev_token_ids=anchor);
+  * ties in argmax and top-k go to the lowest vocabulary index;
+  * sampling is Gumbel-max with Philox4x32-10 words; see ``gumbel``;
+  * the confidence head is w_c.h + b_c, plus w_m.A[prev] when w_m is given
+    ([P1] s_i = w_c^T [h_i; m_i] + b_c); no calibration is applied;
+  * alpha is clamped to [0, 1] and set to 0 at invalid slots; a block with no
+    valid slot reports tau = 0 and is left out of the mean ([P1] 离线指标).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# inputs
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def to_f64(x: np.ndarray, wdtype: str) -> np.ndarray:
+    return widen_bf16(x) if wdtype == "bf16" else np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# S1: LM head.  [P4] §2.2: U_1..U_gamma = W_lm [h_1..h_gamma]; [P1] the frozen
+# LM head maps the final hidden states to full-vocabulary logits (no bias).
+
+
+def lm_head(h: np.ndarray, w_lm: np.ndarray) -> np.ndarray:
+    """U[m, v] = sum_k h[m, k] * w_lm[v, k]   (h [M,H], w_lm [V,H], float64)."""
+    return np.matmul(h, w_lm.T)
+
+
+# --------------------------------------------------------------------------
+# Philox4x32-10 (SC'11): a 10-round Feistel-like bijection of a 128-bit
+# counter under a 64-bit key.  Each round multiplies words 0 and 2 by the
+# round constants, and swaps and xors the high halves with the other words
+# and the key; the key is bumped by the Weyl constants between rounds.
+
+_MASK32 = np.uint64(0xFFFFFFFF)
+_PHILOX_M0 = np.uint64(0xD2511F53)
+_PHILOX_M1 = np.uint64(0xCD9E8D57)
+_PHILOX_W0 = np.uint64(0x9E3779B9)
+_PHILOX_W1 = np.uint64(0xBB67AE85)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Vectorised Philox4x32-10.  Arguments are arrays (or scalars) holding
+    32-bit values; returns the four 32-bit output words as uint64 arrays."""
+    c0, c1, c2, c3, k0, k1 = (np.asarray(x, dtype=np.uint64) & _MASK32
+                              for x in (c0, c1, c2, c3, k0, k1))
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + _PHILOX_W0) & _MASK32
+            k1 = (k1 + _PHILOX_W1) & _MASK32
+        p0 = _PHILOX_M0 * c0          # < 2^64: exact in uint64
+        p1 = _PHILOX_M1 * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _MASK32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _MASK32
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return c0, c1, c2, c3
+
+
+def philox_words(seed: int, offset: int, j: int, V: int) -> np.ndarray:
+    """The V random words of one (request, position): word v is output word
+    (v mod 4) of Philox4x32-10 with key (lo32(seed), hi32(seed)) and counter
+    (v div 4, j, lo32(offset), hi32(offset))."""
+    n4 = (V + 3) // 4
+    ctr = np.arange(n4, dtype=np.uint64)
+    s, o = int(seed), int(offset)
+    w = philox4x32_10(ctr, j, o & 0xFFFFFFFF, (o >> 32) & 0xFFFFFFFF,
+                      s & 0xFFFFFFFF, (s >> 32) & 0xFFFFFFFF)
+    return np.stack(w, axis=1).reshape(-1)[:V]
+
+
+def gumbel(seed: int, offset: int, j: int, V: int) -> np.ndarray:
+    """Standard Gumbel noise G = -log(-log u), u = (floor(w / 2^9) + 1/2) 2^-23.
+
+    u uses the top 23 bits of the word, lies in (0, 1) and is exact in both
+    binary32 and binary64, so both sides start from the same u."""
+    w = philox_words(seed, offset, j, V)
+    u = ((w >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23
+    return -np.log(-np.log(u))
+
+
+# --------------------------------------------------------------------------
+# S2-S4: the sequential Vanilla-Markov stage.
+# [P1] Markov 顺序修正: m_i = W_1[t_{i-1}] (t_0 = anchor), b_i = W_2 m_i,
+# l_i = l_i^0 + b_i, q_i = softmax(l_i); inference selects t_i from l_i and
+# feeds it to position i+1.  [P4] §2.2: x_j ~ softmax(U~_j), U~_j = U_j + b.
+
+
+def markov_chain(U: np.ndarray, anchor: np.ndarray, A: np.ndarray, Bm: np.ndarray, *,
+                 temperature: float = 0.0, seeds: Optional[np.ndarray] = None,
+                 offset: int = 0, topk: int = 0, forced: Optional[np.ndarray] = None,
+                 keep_logits: bool = False) -> dict:
+    """Run the chain for every request.
+
+    U [B, gamma, V] base logits; anchor [B]; A [V, r]; Bm [r, V] (all float64).
+    temperature 0 selects greedily; otherwise token = argmax(U~/T + G).
+    ``forced`` [B, gamma] (int, -1 = free) overrides the selected token at a
+    position (used to continue a chain along another valid choice).
+
+    Returns tokens [B,gamma], tok_logit (U~ at the token), lse (log-sum-exp of
+    U~), gap (best minus second-best of the selection score), argmax (the
+    oracle's own choice), optionally top-k indices/probabilities (softmax of
+    U~ over the k largest, ties to the lower index) and U~ itself.
+    """
+    B, gamma, V = U.shape
+    out = {k: np.zeros((B, gamma), dtype=np.float64) for k in ("tok_logit", "lse", "gap")}
+    out["tokens"] = np.zeros((B, gamma), dtype=np.int64)
+    out["argmax"] = np.zeros((B, gamma), dtype=np.int64)
+    if topk:
+        out["topk_idx"] = np.zeros((B, gamma, topk), dtype=np.int64)
+        out["topk_prob"] = np.zeros((B, gamma, topk), dtype=np.float64)
+    if keep_logits:
+        out["logits"] = np.zeros((B, gamma, V), dtype=np.float64)
+    for b in range(B):
+        prev = int(anchor[b])
+        for j in range(gamma):
+            ut = U[b, j] + A[prev] @ Bm                     # U~_j = U_j + W_2 W_1[prev]
+            mx = ut.max()
+            out["lse"][b, j] = mx + math.log(np.exp(ut - mx).sum())
+            if temperature == 0.0:
+                score = ut
+            else:
+                score = ut / temperature + gumbel(int(seeds[b]), offset, j, V)
+            x = int(np.argmax(score))                       # first maximum = lowest index
+            rest = np.delete(score, x)
+            out["gap"][b, j] = score[x] - rest.max() if rest.size else np.inf
+            out["argmax"][b, j] = x
+            if forced is not None and forced[b, j] >= 0:
+                x = int(forced[b, j])
+            out["tokens"][b, j] = x
+            out["tok_logit"][b, j] = ut[x]
+            if topk:
+                idx = topk_indices(ut, topk)
+                out["topk_idx"][b, j] = idx
+                e = np.exp(ut[idx] - ut[idx[0]])
+                out["topk_prob"][b, j] = e / e.sum()
+            if keep_logits:
+                out["logits"][b, j] = ut
+            prev = x
+    return out
+
+
+def topk_indices(x: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest entries, by value descending, ties to the
+    lower index."""
+    thr = np.partition(x, x.size - k)[x.size - k]
+    cand = np.nonzero(x >= thr)[0]
+    order = np.lexsort((cand, -x[cand]))
+    return cand[order[:k]]
+
+
+def teacher_forced_logits(U: np.ndarray, prev_tokens: np.ndarray, A: np.ndarray,
+                          Bm: np.ndarray) -> np.ndarray:
+    """All positions at once from known previous tokens ([P4] §2.3: training
+    applies the Markov bias to the whole block in one batched step).
+    prev_tokens [B, gamma] = [anchor, t_0, ..., t_{gamma-2}]."""
+    return U + np.einsum("bjr,rv->bjv", A[prev_tokens], Bm)
+
+
+# --------------------------------------------------------------------------
+# S5: confidence head and prefix survival.
+# [P1] s_i = w_c^T [h_i; m_i] + b_c, a^_i = sigma(s_i); [P4] §3.1 prefix
+# survival a_{r,j} = prod_{i<=j} c_{r,i}.
+
+
+def confidence_survival(h: np.ndarray, w_c: np.ndarray, b_c: float, *,
+                        w_m: Optional[np.ndarray] = None, A: Optional[np.ndarray] = None,
+                        anchor: Optional[np.ndarray] = None,
+                        tokens: Optional[np.ndarray] = None):
+    """h [B, gamma, H] -> (conf, survival) [B, gamma]."""
+    s = h @ w_c + b_c
+    if w_m is not None:
+        prev = np.concatenate([anchor[:, None], tokens[:, :-1]], axis=1)
+        s = s + A[prev] @ w_m
+    conf = 1.0 / (1.0 + np.exp(-s))
+    surv = np.empty_like(conf)
+    run = np.ones(conf.shape[0])
+    for j in range(conf.shape[1]):
+        run = run * conf[:, j]
+        surv[:, j] = run
+    return conf, surv
+
+
+# --------------------------------------------------------------------------
+# S6: overlap and probabilistic acceptance length.
+# [P1] 离线指标: a_i = sum_v min(p_i(v), q_i(v)) = 1 - ||p_i - q_i||_1 / 2;
+# tau_prob = 1 + sum_{i=0}^{6} prod_{j<=i} a_j per valid block; invalid
+# slots get a_i = 0; accept_rate@i is aggregated over valid tokens.
+
+
+def softmax(x: np.ndarray) -> np.ndarray:
+    m = x.max(axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def overlap_dense(teacher: np.ndarray, draft: np.ndarray):
+    """Row-wise (sum min(p, q), sum |p - q|) for p = softmax(teacher),
+    q = softmax(draft)."""
+    p, q = softmax(teacher), softmax(draft)
+    return np.minimum(p, q).sum(axis=-1), np.abs(p - q).sum(axis=-1)
+
+
+def overlap_sparse(teacher: np.ndarray, idx: np.ndarray, prob: np.ndarray) -> np.ndarray:
+    """sum_v min(p(v), q'(v)) where q' is zero outside the candidate set
+    ([P1]: the teacher keeps its full-vocabulary probabilities)."""
+    p = softmax(teacher)
+    pc = np.take_along_axis(p, idx.astype(np.int64), axis=-1)
+    return np.minimum(pc, prob).sum(axis=-1)
+
+
+def tau_metrics(alpha: np.ndarray, valid: Optional[np.ndarray] = None):
+    """alpha [N, gamma] raw overlaps -> (alpha_used, tau [N], accept_rate [gamma],
+    tau_mean)."""
+    N, gamma = alpha.shape
+    v = np.ones((N, gamma), dtype=bool) if valid is None else valid.astype(bool)
+    a = np.where(v, np.clip(alpha, 0.0, 1.0), 0.0)
+    tau = np.ones(N)
+    run = np.ones(N)
+    for i in range(gamma):
+        run = run * a[:, i]
+        tau = tau + run
+    has = v.any(axis=1)
+    tau = np.where(has, tau, 0.0)
+    cnt = v.sum(axis=0)
+    acc = np.where(cnt > 0, (a * v).sum(axis=0) / np.maximum(cnt, 1), 0.0)
+    tau_mean = float(tau[has].mean()) if has.any() else 0.0
+    return a, tau, acc, tau_mean
