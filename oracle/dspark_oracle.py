@@ -135,12 +135,14 @@ def markov_chain(U: np.ndarray, anchor: np.ndarray, A: np.ndarray, Bm: np.ndarra
     position (used to continue a chain along another valid choice).
 
     Returns tokens [B,gamma], tok_logit (U~ at the token), lse (log-sum-exp of
-    U~), gap (best minus second-best of the selection score), argmax (the
-    oracle's own choice), optionally top-k indices/probabilities (softmax of
+    U~), gap (best minus second-best of the selection score), score_max and
+    score_tok (the selection score's maximum and its value at the token),
+    argmax (the oracle's own choice), optionally top-k indices/probabilities (softmax of
     U~ over the k largest, ties to the lower index) and U~ itself.
     """
     B, gamma, V = U.shape
-    out = {k: np.zeros((B, gamma), dtype=np.float64) for k in ("tok_logit", "lse", "gap")}
+    out = {k: np.zeros((B, gamma), dtype=np.float64)
+           for k in ("tok_logit", "lse", "gap", "score_max", "score_tok")}
     out["tokens"] = np.zeros((B, gamma), dtype=np.int64)
     out["argmax"] = np.zeros((B, gamma), dtype=np.int64)
     if topk:
@@ -166,6 +168,8 @@ def markov_chain(U: np.ndarray, anchor: np.ndarray, A: np.ndarray, Bm: np.ndarra
                 x = int(forced[b, j])
             out["tokens"][b, j] = x
             out["tok_logit"][b, j] = ut[x]
+            out["score_max"][b, j] = score.max()
+            out["score_tok"][b, j] = score[x]
             if topk:
                 idx = topk_indices(ut, topk)
                 out["topk_idx"][b, j] = idx
