@@ -1,0 +1,203 @@
+/*
+ * dspark.h -- C ABI of the DSpark semi-autoregressive draft-proposal hot path
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * One block per request holds gamma slots: the anchor slot plus gamma-1 MASK
+ * slots, each predicting one draft token.  The library runs, per block:
+ *   S1  the LM-head contraction U = h . W_lm^T over the full vocabulary;
+ *   S2+ the sequential Vanilla-Markov stage: U~_j = U_j + A[x_{j-1}] . Bm with
+ *   S3  x_{-1} = anchor, then greedy argmax or Gumbel-max sampling of x_j;
+ *   S4  optionally the k largest U~_j with their softmax (candidate set);
+ *   S5  the confidence head c_j = sigmoid(w_c.h_j [+ w_m.A[x_{j-1}]] + b_c)
+ *       and the prefix survival a_j = prod_{i<=j} c_i;
+ *   S6  the offline overlap alpha_j = sum_v min(p_j, q_j) against a teacher
+ *       distribution and tau_prob = 1 + sum_i prod_{j<=i} alpha_j.
+ *
+ * Sources, cited by page title and section:
+ *   [P1] "Qwen3.8-Flash-Next DSpark 训练实验" (xpengzhao.github.io):
+ *        评估口径/离线指标; Baseline 架构/Markov 顺序修正; Confidence head.
+ *   [P4] "DSpark 论文精读：置信度调度推测解码、半自回归生成与大模型推理加速"
+ *        (zzqdeco.github.io): §2.2, §2.3, §3.1.
+ *   [P5] "DeepSpec 训练全流程详解（以 Qwen3 + DSpark 为例）"
+ *        (wangjunjian.com): §4.3 propose.
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Scratch memory comes only from the
+ *     caller's workspace argument, sized by the matching *_workspace query.
+ *   - Layouts are dense row-major.  Request-major rows: m = b*gamma + j.
+ *   - Every call only enqueues work on `stream` and returns; results are valid
+ *     once the caller synchronises that stream.  No call synchronises.
+ *   - Calls are stateless and thread-safe; results are bit-identical from run
+ *     to run (all reductions have a fixed order; no floating-point atomics).
+ *   - Errors are returned as a status; no exception crosses the ABI.  All
+ *     argument checks run on the host BEFORE any device work is enqueued, so
+ *     an invalid call leaves the stream untouched.  dspark_last_error() gives
+ *     a message for the last non-OK status of the calling thread.
+ *   - Token and anchor ids must lie in [0, V); this is the caller's contract
+ *     and is not checked on the device.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = 1,       /* NULL where required, non-positive or too large size, inconsistent pointers */
+  DSPARK_EUNSUPPORTED = 2, /* valid but not implemented: a dtype, an alignment, gamma > 16, topk > 32 ... */
+  DSPARK_EWORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace query returned */
+  DSPARK_EHIP = 4          /* a HIP launch failed; dspark_last_error() has the HIP error string */
+} dspark_status_t;
+
+typedef enum {
+  DSPARK_F32 = 0,  /* IEEE binary32 */
+  DSPARK_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} dspark_dtype_t;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* Library version string, e.g. "dspark-mi355x 0.1.0 gfx950". */
+const char* dspark_version(void);
+
+/*
+ * S1 -- LM head.  [P4] §2.2 (U_1..U_gamma = W_lm [h_1..h_gamma]); [P1] the
+ * frozen LM head maps the final draft hidden states to full-vocabulary logits;
+ * [P5] §4.3 compute_logits(block_hidden).  No bias, no scaling.
+ *
+ *   h     [M, H]  dtype dt   final hidden states, row m = b*gamma + j
+ *   w_lm  [V, H]  dtype dt   LM-head weight (nn.Linear layout)
+ *   U     [M, V]  float32    output, U[m, v] = sum_k h[m, k] * w_lm[v, k],
+ *                            accumulated in float32
+ * Requirements: M, H, V > 0; V <= 2^31 - 1; M*V <= 2^40.  For DSPARK_BF16:
+ * H % 8 == 0 and V % 8 == 0 (16-byte rows), else EUNSUPPORTED.
+ */
+dspark_status_t dspark_lm_head(const void* h, const void* w_lm, dspark_dtype_t dt,
+                               int64_t M, int64_t H, int64_t V, float* U,
+                               hipStream_t stream);
+
+/*
+ * Workspace size (bytes) needed by dspark_markov_propose for these sizes.
+ */
+dspark_status_t dspark_markov_propose_workspace(int64_t B, int64_t gamma, int64_t V,
+                                                int32_t topk, size_t* bytes);
+
+/*
+ * S2-S4 -- sequential Vanilla-Markov proposal.  [P1] Markov 顺序修正:
+ * m_i = W_1[t_{i-1}], b_i = W_2 m_i, l_i = l_i^0 + b_i, with t_0 the anchor;
+ * inference selects each token from l_i and feeds it to the next position.
+ * [P4] §2.2: U~_j = U_j + b(x_{j-1}), x_j ~ softmax(U~_j).  [P5] §4.3:
+ * sample_draft_tokens(base_logits, first_prev_token_ids = anchor).
+ * Here W_1 = A (an embedding table) and W_2 m = m . Bm.
+ *
+ *   U          [B, gamma, V] float32   base logits (output of dspark_lm_head)
+ *   anchor     [B]   int32             previous token of slot 0
+ *   A          [V, r] dtype wdt        Markov down table W_1
+ *   Bm         [r, V] dtype wdt        Markov up projection W_2 (r x V, row-major)
+ *   temperature  0: greedy, x_j = argmax_v U~_j[v] (ties: lowest v).
+ *                > 0: x_j = argmax_v (U~_j[v] / T + G[b, j, v]) (Gumbel-max),
+ *                G = -log(-log u), u = (floor(w / 2^9) + 1/2) * 2^-23 where w is
+ *                output word (v mod 4) of Philox4x32-10 (Salmon et al., SC'11)
+ *                with key (lo32(seeds[b]), hi32(seeds[b])) and counter
+ *                (v div 4, j, lo32(offset), hi32(offset)).
+ *   seeds      [B]   uint64            per-request Philox keys (NULL iff T == 0)
+ *   offset     Philox counter offset (e.g. the decoding round)
+ *   topk       0 .. 32: also return the topk largest U~_j (value descending,
+ *              ties to the lower index) and their softmax over that set.
+ * Outputs:
+ *   tokens     [B, gamma] int32        drafted tokens
+ *   tok_logit  [B, gamma] float32      U~_j at the drafted token (may be NULL)
+ *   lse        [B, gamma] float32      log sum_v exp U~_j[v] (may be NULL);
+ *                                      exp(tok_logit - lse) is q_j(x_j) at T = 1
+ *   topk_idx   [B, gamma, topk] int32  candidate ids (NULL iff topk == 0)
+ *   topk_prob  [B, gamma, topk] float32 softmax of U~ over the candidates
+ *   logits_out [B, gamma, V] float32   U~ itself (may be NULL; costs B*gamma*V*4
+ *                                      bytes of extra writes)
+ *   ws, ws_bytes  workspace of at least dspark_markov_propose_workspace() bytes
+ * Requirements: B, gamma, V, r > 0; gamma <= 16; topk <= 32 and topk <= V;
+ * V <= 2^31 - 1.  DSPARK_BF16: r % 32 == 0, r <= 1024, V % 8 == 0.
+ * DSPARK_F32: r <= 1024.  Otherwise EUNSUPPORTED.  T must be finite and >= 0.
+ */
+dspark_status_t dspark_markov_propose(const float* U, int64_t B, int64_t gamma, int64_t V,
+                                      const int32_t* anchor, const void* A, const void* Bm,
+                                      dspark_dtype_t wdt, int64_t r,
+                                      float temperature, const uint64_t* seeds, uint64_t offset,
+                                      int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
+                                      int32_t* topk_idx, float* topk_prob, float* logits_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * S5 -- confidence head and prefix survival.  [P1] Confidence head:
+ * s_i = w_c^T [h_i; m_i] + b_c, a^_i = sigmoid(s_i), m_i = W_1[t_{i-1}];
+ * [P5] §4.3 predict_confidence_step(block_hidden) (hidden states only);
+ * [P4] §3.1 prefix survival a_{r,j} = prod_{i<=j} c_{r,i}.
+ *
+ *   h         [B, gamma, H] dtype dt   final hidden states
+ *   w_c       [H] dtype dt, b_c        linear head H -> 1
+ *   w_m       [r] dtype dt or NULL     weight of the Markov state m_j = A[x_{j-1}];
+ *                                      NULL gives the hidden-only head
+ *   A         [V, r] dtype dt          Markov table (ignored when w_m == NULL)
+ *   anchor    [B] int32, tokens [B, gamma] int32   previous tokens (ignored
+ *                                      when w_m == NULL; may then be NULL)
+ *   conf      [B, gamma] float32       c_j = sigmoid(s_j)
+ *   survival  [B, gamma] float32       a_j = prod_{i<=j} c_i
+ * Requirements: B, gamma, H > 0; gamma <= 16; with w_m: r > 0, A, anchor and
+ * tokens non-NULL.
+ */
+dspark_status_t dspark_confidence_survival(const void* h, dspark_dtype_t dt,
+                                           int64_t B, int64_t gamma, int64_t H,
+                                           const void* w_c, float b_c, const void* w_m,
+                                           const void* A, int64_t r,
+                                           const int32_t* anchor, const int32_t* tokens,
+                                           float* conf, float* survival, hipStream_t stream);
+
+/*
+ * Workspace size (bytes) needed by dspark_overlap_tau for these sizes.
+ */
+dspark_status_t dspark_overlap_tau_workspace(int64_t N, int64_t gamma, int64_t V, size_t* bytes);
+
+/*
+ * S6 -- overlap and probabilistic acceptance length.  [P1] 离线指标:
+ * a_i = sum_v min(p_i(v), q_i(v)) = 1 - ||p_i - q_i||_1 / 2;
+ * tau_prob = 1 + sum_{i=0}^{gamma-1} prod_{j<=i} a_j per valid block; slots that
+ * are not valid get a_i = 0; accept_rate@i is aggregated over valid slots;
+ * for the candidate-set evaluation the draft is the softmax over the candidates
+ * (zero elsewhere) while the teacher keeps its full-vocabulary softmax.
+ * [P4] §3.1 and the clamp to [0, 1] of its loss code.
+ *
+ *   teacher    [N, gamma, V] float32   teacher logits, p = softmax(teacher)
+ *   draft      [N, gamma, V] float32   draft logits, q = softmax(draft)  -- dense mode
+ *              or NULL                 -- candidate mode, then:
+ *   cand_idx   [N, gamma, k] int32     candidate ids (distinct, in [0, V))
+ *   cand_prob  [N, gamma, k] float32   q' on the candidates
+ *   k          candidate count (0 in dense mode)
+ *   valid      [N, gamma] uint8 or NULL (all valid)
+ * Outputs:
+ *   alpha          [N, gamma] float32  clamp(sum_v min(p, q), 0, 1), 0 where invalid
+ *   tau            [N] float32         tau_prob; 0 for a block with no valid slot
+ *   accept_rate_at [gamma] float64 or NULL   sum valid*alpha / sum valid (0 if none)
+ *   tau_mean       [1] float64 or NULL       mean tau over blocks with a valid slot
+ *   ws, ws_bytes   workspace of at least dspark_overlap_tau_workspace() bytes
+ * Requirements: N, gamma, V > 0; gamma <= 16; V % 4 == 0 (16-byte rows);
+ * dense mode: k == 0 and cand_* NULL; candidate mode: 1 <= k <= 64 and cand_*
+ * non-NULL.
+ */
+dspark_status_t dspark_overlap_tau(const float* teacher, const float* draft,
+                                   const int32_t* cand_idx, const float* cand_prob, int32_t k,
+                                   const uint8_t* valid, int64_t N, int64_t gamma, int64_t V,
+                                   float* alpha, float* tau, double* accept_rate_at,
+                                   double* tau_mean, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

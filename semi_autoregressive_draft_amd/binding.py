@@ -1,0 +1,167 @@
+"""ctypes binding of libdspark.so: the C-ABI entry points under the same names.
+
+Argument marshalling only: tensors become device pointers and sizes, the
+stream is torch's current HIP stream, and a non-OK status raises DsparkError.
+Every computation runs in the library's HIP kernels; there is no fallback, and
+loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdspark.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "dspark.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
+F32, BF16 = 0, 1
+
+_vp, _i64, _i32, _f32, _u64, _sz = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_uint64, C.c_size_t
+
+_SIGNATURES = {
+    "dspark_last_error": (C.c_char_p, []),
+    "dspark_version": (C.c_char_p, []),
+    "dspark_lm_head": (C.c_int, [_vp, _vp, C.c_int, _i64, _i64, _i64, _vp, _vp]),
+    "dspark_markov_propose_workspace": (C.c_int, [_i64, _i64, _i64, _i32, C.POINTER(_sz)]),
+    "dspark_markov_propose": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64,
+                                        _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]),
+    "dspark_confidence_survival": (C.c_int, [_vp, C.c_int, _i64, _i64, _i64, _vp, _f32, _vp, _vp,
+                                             _i64, _vp, _vp, _vp, _vp, _vp]),
+    "dspark_overlap_tau_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
+    "dspark_overlap_tau": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp,
+                                     _vp, _vp, _vp, _sz, _vp]),
+}
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+_LIB: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    """The loaded library (raises if it was never built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m semi_autoregressive_draft_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _LIB = L
+    return _LIB
+
+
+def header_symbols() -> list:
+    """Entry points declared in include/dspark.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(dspark_[a-z_0-9]+)\s*\(", text)))
+
+
+def last_error() -> str:
+    return lib().dspark_last_error().decode()
+
+
+def version() -> str:
+    return lib().dspark_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise DsparkError(status, last_error())
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("dspark: tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"dspark: unsupported dtype {t.dtype}")
+
+
+def dspark_lm_head(h, w_lm, U, stream=None) -> None:
+    """U[M, V] = h[M, H] . w_lm[V, H]^T (float32 out)."""
+    M, H = h.shape
+    V = w_lm.shape[0]
+    _check(lib().dspark_lm_head(_ptr(h), _ptr(w_lm), _dtype(h), M, H, V, _ptr(U), _stream(stream)))
+
+
+def dspark_markov_propose_workspace(B: int, gamma: int, V: int, topk: int = 0) -> int:
+    n = _sz(0)
+    _check(lib().dspark_markov_propose_workspace(B, gamma, V, topk, C.byref(n)))
+    return n.value
+
+
+def dspark_markov_propose(U, anchor, A, Bm, tokens, *, temperature: float = 0.0, seeds=None,
+                          offset: int = 0, topk: int = 0, tok_logit=None, lse=None, topk_idx=None,
+                          topk_prob=None, logits_out=None, ws=None, stream=None) -> None:
+    """Sequential Markov proposal over U [B, gamma, V]; writes tokens [B, gamma]."""
+    import torch
+    B, gamma, V = U.shape
+    r = A.shape[1]
+    if ws is None:
+        ws = torch.empty(dspark_markov_propose_workspace(B, gamma, V, topk), dtype=torch.uint8,
+                         device=U.device)
+    _check(lib().dspark_markov_propose(
+        _ptr(U), B, gamma, V, _ptr(anchor), _ptr(A), _ptr(Bm), _dtype(A), r, float(temperature),
+        _ptr(seeds), int(offset), int(topk), _ptr(tokens), _ptr(tok_logit), _ptr(lse),
+        _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dspark_confidence_survival(h, w_c, b_c: float, conf, survival, *, w_m=None, A=None,
+                               anchor=None, tokens=None, stream=None) -> None:
+    """conf/survival [B, gamma] from h [B, gamma, H]."""
+    B, gamma, H = h.shape
+    r = A.shape[1] if (w_m is not None and A is not None) else 0
+    _check(lib().dspark_confidence_survival(
+        _ptr(h), _dtype(h), B, gamma, H, _ptr(w_c), float(b_c), _ptr(w_m), _ptr(A), r,
+        _ptr(anchor), _ptr(tokens), _ptr(conf), _ptr(survival), _stream(stream)))
+
+
+def dspark_overlap_tau_workspace(N: int, gamma: int, V: int) -> int:
+    n = _sz(0)
+    _check(lib().dspark_overlap_tau_workspace(N, gamma, V, C.byref(n)))
+    return n.value
+
+
+def dspark_overlap_tau(teacher, alpha, tau, *, draft=None, cand_idx=None, cand_prob=None,
+                       valid=None, accept_rate_at=None, tau_mean=None, ws=None, stream=None) -> None:
+    """alpha [N, gamma], tau [N] (+ aggregates) from teacher [N, gamma, V]."""
+    import torch
+    N, gamma, V = teacher.shape
+    k = 0 if cand_idx is None else cand_idx.shape[-1]
+    if ws is None:
+        ws = torch.empty(dspark_overlap_tau_workspace(N, gamma, V), dtype=torch.uint8,
+                         device=teacher.device)
+    _check(lib().dspark_overlap_tau(
+        _ptr(teacher), _ptr(draft), _ptr(cand_idx), _ptr(cand_prob), k, _ptr(valid), N, gamma, V,
+        _ptr(alpha), _ptr(tau), _ptr(accept_rate_at), _ptr(tau_mean), _ptr(ws), ws.numel(),
+        _stream(stream)))

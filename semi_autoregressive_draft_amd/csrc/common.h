@@ -1,0 +1,103 @@
+// Device helpers shared by the DSpark hot-path kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+
+// Reinterpret four packed dwords (8 bf16) as an MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// -------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; each round
+// multiplies words 0 and 2 by the round constants, exchanges the halves of
+// the products with the other words and xors in the key, which is bumped by
+// the Weyl constants between rounds.
+struct Philox4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    const uint32_t hi0 = __umulhi(M0, c0), lo0 = M0 * c0;
+    const uint32_t hi1 = __umulhi(M1, c2), lo1 = M1 * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += W0; k1 += W1;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// Standard Gumbel noise from one 32-bit word: u = (w >> 9 + 1/2) 2^-23 lies in
+// (0, 1) and is exact in binary32; -log u is taken through log1p near 1 so
+// that its relative error stays at a few ulp, then G = -log(-log u).
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  const float u = (static_cast<float>(w >> 9) + 0.5f) * 0x1p-23f;
+  const float y = (u >= 0.5f) ? -log1pf(u - 1.0f) : -logf(u);
+  return -logf(y);
+}
+
+// -------------------------------------------------------------------------
+// Online log-sum-exp and argmax states, merged in a fixed order.
+struct LseState { float m, s; };  // value max, sum of exp(x - m)
+
+__device__ __forceinline__ LseState lse_merge(LseState a, LseState b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == kNegInf) return {kNegInf, 0.0f};
+  const float sa = (a.m == kNegInf) ? 0.0f : a.s * __expf(a.m - m);
+  const float sb = (b.m == kNegInf) ? 0.0f : b.s * __expf(b.m - m);
+  return {m, sa + sb};
+}
+
+struct ArgState { float score; int idx; float x; };  // best score, its index, U~ there
+
+__device__ __forceinline__ ArgState arg_merge(ArgState a, ArgState b) {
+  const bool take_b = (b.score > a.score) || (b.score == a.score && b.idx < a.idx);
+  return take_b ? b : a;
+}
+
+__device__ __forceinline__ LseState shfl_xor(LseState v, int mask) {
+  return {__shfl_xor(v.m, mask), __shfl_xor(v.s, mask)};
+}
+__device__ __forceinline__ ArgState shfl_xor(ArgState v, int mask) {
+  return {__shfl_xor(v.score, mask), __shfl_xor(v.idx, mask), __shfl_xor(v.x, mask)};
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace dspark

@@ -1,0 +1,233 @@
+// C ABI of the DSpark draft-proposal hot path: argument checks, workspace
+// carving and kernel dispatch.  Every check runs before anything is enqueued.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "dspark.h"
+#include "internal.h"
+
+using namespace dspark;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dspark_status_t fail(dspark_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dspark_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSPARK_OK;
+  return fail(DSPARK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+constexpr int64_t kI32Max = 2147483647;
+
+size_t markov_ws_bytes(int64_t B, int64_t V, int32_t topk) {
+  const size_t P = markov_partials(V);
+  size_t s = 5 * align_up(static_cast<size_t>(B) * P * 4);
+  if (topk > 0) s += align_up(static_cast<size_t>(B) * markov_segments(V) * 4);
+  return s;
+}
+
+size_t overlap_ws_bytes(int64_t N, int64_t gamma) {
+  return align_up(static_cast<size_t>(overlap_tau_blocks(N)) * (2 * gamma + 2) * sizeof(double));
+}
+
+}  // namespace
+
+extern "C" const char* dspark_last_error(void) { return g_err; }
+
+extern "C" const char* dspark_version(void) { return "dspark-mi355x 0.1.0 gfx950"; }
+
+// ---------------------------------------------------------------------------
+extern "C" dspark_status_t dspark_lm_head(const void* h, const void* w_lm, dspark_dtype_t dt,
+                                          int64_t M, int64_t H, int64_t V, float* U,
+                                          hipStream_t stream) {
+  if (!h || !w_lm || !U) return fail(DSPARK_EINVAL, "dspark_lm_head: h, w_lm and U must be non-NULL");
+  if (M <= 0 || H <= 0 || V <= 0) return fail(DSPARK_EINVAL, "dspark_lm_head: M, H, V must be positive");
+  if (V > kI32Max || H > kI32Max || M > kI32Max || M * V > (int64_t(1) << 40))
+    return fail(DSPARK_EINVAL, "dspark_lm_head: sizes too large (M=%lld H=%lld V=%lld)",
+                (long long)M, (long long)H, (long long)V);
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "dspark_lm_head: unknown dtype %d", (int)dt);
+  const bool bf16 = dt == DSPARK_BF16;
+  if (bf16) {
+    if (H % 8 || V % 8) return fail(DSPARK_EUNSUPPORTED, "dspark_lm_head: bf16 needs H %% 8 == 0 and V %% 8 == 0");
+    if (!aligned16(h) || !aligned16(w_lm) || !aligned16(U))
+      return fail(DSPARK_EUNSUPPORTED, "dspark_lm_head: bf16 operands must be 16-byte aligned");
+    if ((M + 127) / 128 > 65535) return fail(DSPARK_EINVAL, "dspark_lm_head: M too large");
+  } else if ((M + 63) / 64 > 65535) {
+    return fail(DSPARK_EINVAL, "dspark_lm_head: M too large");
+  }
+  return hip_status(launch_lm_head(h, w_lm, bf16, M, H, V, U, stream), "dspark_lm_head");
+}
+
+// ---------------------------------------------------------------------------
+extern "C" dspark_status_t dspark_markov_propose_workspace(int64_t B, int64_t gamma, int64_t V,
+                                                           int32_t topk, size_t* bytes) {
+  if (!bytes) return fail(DSPARK_EINVAL, "dspark_markov_propose_workspace: bytes is NULL");
+  if (B <= 0 || gamma <= 0 || V <= 0 || topk < 0)
+    return fail(DSPARK_EINVAL, "dspark_markov_propose_workspace: B, gamma, V must be positive, topk >= 0");
+  if (V > kI32Max || B > kI32Max) return fail(DSPARK_EINVAL, "dspark_markov_propose_workspace: sizes too large");
+  *bytes = markov_ws_bytes(B, V, topk);
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status_t dspark_markov_propose(
+    const float* U, int64_t B, int64_t gamma, int64_t V, const int32_t* anchor, const void* A,
+    const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
+    uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
+    int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
+    hipStream_t stream) {
+  const char* fn = "dspark_markov_propose";
+  if (!U || !anchor || !A || !Bm || !tokens)
+    return fail(DSPARK_EINVAL, "%s: U, anchor, A, Bm and tokens must be non-NULL", fn);
+  if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0)
+    return fail(DSPARK_EINVAL, "%s: B, gamma, V, r must be positive", fn);
+  if (V > kI32Max || B > kI32Max / 16 || B * gamma > kI32Max)
+    return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  if (!std::isfinite(temperature) || temperature < 0.0f)
+    return fail(DSPARK_EINVAL, "%s: temperature must be finite and >= 0", fn);
+  if (temperature > 0.0f && !seeds) return fail(DSPARK_EINVAL, "%s: sampling (T > 0) needs seeds", fn);
+  if (topk < 0) return fail(DSPARK_EINVAL, "%s: topk must be >= 0", fn);
+  if (topk > 0 && (!topk_idx || !topk_prob))
+    return fail(DSPARK_EINVAL, "%s: topk > 0 needs topk_idx and topk_prob", fn);
+  if (topk == 0 && (topk_idx || topk_prob))
+    return fail(DSPARK_EINVAL, "%s: topk_idx/topk_prob must be NULL when topk == 0", fn);
+  if (topk > V) return fail(DSPARK_EINVAL, "%s: topk > V", fn);
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
+  if (topk > kMaxTopk) return fail(DSPARK_EUNSUPPORTED, "%s: topk > %d", fn, kMaxTopk);
+  if (wdt != DSPARK_F32 && wdt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)wdt);
+  if (r > kMaxRank) return fail(DSPARK_EUNSUPPORTED, "%s: r > %d", fn, kMaxRank);
+  const bool bf16 = wdt == DSPARK_BF16;
+  if (bf16) {
+    if (r % 32) return fail(DSPARK_EUNSUPPORTED, "%s: bf16 needs r %% 32 == 0", fn);
+    if (V % 8) return fail(DSPARK_EUNSUPPORTED, "%s: bf16 needs V %% 8 == 0", fn);
+    if (!aligned16(U) || !aligned16(A) || !aligned16(Bm) || (logits_out && !aligned16(logits_out)))
+      return fail(DSPARK_EUNSUPPORTED, "%s: U, A, Bm, logits_out must be 16-byte aligned", fn);
+  }
+  const size_t need = markov_ws_bytes(B, V, topk);
+  if (!ws || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+
+  StepArgs a{};
+  a.U = U;
+  a.anchor = anchor;
+  a.tokens = tokens;
+  a.A = A;
+  a.Bm = Bm;
+  a.B = static_cast<int>(B);
+  a.gamma = static_cast<int>(gamma);
+  a.V = static_cast<int>(V);
+  a.r = static_cast<int>(r);
+  a.sample = temperature > 0.0f;
+  a.inv_temp = temperature > 0.0f ? 1.0f / temperature : 1.0f;
+  a.seeds = seeds;
+  a.off_lo = static_cast<uint32_t>(offset);
+  a.off_hi = static_cast<uint32_t>(offset >> 32);
+  const size_t P = markov_partials(V);
+  const size_t arr = align_up(static_cast<size_t>(B) * P * 4);
+  char* base = static_cast<char*>(ws);
+  a.p_score = reinterpret_cast<float*>(base);
+  a.p_idx = reinterpret_cast<int32_t*>(base + arr);
+  a.p_x = reinterpret_cast<float*>(base + 2 * arr);
+  a.p_m = reinterpret_cast<float*>(base + 3 * arr);
+  a.p_s = reinterpret_cast<float*>(base + 4 * arr);
+  a.P = static_cast<int>(P);
+  a.S = static_cast<int>(markov_segments(V));
+  a.segmax = topk > 0 ? reinterpret_cast<float*>(base + 5 * arr) : nullptr;
+  a.logits_out = logits_out;
+  a.tok_logit = tok_logit;
+  a.lse = lse;
+  a.topk = topk;
+  a.topk_idx = topk_idx;
+  a.topk_prob = topk_prob;
+  for (int j = 0; j < gamma; ++j) {
+    a.j = j;
+    const hipError_t e = launch_markov_position(a, bf16, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return DSPARK_OK;
+}
+
+// ---------------------------------------------------------------------------
+extern "C" dspark_status_t dspark_confidence_survival(
+    const void* h, dspark_dtype_t dt, int64_t B, int64_t gamma, int64_t H, const void* w_c,
+    float b_c, const void* w_m, const void* A, int64_t r, const int32_t* anchor,
+    const int32_t* tokens, float* conf, float* survival, hipStream_t stream) {
+  const char* fn = "dspark_confidence_survival";
+  if (!h || !w_c || !conf || !survival) return fail(DSPARK_EINVAL, "%s: h, w_c, conf, survival must be non-NULL", fn);
+  if (B <= 0 || gamma <= 0 || H <= 0) return fail(DSPARK_EINVAL, "%s: B, gamma, H must be positive", fn);
+  if (B > kI32Max || H > kI32Max || B * gamma > kI32Max) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  if (w_m && (!A || !anchor || !tokens || r <= 0))
+    return fail(DSPARK_EINVAL, "%s: w_m needs A, anchor, tokens and r > 0", fn);
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)dt);
+  if (w_m && r > kI32Max) return fail(DSPARK_EINVAL, "%s: r too large", fn);
+  return hip_status(launch_confidence(h, dt == DSPARK_BF16, (int)B, (int)gamma, (int)H, w_c, b_c, w_m,
+                                      A, w_m ? (int)r : 0, anchor, tokens, conf, survival, stream),
+                    fn);
+}
+
+// ---------------------------------------------------------------------------
+extern "C" dspark_status_t dspark_overlap_tau_workspace(int64_t N, int64_t gamma, int64_t V, size_t* bytes) {
+  if (!bytes) return fail(DSPARK_EINVAL, "dspark_overlap_tau_workspace: bytes is NULL");
+  if (N <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "dspark_overlap_tau_workspace: sizes must be positive");
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "dspark_overlap_tau_workspace: gamma > %d", kMaxGamma);
+  if (N * gamma > kI32Max) return fail(DSPARK_EINVAL, "dspark_overlap_tau_workspace: sizes too large");
+  *bytes = overlap_ws_bytes(N, gamma);
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float* draft,
+                                              const int32_t* cand_idx, const float* cand_prob,
+                                              int32_t k, const uint8_t* valid, int64_t N,
+                                              int64_t gamma, int64_t V, float* alpha, float* tau,
+                                              double* accept_rate_at, double* tau_mean, void* ws,
+                                              size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "dspark_overlap_tau";
+  if (!teacher || !alpha || !tau) return fail(DSPARK_EINVAL, "%s: teacher, alpha, tau must be non-NULL", fn);
+  if (N <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "%s: N, gamma, V must be positive", fn);
+  if (V > kI32Max || N * gamma > kI32Max) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  if (draft) {
+    if (k != 0 || cand_idx || cand_prob)
+      return fail(DSPARK_EINVAL, "%s: dense mode needs k == 0 and NULL candidates", fn);
+  } else {
+    if (k <= 0 || !cand_idx || !cand_prob)
+      return fail(DSPARK_EINVAL, "%s: candidate mode needs k > 0, cand_idx and cand_prob", fn);
+    if (k > V) return fail(DSPARK_EINVAL, "%s: k > V", fn);
+    if (k > kMaxCand) return fail(DSPARK_EUNSUPPORTED, "%s: k > %d", fn, kMaxCand);
+  }
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
+  if (V % 4) return fail(DSPARK_EUNSUPPORTED, "%s: V %% 4 != 0", fn);
+  if (!aligned16(teacher) || (draft && !aligned16(draft)))
+    return fail(DSPARK_EUNSUPPORTED, "%s: teacher/draft must be 16-byte aligned", fn);
+  const size_t need = overlap_ws_bytes(N, gamma);
+  if (!ws || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+  OverlapArgs a{};
+  a.teacher = teacher;
+  a.draft = draft;
+  a.cand_idx = cand_idx;
+  a.cand_prob = cand_prob;
+  a.k = draft ? 0 : k;
+  a.valid = valid;
+  a.N = static_cast<int>(N);
+  a.gamma = static_cast<int>(gamma);
+  a.V = static_cast<int>(V);
+  a.alpha = alpha;
+  a.tau = tau;
+  a.accept_rate_at = accept_rate_at;
+  a.tau_mean = tau_mean;
+  a.ws_acc = static_cast<double*>(ws);
+  return hip_status(launch_overlap_tau(a, stream), fn);
+}

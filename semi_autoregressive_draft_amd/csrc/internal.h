@@ -1,0 +1,77 @@
+// Internal launch interface between the C ABI (dspark_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kMaxRank = 1024;
+constexpr int kMaxTopk = 32;
+constexpr int kMaxGamma = 16;
+constexpr int kMaxCand = 64;
+constexpr size_t kSkinnyMaxLds = 64 * 1024;
+
+// Arguments of one Markov position (step + merge kernels).
+struct StepArgs {
+  const float* U;          // [B, gamma, V]
+  const int32_t* anchor;   // [B]
+  int32_t* tokens;         // [B, gamma] (read for j > 0, written by the merge)
+  const void* A;           // [V, r]
+  const void* Bm;          // [r, V]
+  int B, gamma, V, r, j;
+  int sample;              // 0 greedy, 1 Gumbel-max
+  float inv_temp;
+  const uint64_t* seeds;   // [B]
+  uint32_t off_lo, off_hi;
+  // per (request, tile) partials, [B][P]
+  float* p_score;
+  int32_t* p_idx;
+  float* p_x;
+  float* p_m;
+  float* p_s;
+  int P;                   // stride of the partial arrays
+  int Pn;                  // partials actually produced (set by the launcher)
+  float* segmax;           // [B][S] segment maxima (top-k only, else null)
+  int S;
+  float* logits_out;       // [B, gamma, V] or null
+  float* tok_logit;        // [B, gamma] or null
+  float* lse;              // [B, gamma] or null
+  int topk;
+  int32_t* topk_idx;       // [B, gamma, topk]
+  float* topk_prob;
+};
+
+size_t markov_partials(int64_t V);
+size_t markov_segments(int64_t V);
+hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s);
+
+hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
+                          int64_t V, float* U, hipStream_t s);
+
+hipError_t launch_confidence(const void* h, bool bf16, int B, int gamma, int H,
+                             const void* w_c, float b_c, const void* w_m, const void* A, int r,
+                             const int32_t* anchor, const int32_t* tokens, float* conf,
+                             float* surv, hipStream_t s);
+
+struct OverlapArgs {
+  const float* teacher;
+  const float* draft;
+  const int32_t* cand_idx;
+  const float* cand_prob;
+  int k;
+  const uint8_t* valid;
+  int N, gamma, V;
+  float* alpha;
+  float* tau;
+  double* accept_rate_at;
+  double* tau_mean;
+  double* ws_acc;        // [nblk][2*gamma + 2] per-workgroup partial sums
+  int nblk;
+};
+
+int overlap_tau_blocks(int64_t N);
+hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s);
+
+}  // namespace dspark

@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, answers the workspace queries, and rejects invalid
+arguments with the documented status before any device work is enqueued.
+
+Every call below fails validation on the host (a required pointer is NULL, a
+size is invalid, or the workspace is too small), so no kernel is launched; the
+fake non-NULL pointers are never dereferenced."""
+import ctypes as C
+import os
+
+import pytest
+
+from semi_autoregressive_draft_amd import binding as bd
+
+FAKE = 0x1000        # 16-byte aligned, never dereferenced
+MISALIGNED = 0x1004
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bd.LIB_PATH):
+        from semi_autoregressive_draft_amd import build
+        build.build()
+    return bd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = bd.header_symbols()
+    assert set(names) >= {"dspark_lm_head", "dspark_markov_propose", "dspark_confidence_survival",
+                          "dspark_overlap_tau", "dspark_last_error", "dspark_version",
+                          "dspark_markov_propose_workspace", "dspark_overlap_tau_workspace"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(bd._SIGNATURES)
+
+
+def test_version(L):
+    assert bd.version().startswith("dspark-mi355x") and "gfx950" in bd.version()
+
+
+def _ws(fn, *args):
+    n = C.c_size_t(0)
+    st = fn(*args, C.byref(n))
+    return st, n.value
+
+
+def test_workspace_queries(L):
+    st, n = _ws(L.dspark_markov_propose_workspace, 1, 7, 151936, 0)
+    assert st == bd.OK and n >= 5 * 1187 * 4
+    st, n16 = _ws(L.dspark_markov_propose_workspace, 1, 7, 151936, 16)
+    assert st == bd.OK and n16 >= n + 4748 * 4
+    st, n256 = _ws(L.dspark_markov_propose_workspace, 256, 7, 151936, 16)
+    assert st == bd.OK and n256 > 200 * n16
+    assert _ws(L.dspark_markov_propose_workspace, 0, 7, 100, 0)[0] == bd.EINVAL
+    assert _ws(L.dspark_markov_propose_workspace, 1, 7, 100, -1)[0] == bd.EINVAL
+    st, n = _ws(L.dspark_overlap_tau_workspace, 4096, 7, 151936)
+    assert st == bd.OK and n >= 16 * 16 * 8
+    assert _ws(L.dspark_overlap_tau_workspace, 10, 17, 100)[0] == bd.EUNSUPPORTED
+    assert L.dspark_markov_propose_workspace(1, 7, 100, 0, None) == bd.EINVAL
+
+
+def test_lm_head_validation(L):
+    f = L.dspark_lm_head
+    assert f(None, FAKE, bd.BF16, 7, 2560, 151936, FAKE, None) == bd.EINVAL
+    assert "non-NULL" in bd.last_error()
+    assert f(FAKE, FAKE, bd.BF16, 0, 2560, 151936, FAKE, None) == bd.EINVAL
+    assert f(FAKE, FAKE, bd.BF16, 7, 2560, 2 ** 31, FAKE, None) == bd.EINVAL
+    assert f(FAKE, FAKE, bd.BF16, 7, 2564, 151936, FAKE, None) == bd.EUNSUPPORTED
+    assert f(FAKE, FAKE, bd.BF16, 7, 2560, 151932, FAKE, None) == bd.EUNSUPPORTED
+    assert f(MISALIGNED, FAKE, bd.BF16, 7, 2560, 151936, FAKE, None) == bd.EUNSUPPORTED
+    assert f(FAKE, FAKE, 7, 7, 2560, 151936, FAKE, None) == bd.EUNSUPPORTED
+
+
+def _propose(L, **kw):
+    a = dict(U=FAKE, B=1, gamma=7, V=151936, anchor=FAKE, A=FAKE, Bm=FAKE, wdt=bd.BF16, r=256,
+             T=0.0, seeds=None, offset=0, topk=0, tokens=FAKE, tok_logit=None, lse=None,
+             topk_idx=None, topk_prob=None, logits_out=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.dspark_markov_propose(a["U"], a["B"], a["gamma"], a["V"], a["anchor"], a["A"], a["Bm"],
+                                   a["wdt"], a["r"], a["T"], a["seeds"], a["offset"], a["topk"],
+                                   a["tokens"], a["tok_logit"], a["lse"], a["topk_idx"],
+                                   a["topk_prob"], a["logits_out"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
+
+
+def test_markov_validation(L):
+    assert _propose(L, U=None) == bd.EINVAL
+    assert _propose(L, tokens=None) == bd.EINVAL
+    assert _propose(L, B=0) == bd.EINVAL
+    assert _propose(L, r=0) == bd.EINVAL
+    assert _propose(L, T=-1.0) == bd.EINVAL
+    assert _propose(L, T=float("nan")) == bd.EINVAL
+    assert _propose(L, T=1.0) == bd.EINVAL                       # sampling without seeds
+    assert _propose(L, topk=16) == bd.EINVAL                     # no topk outputs
+    assert _propose(L, topk_idx=FAKE, topk_prob=FAKE) == bd.EINVAL   # outputs with topk == 0
+    assert _propose(L, topk=200000, topk_idx=FAKE, topk_prob=FAKE) == bd.EINVAL  # topk > V
+    assert _propose(L, gamma=17) == bd.EUNSUPPORTED
+    assert _propose(L, topk=33, topk_idx=FAKE, topk_prob=FAKE) == bd.EUNSUPPORTED
+    assert _propose(L, r=48) == bd.EUNSUPPORTED                  # bf16 rank not a multiple of 32
+    assert _propose(L, r=2048) == bd.EUNSUPPORTED
+    assert _propose(L, V=151932) == bd.EUNSUPPORTED              # bf16 rows not 16-byte multiples
+    assert _propose(L, A=MISALIGNED) == bd.EUNSUPPORTED
+    assert _propose(L, wdt=5) == bd.EUNSUPPORTED
+    assert _propose(L) == bd.EWORKSPACE                          # no workspace
+    st, need = _ws(L.dspark_markov_propose_workspace, 1, 7, 151936, 0)
+    assert _propose(L, ws=FAKE, ws_bytes=need - 1) == bd.EWORKSPACE
+    assert "workspace" in bd.last_error()
+    # float32 tables accept any rank and V
+    assert _propose(L, wdt=bd.F32, r=48, V=151932) == bd.EWORKSPACE
+
+
+def test_confidence_validation(L):
+    f = L.dspark_confidence_survival
+    assert f(None, bd.BF16, 1, 7, 2560, FAKE, 0.0, None, None, 0, None, None, FAKE, FAKE, None) == bd.EINVAL
+    assert f(FAKE, bd.BF16, 1, 7, 2560, FAKE, 0.0, FAKE, None, 256, FAKE, FAKE, FAKE, FAKE, None) == bd.EINVAL
+    assert f(FAKE, bd.BF16, 1, 7, 2560, FAKE, 0.0, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == bd.EINVAL
+    assert f(FAKE, bd.BF16, 1, 17, 2560, FAKE, 0.0, None, None, 0, None, None, FAKE, FAKE, None) == bd.EUNSUPPORTED
+    assert f(FAKE, 3, 1, 7, 2560, FAKE, 0.0, None, None, 0, None, None, FAKE, FAKE, None) == bd.EUNSUPPORTED
+
+
+def test_overlap_validation(L):
+    f = L.dspark_overlap_tau
+    args = lambda **k: [k.get(n, d) for n, d in (
+        ("teacher", FAKE), ("draft", FAKE), ("idx", None), ("prob", None), ("k", 0), ("valid", None),
+        ("N", 4), ("gamma", 7), ("V", 151936), ("alpha", FAKE), ("tau", FAKE), ("acc", None),
+        ("mean", None), ("ws", None), ("wsb", 0), ("s", None))]
+    assert f(*args(teacher=None)) == bd.EINVAL
+    assert f(*args(k=16)) == bd.EINVAL                       # dense with k
+    assert f(*args(draft=None)) == bd.EINVAL                 # sparse without candidates
+    assert f(*args(draft=None, idx=FAKE, prob=FAKE, k=0)) == bd.EINVAL
+    assert f(*args(draft=None, idx=FAKE, prob=FAKE, k=65)) == bd.EUNSUPPORTED
+    assert f(*args(gamma=17)) == bd.EUNSUPPORTED
+    assert f(*args(V=151934)) == bd.EUNSUPPORTED
+    assert f(*args(draft=MISALIGNED)) == bd.EUNSUPPORTED
+    assert f(*args()) == bd.EWORKSPACE
+    assert f(*args(draft=None, idx=FAKE, prob=FAKE, k=16)) == bd.EWORKSPACE

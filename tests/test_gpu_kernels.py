@@ -1,0 +1,233 @@
+"""GPU parity of each C-ABI entry point against the fp64 oracle, at sizes the
+oracle finishes in seconds that still span several tiles and a ragged tail,
+plus degenerate cases (ties, zero transitions, invalid blocks)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import dspark_oracle as o
+from semi_autoregressive_draft_amd import binding as bd
+from tests.parity import (ALPHA_ABS, check_chain, rel_check, require_gpu, tight_check, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------------------- S1
+@pytest.mark.parametrize("M,H,V,wdtype", [
+    (7, 256, 4096, "f32"),        # tiny reference config shape
+    (5, 100, 333, "f32"),         # ragged everything
+    (1, 256, 5000, "bf16"),       # skinny path, ragged vocabulary tail
+    (7, 296, 5000, "bf16"),       # skinny, K not a multiple of 32
+    (12, 2560, 1000, "bf16"),     # skinny, largest M that keeps h in 64 KB of LDS
+    (13, 2560, 1000, "bf16"),     # tiled path, ragged M
+    (130, 296, 5000, "bf16"),     # tiled, ragged M/K/V tiles
+    (448, 320, 3000, "bf16"),
+])
+def test_lm_head_parity(M, H, V, wdtype):
+    dev = require_gpu()
+    h = synth.normal((M, H), 1.0, 11, synth.TID_H, wdtype)
+    w = synth.normal((V, H), 0.02, 11, synth.TID_WLM, wdtype)
+    U = torch.empty((M, V), dtype=torch.float32, device=dev)
+    bd.dspark_lm_head(to_dev(h, wdtype), to_dev(w, wdtype), U)
+    got = U.cpu().numpy()
+    want = o.lm_head(o.to_f64(h, wdtype), o.to_f64(w, wdtype))
+    rms = np.sqrt((want ** 2).mean(axis=1, keepdims=True))
+    rel_check(got, want, rms, what="U")
+    tight_check(got, want, rms, what="U")
+
+
+# ----------------------------------------------------------------------------- S2-S4
+def _run_markov(U, anchor, A, Bm, wdtype, *, T=0.0, seeds=None, offset=0, topk=0, dump=True):
+    dev = require_gpu()
+    B, gamma, V = U.shape
+    Ud = to_dev(U)
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    tl = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    ls = torch.empty_like(tl)
+    ti = torch.empty((B, gamma, topk), dtype=torch.int32, device=dev) if topk else None
+    tp = torch.empty((B, gamma, topk), dtype=torch.float32, device=dev) if topk else None
+    lo = torch.empty((B, gamma, V), dtype=torch.float32, device=dev) if dump else None
+    sd = to_dev(seeds) if seeds is not None else None
+    bd.dspark_markov_propose(Ud, to_dev(anchor), to_dev(A, wdtype), to_dev(Bm, wdtype), tokens,
+                             temperature=T, seeds=sd, offset=offset, topk=topk, tok_logit=tl,
+                             lse=ls, topk_idx=ti, topk_prob=tp, logits_out=lo)
+    torch.cuda.synchronize()
+    out = dict(tokens=tokens.cpu().numpy(), tok_logit=tl.cpu().numpy(), lse=ls.cpu().numpy())
+    if topk:
+        out["topk_idx"], out["topk_prob"] = ti.cpu().numpy(), tp.cpu().numpy()
+    if dump:
+        out["logits"] = lo.cpu().numpy()
+    return out
+
+
+def _markov_case(B, V, r, wdtype, seed=3, mstd=0.25):
+    U = synth.base_logits(B, V, seed=seed)
+    A = synth.normal((V, r), mstd, seed, synth.TID_A, wdtype)
+    Bm = synth.normal((r, V), mstd, seed, synth.TID_BM, wdtype)
+    anchor = synth.rng(seed, synth.TID_ANCHOR).integers(0, V, size=B).astype(np.int32)
+    return U, anchor, A, Bm
+
+
+@pytest.mark.parametrize("B,V,r,wdtype,T,topk", [
+    (1, 5000, 256, "bf16", 0.0, 0),     # one request, r split over 4 waves
+    (3, 5000, 64, "bf16", 0.0, 0),      # r split over 2 waves
+    (5, 4096, 32, "bf16", 0.7, 0),      # sampled, no r split
+    (17, 5000, 128, "bf16", 0.0, 0),    # 2 request groups per wave, ragged request block
+    (40, 3000, 256, "bf16", 1.0, 0),    # 4 request groups per wave, sampled
+    (70, 2000, 64, "bf16", 0.0, 16),    # two request blocks, top-16
+    (2, 5000, 256, "bf16", 0.0, 32),    # top-32
+    (1, 1000, 64, "bf16", 1.0, 16),     # sampled with top-16
+    (1, 4096, 32, "f32", 0.0, 0),       # tiny reference config
+    (3, 1000, 48, "f32", 1.0, 5),       # float32 tables, any rank
+])
+def test_markov_parity(B, V, r, wdtype, T, topk):
+    U, anchor, A, Bm = _markov_case(B, V, r, wdtype)
+    seeds = np.arange(B, dtype=np.uint64) * 7919 + 3 if T > 0 else None
+    gpu = _run_markov(U, anchor, A, Bm, wdtype, T=T, seeds=seeds, offset=5, topk=topk)
+    check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, wdtype), o.to_f64(Bm, wdtype),
+                temperature=T, seeds=seeds, offset=5, topk=topk)
+
+
+def test_markov_walks_a_permutation():
+    # A = identity rows, Bm = 4 * permutation, |U| < 1.6: x_j = pi^{j+1}(anchor).
+    # All values are exact in bf16, so this checks the previous-token wiring
+    # (anchor at slot 0, token j-1 at slot j) independently of rounding.
+    V = r = 64
+    rng = np.random.default_rng(5)
+    pi = rng.permutation(V)
+    A = synth.bf16_bits(np.eye(V, dtype=np.float32))
+    Bmf = np.zeros((r, V), dtype=np.float32)
+    Bmf[np.arange(r), pi] = 4.0
+    U = rng.uniform(-1.6, 1.6, size=(3, 7, V)).astype(np.float32)
+    anchor = np.array([0, 17, 63], dtype=np.int32)
+    gpu = _run_markov(U, anchor, A, synth.bf16_bits(Bmf), "bf16")
+    for b in range(3):
+        t = anchor[b]
+        for j in range(7):
+            t = pi[t]
+            assert gpu["tokens"][b, j] == t
+
+
+def test_markov_ties_take_lowest_index_and_slow_topk_path():
+    # constant logits and zero transitions: every column ties, so the token is
+    # column 0 and the top-k candidate lists overflow into the exact slow path
+    B, V, r, k = 2, 1024, 32, 16
+    U = np.zeros((B, 7, V), dtype=np.float32)
+    zeros_A = synth.bf16_bits(np.zeros((V, r), np.float32))
+    zeros_B = synth.bf16_bits(np.zeros((r, V), np.float32))
+    gpu = _run_markov(U, np.array([3, 9], np.int32), zeros_A, zeros_B, "bf16", topk=k)
+    assert np.all(gpu["tokens"] == 0)
+    assert np.all(gpu["topk_idx"] == np.arange(k))
+    assert np.allclose(gpu["topk_prob"], 1.0 / k, atol=1e-7)
+    assert np.allclose(gpu["lse"], np.log(V), atol=1e-5)
+
+
+def test_markov_zero_transition_is_parallel_argmax():
+    B, V, r = 4, 3000, 64
+    U = synth.base_logits(B, V, seed=8)
+    gpu = _run_markov(U, np.zeros(B, np.int32), synth.bf16_bits(np.zeros((V, r), np.float32)),
+                      synth.normal((r, V), 0.25, 8, synth.TID_BM, "bf16"), "bf16", dump=False)
+    assert np.array_equal(gpu["tokens"], U.argmax(axis=-1))
+
+
+def test_markov_is_deterministic():
+    U, anchor, A, Bm = _markov_case(33, 5000, 256, "bf16", seed=4)
+    seeds = np.arange(33, dtype=np.uint64)
+    a = _run_markov(U, anchor, A, Bm, "bf16", T=1.0, seeds=seeds, topk=16)
+    b = _run_markov(U, anchor, A, Bm, "bf16", T=1.0, seeds=seeds, topk=16)
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+# ----------------------------------------------------------------------------- S5
+@pytest.mark.parametrize("B,H,r,wdtype,with_wm", [
+    (5, 2560, 256, "bf16", True),
+    (1, 256, 32, "f32", False),
+    (256, 2560, 256, "bf16", False),
+    (3, 100, 48, "f32", True),
+])
+def test_confidence_parity(B, H, r, wdtype, with_wm):
+    dev = require_gpu()
+    gamma, V = 7, 777
+    h = synth.normal((B, gamma, H), 1.0, 2, synth.TID_H, wdtype)
+    w_c = synth.normal((H,), 0.02, 2, synth.TID_WC, wdtype)
+    w_m = synth.normal((r,), 0.5, 2, synth.TID_WM, wdtype) if with_wm else None
+    A = synth.normal((V, r), 0.25, 2, synth.TID_A, wdtype)
+    anchor = synth.rng(2, synth.TID_ANCHOR).integers(0, V, size=B).astype(np.int32)
+    tokens = synth.rng(3, synth.TID_ANCHOR).integers(0, V, size=(B, gamma)).astype(np.int32)
+    conf = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    surv = torch.empty_like(conf)
+    bd.dspark_confidence_survival(to_dev(h, wdtype), to_dev(w_c, wdtype), 0.3, conf, surv,
+                                  w_m=to_dev(w_m, wdtype) if with_wm else None,
+                                  A=to_dev(A, wdtype), anchor=to_dev(anchor), tokens=to_dev(tokens))
+    torch.cuda.synchronize()
+    c_ref, s_ref = o.confidence_survival(
+        o.to_f64(h, wdtype), o.to_f64(w_c, wdtype), 0.3,
+        w_m=o.to_f64(w_m, wdtype) if with_wm else None, A=o.to_f64(A, wdtype),
+        anchor=anchor, tokens=tokens)
+    rel_check(conf.cpu().numpy(), c_ref, 0.0, what="conf")
+    rel_check(surv.cpu().numpy(), s_ref, 0.0, what="survival")
+    assert np.abs(conf.cpu().numpy() - c_ref).max() < 1e-5
+    assert np.abs(surv.cpu().numpy() - s_ref).max() < 1e-5
+
+
+# ----------------------------------------------------------------------------- S6
+def _run_overlap(teacher, *, draft=None, idx=None, prob=None, valid=None):
+    dev = require_gpu()
+    N, gamma, V = teacher.shape
+    alpha = torch.empty((N, gamma), dtype=torch.float32, device=dev)
+    tau = torch.empty((N,), dtype=torch.float32, device=dev)
+    acc = torch.empty((gamma,), dtype=torch.float64, device=dev)
+    mean = torch.empty((1,), dtype=torch.float64, device=dev)
+    bd.dspark_overlap_tau(to_dev(teacher), alpha, tau,
+                          draft=None if draft is None else to_dev(draft),
+                          cand_idx=None if idx is None else to_dev(idx),
+                          cand_prob=None if prob is None else to_dev(prob),
+                          valid=None if valid is None else to_dev(valid),
+                          accept_rate_at=acc, tau_mean=mean)
+    torch.cuda.synchronize()
+    return alpha.cpu().numpy(), tau.cpu().numpy(), acc.cpu().numpy(), float(mean.cpu()[0])
+
+
+def _check_tau(got, alpha_raw, valid):
+    a_ref, tau_ref, acc_ref, mean_ref = o.tau_metrics(alpha_raw, valid)
+    alpha, tau, acc, mean = got
+    assert np.abs(alpha - a_ref).max() < ALPHA_ABS
+    assert np.abs(alpha - a_ref).max() < 2e-5                    # tighter: fp32 sums
+    assert np.abs(tau - tau_ref).max() < ALPHA_ABS
+    assert np.abs(acc - acc_ref).max() < ALPHA_ABS
+    assert abs(mean - mean_ref) < ALPHA_ABS
+
+
+@pytest.mark.parametrize("sigma", [0.5, 1.0, 2.0])
+def test_overlap_dense_parity(sigma):
+    N, V = 9, 5000
+    teacher, draft = synth.overlap_inputs(N, V, sigma, seed=1)
+    valid = synth.validity(N, seed=1, trunc_frac=0.4, n_dummy=1)
+    got = _run_overlap(teacher, draft=draft, valid=valid)
+    a_raw, _ = o.overlap_dense(teacher.astype(np.float64), draft.astype(np.float64))
+    _check_tau(got, a_raw, valid)
+    assert got[1][-1] == 0.0                                   # padding block sentinel
+
+
+def test_overlap_identical_rows_give_tau_eight():
+    teacher, _ = synth.overlap_inputs(3, 4096, 1.0, seed=2)
+    alpha, tau, acc, mean = _run_overlap(teacher, draft=teacher.copy())
+    assert np.allclose(alpha, 1.0, atol=2e-5) and np.allclose(tau, 8.0, atol=2e-4)
+
+
+@pytest.mark.parametrize("k", [16, 64])
+def test_overlap_candidates_parity(k):
+    N, V = 5, 5000
+    teacher, _ = synth.overlap_inputs(N, V, 1.0, seed=3)
+    teacher = teacher * 3.0                           # peakier teacher: visible overlap
+    idx, prob = synth.candidates(N, V, k, seed=3)
+    # give the candidates the teacher's largest entries so that alpha is O(0.1)
+    t64 = teacher.astype(np.float64)
+    order = np.argsort(-t64, axis=-1)[..., :k]
+    idx = order.astype(np.int32)
+    got = _run_overlap(teacher.astype(np.float32), idx=idx, prob=prob)
+    a_raw = o.overlap_sparse(t64, idx, prob.astype(np.float64))
+    assert a_raw.max() > 0.05
+    _check_tau(got, a_raw, None)
