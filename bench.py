@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2_qwen3_4b_b1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch copy_) 5 times; its "
+                         "rocprofv3 FETCH_SIZE/WRITE_SIZE per dispatch calibrate the counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the multi-GPU path is a design only "
@@ -140,6 +143,16 @@ def main():
     import torch
     import synth
     from semi_autoregressive_draft_amd.path import DraftPath
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
 
     cfg_name, over, overlap = WORKLOADS[args.workload]
     cfg = dict(synth.CONFIGS[cfg_name])

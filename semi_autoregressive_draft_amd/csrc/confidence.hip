@@ -4,61 +4,90 @@
 // predict_confidence_step (hidden states only, the w_m == null case);
 // "DSpark 论文精读", §3.1: a_{r,j} = prod_{i<=j} c_{r,i}.
 //
-// One workgroup per request: each of the gamma dot products (H + r terms) is
-// reduced by a fixed tree, and thread 0 runs the sigmoid and the running
-// product in position order.  The work is a few KB per request, so the
-// kernel is bound by launch latency, not by HBM.
+// One workgroup per request with one wave per slot j: each wave reduces its
+// dot product (H terms, plus r for the Markov term) from 16-byte loads by a
+// fixed tree, then thread 0 runs the sigmoid and the running product in
+// position order.  The work is a few KB per request, so the kernel is bound by
+// latency, not by HBM; the gamma dot products run concurrently.
 #include "common.h"
 #include "internal.h"
 
 namespace dspark {
 
 template <typename T>
-__global__ __launch_bounds__(256) void confidence_survival_kernel(
+__device__ __forceinline__ float dot_row(const T* x, const T* y, int n, int lane, bool vec) {
+  float s = 0.f;
+  int done = 0;
+  if (vec) {  // 16-byte loads: 8 bf16 or 4 float per lane and step
+    constexpr int E = 16 / sizeof(T);
+    const int nv = n / E;
+    for (int i = lane; i < nv; i += kWave) {
+      const u32x4 a = reinterpret_cast<const u32x4*>(x)[i];
+      const u32x4 b = reinterpret_cast<const u32x4*>(y)[i];
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s = fmaf(__uint_as_float(a[q] << 16), __uint_as_float(b[q] << 16), s);
+          s = fmaf(__uint_as_float(a[q] & 0xFFFF0000u), __uint_as_float(b[q] & 0xFFFF0000u), s);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s = fmaf(__uint_as_float(a[q]), __uint_as_float(b[q]), s);
+      }
+    }
+    done = nv * E;
+  }
+  for (int k = done + lane; k < n; k += kWave) s = fmaf(to_f32(x[k]), to_f32(y[k]), s);
+  return s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWave* kMaxGamma) void confidence_survival_kernel(
     const T* __restrict__ h, int gamma, int H, const T* __restrict__ w_c, float b_c,
     const T* __restrict__ w_m, const T* __restrict__ A, int r, const int32_t* __restrict__ anchor,
-    const int32_t* __restrict__ tokens, float* __restrict__ conf, float* __restrict__ surv) {
-  __shared__ float part[kMaxGamma][4];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int j = 0; j < gamma; ++j) {
-    const T* hr = h + (static_cast<size_t>(b) * gamma + j) * H;
-    float s = 0.f;
-    for (int k = tid; k < H; k += 256) s = fmaf(to_f32(hr[k]), to_f32(w_c[k]), s);
-    if (w_m) {
-      const int prev = j == 0 ? anchor[b] : tokens[b * gamma + j - 1];
-      const T* ar = A + static_cast<size_t>(prev) * r;
-      for (int k = tid; k < r; k += 256) s = fmaf(to_f32(ar[k]), to_f32(w_m[k]), s);
-    }
-    s = wave_sum(s);
-    if (lane == 0) part[j][w] = s;
+    const int32_t* __restrict__ tokens, float* __restrict__ conf, float* __restrict__ surv,
+    int vec_h, int vec_r) {
+  __shared__ float part[kMaxGamma];
+  const int b = blockIdx.x, lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  float s = dot_row(h + (static_cast<size_t>(b) * gamma + j) * H, w_c, H, lane, vec_h);
+  if (w_m) {
+    const int prev = j == 0 ? anchor[b] : tokens[b * gamma + j - 1];
+    s += dot_row(A + static_cast<size_t>(prev) * r, w_m, r, lane, vec_r);
   }
+  s = wave_sum(s);
+  if (lane == 0) part[j] = s;
   __syncthreads();
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     float run = 1.f;
-    for (int j = 0; j < gamma; ++j) {
-      const float s = ((part[j][0] + part[j][1]) + (part[j][2] + part[j][3])) + b_c;
-      const float c = 1.0f / (1.0f + __expf(-s));
+    for (int jj = 0; jj < gamma; ++jj) {
+      const float c = 1.0f / (1.0f + __expf(-(part[jj] + b_c)));
       run *= c;
-      conf[b * gamma + j] = c;
-      surv[b * gamma + j] = run;
+      conf[b * gamma + jj] = c;
+      surv[b * gamma + jj] = run;
     }
   }
 }
+
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 hipError_t launch_confidence(const void* h, bool bf16, int B, int gamma, int H,
                              const void* w_c, float b_c, const void* w_m, const void* A, int r,
                              const int32_t* anchor, const int32_t* tokens, float* conf,
                              float* surv, hipStream_t s) {
+  const int es = bf16 ? 2 : 4;
+  const int vec_h = al16(h) && al16(w_c) && (H * es) % 16 == 0;
+  const int vec_r = w_m && al16(A) && al16(w_m) && (r * es) % 16 == 0;
+  const dim3 block(kWave * gamma);
   if (bf16)
-    hipLaunchKernelGGL(confidence_survival_kernel<uint16_t>, dim3(B), dim3(256), 0, s,
+    hipLaunchKernelGGL(confidence_survival_kernel<uint16_t>, dim3(B), block, 0, s,
                        static_cast<const uint16_t*>(h), gamma, H, static_cast<const uint16_t*>(w_c),
                        b_c, static_cast<const uint16_t*>(w_m), static_cast<const uint16_t*>(A), r,
-                       anchor, tokens, conf, surv);
+                       anchor, tokens, conf, surv, vec_h, vec_r);
   else
-    hipLaunchKernelGGL(confidence_survival_kernel<float>, dim3(B), dim3(256), 0, s,
+    hipLaunchKernelGGL(confidence_survival_kernel<float>, dim3(B), block, 0, s,
                        static_cast<const float*>(h), gamma, H, static_cast<const float*>(w_c), b_c,
                        static_cast<const float*>(w_m), static_cast<const float*>(A), r, anchor,
-                       tokens, conf, surv);
+                       tokens, conf, surv, vec_h, vec_r);
   return hipGetLastError();
 }
 

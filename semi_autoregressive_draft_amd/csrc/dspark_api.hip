@@ -32,15 +32,23 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 constexpr int64_t kI32Max = 2147483647;
 
-size_t markov_ws_bytes(int64_t B, int64_t V, int32_t topk) {
-  const size_t P = markov_partials(V);
-  size_t s = 5 * align_up(static_cast<size_t>(B) * P * 4);
-  if (topk > 0) s += align_up(static_cast<size_t>(B) * markov_segments(V) * 4);
+// per (request, position): 5 partial arrays of one entry per vocabulary tile,
+// plus the segment maxima when top-k is asked for
+size_t markov_ws_bytes(int64_t B, int64_t gamma, int64_t V, int32_t topk) {
+  const size_t rows = static_cast<size_t>(B) * gamma;
+  size_t s = 5 * align_up(rows * markov_partials(V) * 4);
+  if (topk > 0) s += align_up(rows * markov_segments(V) * 4);
   return s;
 }
 
-size_t overlap_ws_bytes(int64_t N, int64_t gamma) {
+size_t overlap_ws_tau_bytes(int64_t N, int64_t gamma) {
   return align_up(static_cast<size_t>(overlap_tau_blocks(N)) * (2 * gamma + 2) * sizeof(double));
+}
+
+size_t overlap_ws_bytes(int64_t N, int64_t gamma, int64_t V) {
+  const int nchunk = overlap_split_chunks(N * gamma, V);
+  const size_t split = nchunk > 1 ? align_up(static_cast<size_t>(N * gamma) * nchunk * 5 * sizeof(float)) : 0;
+  return overlap_ws_tau_bytes(N, gamma) + split;
 }
 
 }  // namespace
@@ -78,7 +86,7 @@ extern "C" dspark_status_t dspark_markov_propose_workspace(int64_t B, int64_t ga
   if (B <= 0 || gamma <= 0 || V <= 0 || topk < 0)
     return fail(DSPARK_EINVAL, "dspark_markov_propose_workspace: B, gamma, V must be positive, topk >= 0");
   if (V > kI32Max || B > kI32Max) return fail(DSPARK_EINVAL, "dspark_markov_propose_workspace: sizes too large");
-  *bytes = markov_ws_bytes(B, V, topk);
+  *bytes = markov_ws_bytes(B, gamma, V, topk);
   return DSPARK_OK;
 }
 
@@ -115,7 +123,7 @@ extern "C" dspark_status_t dspark_markov_propose(
     if (!aligned16(U) || !aligned16(A) || !aligned16(Bm) || (logits_out && !aligned16(logits_out)))
       return fail(DSPARK_EUNSUPPORTED, "%s: U, A, Bm, logits_out must be 16-byte aligned", fn);
   }
-  const size_t need = markov_ws_bytes(B, V, topk);
+  const size_t need = markov_ws_bytes(B, gamma, V, topk);
   if (!ws || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
 
@@ -135,7 +143,7 @@ extern "C" dspark_status_t dspark_markov_propose(
   a.off_lo = static_cast<uint32_t>(offset);
   a.off_hi = static_cast<uint32_t>(offset >> 32);
   const size_t P = markov_partials(V);
-  const size_t arr = align_up(static_cast<size_t>(B) * P * 4);
+  const size_t arr = align_up(static_cast<size_t>(B) * gamma * P * 4);
   char* base = static_cast<char*>(ws);
   a.p_score = reinterpret_cast<float*>(base);
   a.p_idx = reinterpret_cast<int32_t*>(base + arr);
@@ -156,6 +164,7 @@ extern "C" dspark_status_t dspark_markov_propose(
     const hipError_t e = launch_markov_position(a, bf16, stream);
     if (e != hipSuccess) return hip_status(e, fn);
   }
+  if (topk > 0) return hip_status(launch_markov_topk(a, bf16, stream), fn);
   return DSPARK_OK;
 }
 
@@ -184,7 +193,7 @@ extern "C" dspark_status_t dspark_overlap_tau_workspace(int64_t N, int64_t gamma
   if (N <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "dspark_overlap_tau_workspace: sizes must be positive");
   if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "dspark_overlap_tau_workspace: gamma > %d", kMaxGamma);
   if (N * gamma > kI32Max) return fail(DSPARK_EINVAL, "dspark_overlap_tau_workspace: sizes too large");
-  *bytes = overlap_ws_bytes(N, gamma);
+  *bytes = overlap_ws_bytes(N, gamma, V);
   return DSPARK_OK;
 }
 
@@ -211,7 +220,7 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
   if (V % 4) return fail(DSPARK_EUNSUPPORTED, "%s: V %% 4 != 0", fn);
   if (!aligned16(teacher) || (draft && !aligned16(draft)))
     return fail(DSPARK_EUNSUPPORTED, "%s: teacher/draft must be 16-byte aligned", fn);
-  const size_t need = overlap_ws_bytes(N, gamma);
+  const size_t need = overlap_ws_bytes(N, gamma, V);
   if (!ws || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
   OverlapArgs a{};
@@ -229,5 +238,9 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
   a.accept_rate_at = accept_rate_at;
   a.tau_mean = tau_mean;
   a.ws_acc = static_cast<double*>(ws);
+  a.nchunk = overlap_split_chunks(N * gamma, V);
+  a.ws_split = a.nchunk > 1
+      ? reinterpret_cast<float*>(static_cast<char*>(ws) + overlap_ws_tau_bytes(N, gamma))
+      : nullptr;
   return hip_status(launch_overlap_tau(a, stream), fn);
 }

@@ -25,7 +25,7 @@ struct StepArgs {
   float inv_temp;
   const uint64_t* seeds;   // [B]
   uint32_t off_lo, off_hi;
-  // per (request, tile) partials, [B][P]
+  // per (request, position, tile) partials, [B][gamma][P]
   float* p_score;
   int32_t* p_idx;
   float* p_x;
@@ -33,7 +33,7 @@ struct StepArgs {
   float* p_s;
   int P;                   // stride of the partial arrays
   int Pn;                  // partials actually produced (set by the launcher)
-  float* segmax;           // [B][S] segment maxima (top-k only, else null)
+  float* segmax;           // [B][gamma][S] segment maxima (top-k only, else null)
   int S;
   float* logits_out;       // [B, gamma, V] or null
   float* tok_logit;        // [B, gamma] or null
@@ -46,6 +46,7 @@ struct StepArgs {
 size_t markov_partials(int64_t V);
 size_t markov_segments(int64_t V);
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s);
+hipError_t launch_markov_topk(StepArgs a, bool bf16, hipStream_t s);
 
 hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
                           int64_t V, float* U, hipStream_t s);
@@ -69,9 +70,13 @@ struct OverlapArgs {
   double* tau_mean;
   double* ws_acc;        // [nblk][2*gamma + 2] per-workgroup partial sums
   int nblk;
+  float* ws_split;       // [rows][nchunk][5] chunk states (split path only)
+  int nchunk;            // workgroups per row (1: one workgroup per row)
+  int chunk4;            // float4 elements per chunk (set by the launcher)
 };
 
 int overlap_tau_blocks(int64_t N);
+int overlap_split_chunks(int64_t rows, int64_t V);
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s);
 
 }  // namespace dspark

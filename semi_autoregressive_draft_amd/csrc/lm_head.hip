@@ -15,7 +15,7 @@ namespace dspark {
 // as the B operand (zero for columns >= M).  The output tile D[v][m] leaves each
 // lane 4 consecutive vocabulary entries of one row m: one 16-byte store.
 constexpr int kSkinnyWaves = 4;
-constexpr int kSkinnyTilesPerWave = 2;
+constexpr int kSkinnyTilesPerWave = 1;
 constexpr int kSkinnyUnroll = 8;
 
 __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(

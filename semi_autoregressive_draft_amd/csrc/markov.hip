@@ -34,7 +34,7 @@ namespace dspark {
 // and add their accumulators through LDS in a fixed order.
 constexpr int kMarkovTile = 128;   // vocabulary columns per bf16 step tile
 constexpr int kMarkovTileF32 = 256;
-constexpr int kSeg = 32;           // vocabulary columns per top-k segment
+constexpr int kSeg = 8;            // vocabulary columns per top-k segment
 
 template <int RG, int KS>
 __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
@@ -167,18 +167,15 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
       for (int c = 1; c < 8; ++c)
         if (score[c] > as.score) as = ArgState{score[c], vcol + c, x[c]};
 
-      if (a.segmax) {  // max over 32 consecutive columns = 4 neighbouring lanes
-        float sm = fmaxf(m8, __shfl_xor(m8, 1));
-        sm = fmaxf(sm, __shfl_xor(sm, 2));
-        if ((n & 3) == 0 && live) a.segmax[static_cast<size_t>(b) * a.S + vcol / kSeg] = sm;
-      }
+      // the lane's 8 columns are one top-k segment
+      if (a.segmax && live) a.segmax[(static_cast<size_t>(b) * a.gamma + a.j) * a.S + vcol / kSeg] = m8;
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
         ls = lse_merge(ls, shfl_xor(ls, o));
         as = arg_merge(as, shfl_xor(as, o));
       }
       if (n == 0 && b < a.B) {
-        const size_t q = static_cast<size_t>(b) * P + tile;
+        const size_t q = (static_cast<size_t>(b) * a.gamma + a.j) * P + tile;
         a.p_m[q] = ls.m;
         a.p_s[q] = ls.s;
         a.p_score[q] = as.score;
@@ -227,7 +224,7 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
     float sm = x;
 #pragma unroll
     for (int o = 1; o < kSeg; o <<= 1) sm = fmaxf(sm, __shfl_xor(sm, o));
-    if ((lane & (kSeg - 1)) == 0 && live) a.segmax[static_cast<size_t>(b) * a.S + v / kSeg] = sm;
+    if ((lane & (kSeg - 1)) == 0 && live) a.segmax[(static_cast<size_t>(b) * a.gamma + a.j) * a.S + v / kSeg] = sm;
   }
   LseState ls{x, live ? 1.0f : 0.0f};
   ArgState as{score, live ? v : 0x7fffffff, x};
@@ -240,7 +237,7 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
   __syncthreads();
   if (tid == 0) {
     for (int i = 1; i < 4; ++i) { ls = lse_merge(red_l[0], red_l[i]); as = arg_merge(red_a[0], red_a[i]); red_l[0] = ls; red_a[0] = as; }
-    const size_t q = static_cast<size_t>(b) * a.P + tile;
+    const size_t q = (static_cast<size_t>(b) * a.gamma + a.j) * a.P + tile;
     a.p_m[q] = red_l[0].m;
     a.p_s[q] = red_l[0].s;
     a.p_score[q] = red_a[0].score;
@@ -250,52 +247,37 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel: one workgroup of 256 threads per request.
-//
-// Greedy/sampled token and lse: thread t folds partials t, t+256, ... in
-// order; the 256 thread states are folded by a fixed xor tree and then wave 0..3
-// in order.
-//
-// Top-k (k <= 32), exact: the step kernel left the maximum of every segment of
-// 32 columns.  (1) theta0 = k-th largest of the 256 per-thread maxima of those
-// segment maxima: k distinct segments have a maximum >= theta0, so every
-// element of the top k lies in a segment whose maximum is >= theta0.  (2) The
-// candidate segments are recomputed element by element (U + A[x_{j-1}] . Bm
-// in float32).  (3) theta1 = k-th largest candidate-segment maximum bounds the
-// k-th largest element from below; the elements >= theta1 are ranked by
-// (value descending, index ascending) and the first k kept.  If a list
-// overflows its LDS capacity (massive ties), a slow exact path selects the k
-// elements one by one over the whole row.
+// Merge kernel (on the sequential path): one workgroup of 256 threads per
+// request folds the per-tile partials of position j in a fixed order (thread t
+// takes tiles t, t+256, ... with its loads issued together; then a fixed xor
+// tree and waves 0..3 in order) and writes x_j, U~_j[x_j] and lse_j.
 constexpr int kMergeThreads = 256;
-constexpr int kCandSegCap = 128;
-constexpr int kSurvCap = 256;
+constexpr int kFoldBatch = 4;
 
-template <typename WT>
-__device__ float recompute_logit(const StepArgs& a, const float* arow_s, int b, int v) {
-  const WT* Bm = static_cast<const WT*>(a.Bm);
-  const size_t V = static_cast<size_t>(a.V);
-  float bias = 0.f;
-  for (int k = 0; k < a.r; ++k) bias = fmaf(arow_s[k], to_f32(Bm[static_cast<size_t>(k) * V + v]), bias);
-  return a.U[(static_cast<size_t>(b) * a.gamma + a.j) * V + v] + bias;
-}
-
-__device__ __forceinline__ bool ranks_before(float xa, int ia, float xb, int ib) {
-  return xa > xb || (xa == xb && ia < ib);
-}
-
-template <typename WT>
 __global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x;
   __shared__ LseState red_l[4];
   __shared__ ArgState red_a[4];
-
   LseState ls{kNegInf, 0.f};
   ArgState as{kNegInf, 0x7fffffff, 0.f};
-  const size_t base = static_cast<size_t>(b) * a.P;
-  for (int p = tid; p < a.Pn; p += kMergeThreads) {
-    ls = lse_merge(ls, LseState{a.p_m[base + p], a.p_s[base + p]});
-    as = arg_merge(as, ArgState{a.p_score[base + p], a.p_idx[base + p], a.p_x[base + p]});
+  const size_t base = (static_cast<size_t>(b) * a.gamma + a.j) * a.P;
+  for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kMergeThreads) {
+    LseState l[kFoldBatch];
+    ArgState g[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const int p = p0 + u * kMergeThreads + tid;
+      if (p < a.Pn) {
+        l[u] = LseState{a.p_m[base + p], a.p_s[base + p]};
+        g[u] = ArgState{a.p_score[base + p], a.p_idx[base + p], a.p_x[base + p]};
+      } else {
+        l[u] = LseState{kNegInf, 0.f};
+        g[u] = ArgState{kNegInf, 0x7fffffff, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) { ls = lse_merge(ls, l[u]); as = arg_merge(as, g[u]); }
   }
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -313,89 +295,211 @@ __global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
     if (a.tok_logit) a.tok_logit[row] = s.x;
     if (a.lse) a.lse[row] = l.m + logf(l.s);
   }
-  if (a.topk == 0) return;
+}
 
-  // ------------------------------ top-k ------------------------------------
+// ---------------------------------------------------------------------------
+// Top-k kernel (off the sequential path): one workgroup per (request,
+// position), launched once after the chain.  Exact for k <= 32.
+//
+// Bounds used (each holds because k distinct tiles or segments reach them):
+//  theta00 = k-th largest of the 256 per-thread maxima of the tile maxima
+//            (the per-tile U~ maximum from the step kernel); every segment whose
+//            maximum is >= theta00 lies in a tile whose maximum is >= theta00,
+//            and at least k segments do;
+//  theta   = exact k-th largest segment maximum, found among those segments;
+//            the k-th largest element is >= theta, so the top k lie in the
+//            segments (8 columns each) whose maximum is >= theta: k plus ties.
+// Those segments are recomputed column by column (U + A[x_{j-1}] . Bm in
+// float32, 16 threads per segment over slices of r, 8 columns per 16-byte
+// load) and their elements ranked by (value descending, index ascending).  If
+// a candidate list overflows its LDS capacity (massive ties), a slow exact
+// path selects the k elements one by one over the whole row.
+constexpr int kTopkThreads = 256;
+constexpr int kTileCap = 128;
+constexpr int kCand1Cap = 512;
+constexpr int kCand2Cap = 64;
+constexpr int kSliceThreads = 16;   // threads sharing one segment's r-loop
+constexpr int kRowBatch = 8;        // Bm rows in flight per thread
+
+template <typename WT>
+__device__ float recompute_logit(const StepArgs& a, const float* arow_s, const float* urow, int v) {
+  const WT* Bm = static_cast<const WT*>(a.Bm);
+  const size_t V = static_cast<size_t>(a.V);
+  float bias = 0.f;
+  for (int k = 0; k < a.r; ++k) bias = fmaf(arow_s[k], to_f32(Bm[static_cast<size_t>(k) * V + v]), bias);
+  return urow[v] + bias;
+}
+
+// 8 consecutive columns v0..v0+7 of Bm row k (columns >= V read as 0)
+__device__ __forceinline__ void load_seg(const uint16_t* Bm, int k, int v0, int V, float* c) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(Bm + static_cast<size_t>(k) * V + v0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = __uint_as_float(w[i] << 16);
+    c[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load_seg(const float* Bm, int k, int v0, int V, float* c) {
+  const float* row = Bm + static_cast<size_t>(k) * V;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = (v0 + i < V) ? row[v0 + i] : 0.f;
+}
+
+__device__ __forceinline__ bool ranks_before(float xa, int ia, float xb, int ib) {
+  return xa > xb || (xa == xb && ia < ib);
+}
+
+// value of rank k-1 among the n values of `vals` (ties ranked by position);
+// every thread calls it, the result is broadcast through `out`
+__device__ void kth_largest(const float* vals, int n, int k, float* out) {
+  for (int i = threadIdx.x; i < n; i += kTopkThreads) {
+    const float m = vals[i];
+    int rank = 0;
+    for (int u = 0; u < n; ++u) rank += (vals[u] > m) || (vals[u] == m && u < i);
+    if (rank == k - 1) *out = m;
+  }
+  if (threadIdx.x == 0 && n < k) *out = kNegInf;
+  __syncthreads();
+}
+
+template <typename WT>
+__global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile_cols) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.x, j = blockIdx.y;
+  const int k = a.topk;
+  const size_t row = static_cast<size_t>(b) * a.gamma + j;
   __shared__ float arow_s[kMaxRank];
-  __shared__ float tmax[kMergeThreads];
-  __shared__ int cseg[kCandSegCap];
-  __shared__ float cval[kCandSegCap * kSeg];
-  __shared__ float csegmax[kCandSegCap];
-  __shared__ float sval[kSurvCap];
-  __shared__ int sidx[kSurvCap];
-  __shared__ int counter[2];
+  __shared__ float tmax[kTopkThreads];
+  __shared__ int tiles[kTileCap];
+  __shared__ int c1s[kCand1Cap];
+  __shared__ float c1v[kCand1Cap];
+  __shared__ int c2s[kCand2Cap];
+  __shared__ float ev[kCand2Cap * kSeg];
+  __shared__ int counter[3];
   __shared__ float theta[2];
   __shared__ float selv[kMaxTopk];
   __shared__ int seli[kMaxTopk];
 
-  const int k = a.topk;
-  const int prev = a.j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + a.j - 1];
+  const int prev = j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + j - 1];
   const WT* A = static_cast<const WT*>(a.A);
-  for (int i = tid; i < a.r; i += kMergeThreads) arow_s[i] = to_f32(A[static_cast<size_t>(prev) * a.r + i]);
-  const float* sm = a.segmax + static_cast<size_t>(b) * a.S;
+  for (int i = tid; i < a.r; i += kTopkThreads) arow_s[i] = to_f32(A[static_cast<size_t>(prev) * a.r + i]);
+  const float* pm = a.p_m + row * a.P;
+  const float* sm = a.segmax + row * a.S;
+  const float* urow = a.U + row * static_cast<size_t>(a.V);
   float mt = kNegInf;
-  for (int s = tid; s < a.S; s += kMergeThreads) mt = fmaxf(mt, sm[s]);
+  for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kTopkThreads) {
+    float v[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const int p = p0 + u * kTopkThreads + tid;
+      v[u] = p < a.Pn ? pm[p] : kNegInf;
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) mt = fmaxf(mt, v[u]);
+  }
   tmax[tid] = mt;
-  if (tid < 2) counter[tid] = 0;
+  if (tid < 3) counter[tid] = 0;
   __syncthreads();
-  {  // (1) theta0: the thread maximum of rank k-1
-    int rank = 0;
-    for (int u = 0; u < kMergeThreads; ++u) {
-      const float o = tmax[u];
-      rank += (o > mt) || (o == mt && u < tid);
+  kth_largest(tmax, kTopkThreads, k, &theta[0]);
+  const float th00 = theta[0];
+  // tiles that can hold a segment >= theta00
+  for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kTopkThreads) {
+    float v[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const int p = p0 + u * kTopkThreads + tid;
+      v[u] = p < a.Pn ? pm[p] : kNegInf;
     }
-    if (rank == k - 1) theta[0] = mt;
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      if (v[u] >= th00 && v[u] != kNegInf) {
+        const int slot = atomicAdd(&counter[0], 1);
+        if (slot < kTileCap) tiles[slot] = p0 + u * kTopkThreads + tid;
+      }
+    }
   }
   __syncthreads();
-  const float th0 = theta[0];
-  for (int s = tid; s < a.S; s += kMergeThreads) {
-    if (sm[s] >= th0) {
-      const int slot = atomicAdd(&counter[0], 1);
-      if (slot < kCandSegCap) cseg[slot] = s;
-    }
-  }
-  __syncthreads();
-  const int ncs = counter[0];
-  bool overflow = ncs > kCandSegCap;
+  const int nt = counter[0];
+  const int spt = tile_cols / kSeg;      // segments per tile
+  bool overflow = nt > kTileCap;
   if (!overflow) {
-    // (2) recompute the candidate segments
-    for (int e = tid; e < ncs * kSeg; e += kMergeThreads) {
-      const int v = cseg[e / kSeg] * kSeg + (e % kSeg);
-      cval[e] = v < a.V ? recompute_logit<WT>(a, arow_s, b, v) : kNegInf;
-    }
-    __syncthreads();
-    for (int c = tid; c < ncs; c += kMergeThreads) {
-      float m = kNegInf;
-      for (int i = 0; i < kSeg; ++i) m = fmaxf(m, cval[c * kSeg + i]);
-      csegmax[c] = m;
-    }
-    __syncthreads();
-    // (3) theta1: k-th largest candidate-segment maximum (fewer than k
-    // candidate segments only happens when every segment is a candidate)
-    if (tid < ncs) {
-      const float m = csegmax[tid];
-      int rank = 0;
-      for (int u = 0; u < ncs; ++u) rank += (csegmax[u] > m) || (csegmax[u] == m && u < tid);
-      if (rank == k - 1) theta[1] = m;
-    }
-    if (tid == 0 && ncs < k) theta[1] = kNegInf;
-    __syncthreads();
-    const float th1 = theta[1];
-    for (int e = tid; e < ncs * kSeg; e += kMergeThreads) {
-      const float x = cval[e];
-      if (x >= th1 && x != kNegInf) {
-        const int slot = atomicAdd(&counter[1], 1);
-        if (slot < kSurvCap) { sval[slot] = x; sidx[slot] = cseg[e / kSeg] * kSeg + (e % kSeg); }
+    for (int e = tid; e < nt * spt; e += kTopkThreads) {
+      const int s = tiles[e / spt] * spt + e % spt;
+      if (s < a.S) {
+        const float v = sm[s];
+        if (v >= th00) {
+          const int slot = atomicAdd(&counter[1], 1);
+          if (slot < kCand1Cap) { c1s[slot] = s; c1v[slot] = v; }
+        }
       }
     }
     __syncthreads();
-    const int ns = counter[1];
-    overflow = ns > kSurvCap;
+    const int n1 = counter[1];
+    overflow = n1 > kCand1Cap;
     if (!overflow) {
-      for (int s = tid; s < ns; s += kMergeThreads) {
-        int rank = 0;
-        for (int u = 0; u < ns; ++u) rank += ranks_before(sval[u], sidx[u], sval[s], sidx[s]);
-        if (rank < k) { selv[rank] = sval[s]; seli[rank] = sidx[s]; }
+      kth_largest(c1v, n1, k, &theta[1]);
+      const float th = theta[1];
+      for (int i = tid; i < n1; i += kTopkThreads) {
+        if (c1v[i] >= th) {
+          const int slot = atomicAdd(&counter[2], 1);
+          if (slot < kCand2Cap) c2s[slot] = c1s[i];
+        }
+      }
+      __syncthreads();
+      const int n2 = counter[2];
+      overflow = n2 > kCand2Cap;
+      if (!overflow) {
+        const WT* Bm = static_cast<const WT*>(a.Bm);
+        const int q = tid % kSliceThreads;
+        for (int c0 = 0; c0 < n2; c0 += kTopkThreads / kSliceThreads) {
+          const int c = c0 + tid / kSliceThreads;
+          const bool on = c < n2;          // uniform across each 16-lane slice group
+          const int v0 = on ? c2s[c] * kSeg : 0;
+          float acc[kSeg];
+#pragma unroll
+          for (int i = 0; i < kSeg; ++i) acc[i] = 0.f;
+          if (on) {
+            // rows q, q+16, ... of Bm, issued kRowBatch at a time
+            for (int k0 = q; k0 < a.r; k0 += kRowBatch * kSliceThreads) {
+              float col[kRowBatch][kSeg];
+#pragma unroll
+              for (int u = 0; u < kRowBatch; ++u) {
+                const int kk = k0 + u * kSliceThreads;
+                if (kk < a.r) load_seg(Bm, kk, v0, a.V, col[u]);
+                else {
+#pragma unroll
+                  for (int i = 0; i < kSeg; ++i) col[u][i] = 0.f;
+                }
+              }
+#pragma unroll
+              for (int u = 0; u < kRowBatch; ++u) {
+                const int kk = k0 + u * kSliceThreads;
+                const float am = kk < a.r ? arow_s[kk] : 0.f;
+#pragma unroll
+                for (int i = 0; i < kSeg; ++i) acc[i] = fmaf(am, col[u][i], acc[i]);
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < kSeg; ++i) {
+#pragma unroll
+            for (int o = 1; o < kSliceThreads; o <<= 1) acc[i] += __shfl_xor(acc[i], o);
+          }
+          if (on && q == 0) {
+#pragma unroll
+            for (int i = 0; i < kSeg; ++i)
+              ev[c * kSeg + i] = (v0 + i < a.V) ? urow[v0 + i] + acc[i] : kNegInf;
+          }
+        }
+        __syncthreads();
+        const int ne = n2 * kSeg;
+        for (int e = tid; e < ne; e += kTopkThreads) {
+          const float x = ev[e];
+          const int ix = c2s[e / kSeg] * kSeg + e % kSeg;
+          int rank = 0;
+          for (int u = 0; u < ne; ++u) rank += ranks_before(ev[u], c2s[u / kSeg] * kSeg + u % kSeg, x, ix);
+          if (rank < k) { selv[rank] = x; seli[rank] = ix; }
+        }
       }
     }
   }
@@ -409,8 +513,8 @@ __global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
     for (int t = 0; t < k; ++t) {
       float bv = kNegInf;
       int bi = 0x7fffffff;
-      for (int v = tid; v < a.V; v += kMergeThreads) {
-        const float x = recompute_logit<WT>(a, arow_s, b, v);
+      for (int v = tid; v < a.V; v += kTopkThreads) {
+        const float x = recompute_logit<WT>(a, arow_s, urow, v);
         if (ranks_before(lastv, lasti, x, v) && ranks_before(x, v, bv, bi)) { bv = x; bi = v; }
       }
 #pragma unroll
@@ -434,7 +538,7 @@ __global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
   }
   __syncthreads();
   if (tid == 0) {
-    const size_t o = (static_cast<size_t>(b) * a.gamma + a.j) * k;
+    const size_t o = row * k;
     float ssum = 0.f;
     for (int t = 0; t < k; ++t) ssum += __expf(selv[t] - selv[0]);
     const float inv = 1.0f / ssum;
@@ -457,9 +561,14 @@ static void launch_bf16(const StepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((markov_step_bf16<RG, KS>), grid, dim3(kWave * KS), 0, s, a);
 }
 
+static int partial_count(const StepArgs& a, bool bf16) {
+  return static_cast<int>(bf16 ? (a.V + kMarkovTile - 1) / kMarkovTile
+                               : (a.V + kMarkovTileF32 - 1) / kMarkovTileF32);
+}
+
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
+  a.Pn = partial_count(a, bf16);
   if (bf16) {
-    a.Pn = static_cast<int>((a.V + kMarkovTile - 1) / kMarkovTile);
     // request blocking and r-split: small batches split r over 4 waves so a
     // step has enough waves in flight; large batches reuse each transposed Bm
     // block for 4 request groups.
@@ -474,14 +583,22 @@ hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
       launch_bf16<4, 1>(a, s);
     }
   } else {
-    a.Pn = static_cast<int>((a.V + kMarkovTileF32 - 1) / kMarkovTileF32);
     const dim3 grid(a.Pn, a.B);
     hipLaunchKernelGGL(markov_step_f32, grid, dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (bf16) hipLaunchKernelGGL(markov_merge<uint16_t>, dim3(a.B), dim3(kMergeThreads), 0, s, a);
-  else hipLaunchKernelGGL(markov_merge<float>, dim3(a.B), dim3(kMergeThreads), 0, s, a);
+  hipLaunchKernelGGL(markov_merge, dim3(a.B), dim3(kMergeThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_markov_topk(StepArgs a, bool bf16, hipStream_t s) {
+  a.Pn = partial_count(a, bf16);
+  const dim3 grid(a.B, a.gamma);
+  if (bf16)
+    hipLaunchKernelGGL(markov_topk<uint16_t>, grid, dim3(kTopkThreads), 0, s, a, kMarkovTile);
+  else
+    hipLaunchKernelGGL(markov_topk<float>, grid, dim3(kTopkThreads), 0, s, a, kMarkovTileF32);
   return hipGetLastError();
 }
 

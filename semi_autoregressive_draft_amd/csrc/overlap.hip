@@ -18,8 +18,11 @@
 namespace dspark {
 
 constexpr int kOvThreads = 512;
-constexpr int kOvWaves = kOvThreads / kWave;
+constexpr int kSplitThreads = 256;
 constexpr int kTauThreads = 256;
+constexpr int kSplitChunk = 2048;      // elements per workgroup on the split path
+constexpr int kSplitRowsMax = 1024;    // at and above this many rows, one workgroup per row
+constexpr int kFusedFinishRows = 64;   // up to this many rows, one workgroup finishes rows and tau
 
 __device__ __forceinline__ void online_add4(LseState& st, f32x4 x) {
   const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -30,31 +33,52 @@ __device__ __forceinline__ void online_add4(LseState& st, f32x4 x) {
   st.s += (__expf(x[0] - st.m) + __expf(x[1] - st.m)) + (__expf(x[2] - st.m) + __expf(x[3] - st.m));
 }
 
-__device__ float block_lse(LseState st, LseState* red) {
+template <int NW>
+__device__ LseState block_lse_state(LseState st, LseState* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) st = lse_merge(st, shfl_xor(st, o));
   if (lane == 0) red[w] = st;
   __syncthreads();
   LseState r = red[0];
-  for (int i = 1; i < kOvWaves; ++i) r = lse_merge(r, red[i]);
+  for (int i = 1; i < NW; ++i) r = lse_merge(r, red[i]);
   __syncthreads();
-  return r.m + logf(r.s);
+  return r;
 }
 
+template <int NW>
 __device__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_sum(v);
   if (lane == 0) red[w] = v;
   __syncthreads();
   float r = 0.f;
-  for (int i = 0; i < kOvWaves; ++i) r += red[i];
+  for (int i = 0; i < NW; ++i) r += red[i];
+  __syncthreads();
   return r;
 }
 
+__device__ __forceinline__ float sum_exp_min4(f32x4 t, f32x4 d, float Lt, float Ld) {
+  return (__expf(fminf(t[0] - Lt, d[0] - Ld)) + __expf(fminf(t[1] - Lt, d[1] - Ld))) +
+         (__expf(fminf(t[2] - Lt, d[2] - Ld)) + __expf(fminf(t[3] - Lt, d[3] - Ld)));
+}
+
+// candidate-set overlap of one row: sum over the k candidates of min(p, q')
+__device__ float candidate_overlap(const OverlapArgs& a, int row, float Lt) {
+  float s = 0.f;
+  for (int c = threadIdx.x; c < a.k; c += blockDim.x) {
+    const size_t ci = static_cast<size_t>(row) * a.k + c;
+    const float p = __expf(a.teacher[static_cast<size_t>(row) * a.V + a.cand_idx[ci]] - Lt);
+    s += fminf(p, a.cand_prob[ci]);
+  }
+  return s;
+}
+
+// ---- one workgroup per row (many rows) ------------------------------------
 __global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
-  __shared__ LseState red_l[kOvWaves];
-  __shared__ float red_f[kOvWaves];
+  constexpr int NW = kOvThreads / kWave;
+  __shared__ LseState red_l[NW];
+  __shared__ float red_f[NW];
   const int row = blockIdx.x, tid = threadIdx.x;
   if (a.valid && !a.valid[row]) {
     if (tid == 0) a.alpha[row] = 0.f;
@@ -71,36 +95,118 @@ __global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
       online_add4(lt, tp[e]);
       online_add4(ld, dp[e]);
     }
-    const float Lt = block_lse(lt, red_l);
-    const float Ld = block_lse(ld, red_l);
+    const LseState rt = block_lse_state<NW>(lt, red_l);
+    const LseState rd = block_lse_state<NW>(ld, red_l);
+    const float Lt = rt.m + logf(rt.s), Ld = rd.m + logf(rd.s);
     float s = 0.f;
     const int last = (n4 - 1 - tid) >= 0 ? tid + ((n4 - 1 - tid) / kOvThreads) * kOvThreads : -1;
-    for (int e = last; e >= 0; e -= kOvThreads) {
-      const f32x4 t = tp[e], d = dp[e];
-      s += (__expf(fminf(t[0] - Lt, d[0] - Ld)) + __expf(fminf(t[1] - Lt, d[1] - Ld))) +
-           (__expf(fminf(t[2] - Lt, d[2] - Ld)) + __expf(fminf(t[3] - Lt, d[3] - Ld)));
-    }
-    total = block_sum(s, red_f);
+    for (int e = last; e >= 0; e -= kOvThreads) s += sum_exp_min4(tp[e], dp[e], Lt, Ld);
+    total = block_sum<NW>(s, red_f);
   } else {
     LseState lt{kNegInf, 0.f};
     for (int e = tid; e < n4; e += kOvThreads) online_add4(lt, tp[e]);
-    const float Lt = block_lse(lt, red_l);
-    float s = 0.f;
-    if (tid < a.k) {
-      const size_t c = static_cast<size_t>(row) * a.k + tid;
-      const float p = __expf(a.teacher[row * V + a.cand_idx[c]] - Lt);
-      s = fminf(p, a.cand_prob[c]);
-    }
-    total = block_sum(s, red_f);
+    const LseState rt = block_lse_state<NW>(lt, red_l);
+    total = block_sum<NW>(candidate_overlap(a, row, rt.m + logf(rt.s)), red_f);
   }
   if (tid == 0) a.alpha[row] = fminf(fmaxf(total, 0.f), 1.f);
 }
 
-// tau per block and per-workgroup partial sums for the aggregates
-__global__ __launch_bounds__(kTauThreads) void tau_blocks(OverlapArgs a) {
+// ---- several workgroups per row (few rows) ---------------------------------
+// pass 1: per (row, chunk) online states of teacher and draft
+__global__ __launch_bounds__(kSplitThreads) void overlap_split_stats(OverlapArgs a) {
+  constexpr int NW = kSplitThreads / kWave;
+  __shared__ LseState red_l[NW];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  if (a.valid && !a.valid[row]) return;
+  const size_t V = static_cast<size_t>(a.V);
+  const int e0 = c * a.chunk4, e1 = min(e0 + a.chunk4, a.V / 4);
+  const f32x4* tp = reinterpret_cast<const f32x4*>(a.teacher + row * V);
+  LseState lt{kNegInf, 0.f}, ld{kNegInf, 0.f};
+  for (int e = e0 + tid; e < e1; e += kSplitThreads) online_add4(lt, tp[e]);
+  if (a.draft) {
+    const f32x4* dp = reinterpret_cast<const f32x4*>(a.draft + row * V);
+    for (int e = e0 + tid; e < e1; e += kSplitThreads) online_add4(ld, dp[e]);
+  }
+  const LseState rt = block_lse_state<NW>(lt, red_l);
+  const LseState rd = block_lse_state<NW>(ld, red_l);
+  if (tid == 0) {
+    float* st = a.ws_split + (static_cast<size_t>(row) * a.nchunk + c) * 5;
+    st[0] = rt.m; st[1] = rt.s; st[2] = rd.m; st[3] = rd.s;
+  }
+}
+
+// log-normalisers of one row from its chunk states, merged by one wave: lane
+// c folds chunks c, c+64, ... in order, then a fixed xor tree (all lanes
+// return the same values)
+__device__ void row_normalisers(const OverlapArgs& a, int row, float& Lt, float& Ld) {
+  const int lane = threadIdx.x & 63;
+  LseState lt{kNegInf, 0.f}, ld{kNegInf, 0.f};
+  const float* st = a.ws_split + static_cast<size_t>(row) * a.nchunk * 5;
+  for (int c = lane; c < a.nchunk; c += kWave) {
+    lt = lse_merge(lt, LseState{st[c * 5 + 0], st[c * 5 + 1]});
+    ld = lse_merge(ld, LseState{st[c * 5 + 2], st[c * 5 + 3]});
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    lt = lse_merge(lt, shfl_xor(lt, o));
+    ld = lse_merge(ld, shfl_xor(ld, o));
+  }
+  Lt = lt.m + logf(lt.s);
+  Ld = ld.m + logf(ld.s);
+}
+
+// pass 2 (dense): per (row, chunk) sum of exp(min(t - L_p, d - L_q))
+__global__ __launch_bounds__(kSplitThreads) void overlap_split_sum(OverlapArgs a) {
+  constexpr int NW = kSplitThreads / kWave;
+  __shared__ float L[2];
+  __shared__ float red_f[NW];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  if (a.valid && !a.valid[row]) return;
+  if (tid < kWave) {
+    float lt, ld;
+    row_normalisers(a, row, lt, ld);
+    if (tid == 0) { L[0] = lt; L[1] = ld; }
+  }
+  __syncthreads();
+  const float Lt = L[0], Ld = L[1];
+  const size_t V = static_cast<size_t>(a.V);
+  const int e0 = c * a.chunk4, e1 = min(e0 + a.chunk4, a.V / 4);
+  const f32x4* tp = reinterpret_cast<const f32x4*>(a.teacher + row * V);
+  const f32x4* dp = reinterpret_cast<const f32x4*>(a.draft + row * V);
+  float s = 0.f;
+  for (int e = e0 + tid; e < e1; e += kSplitThreads) s += sum_exp_min4(tp[e], dp[e], Lt, Ld);
+  const float tot = block_sum<NW>(s, red_f);
+  if (tid == 0) a.ws_split[(static_cast<size_t>(row) * a.nchunk + c) * 5 + 4] = tot;
+}
+
+// pass 3: one wave per row folds the chunk sums (dense) or gathers the
+// candidates (candidate mode)
+__global__ __launch_bounds__(kWave) void overlap_split_finish(OverlapArgs a) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  if (a.valid && !a.valid[row]) {
+    if (lane == 0) a.alpha[row] = 0.f;
+    return;
+  }
+  float s = 0.f;
+  if (a.draft) {
+    const float* st = a.ws_split + static_cast<size_t>(row) * a.nchunk * 5;
+    for (int c = lane; c < a.nchunk; c += kWave) s += st[c * 5 + 4];
+  } else {
+    float lt, ld;
+    row_normalisers(a, row, lt, ld);
+    s = candidate_overlap(a, row, lt);
+  }
+  s = wave_sum(s);
+  if (lane == 0) a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
+}
+
+// tau per block and per-workgroup partial sums for the aggregates (a full
+// workgroup of kTauThreads threads calls it for its range of blocks)
+__device__ void tau_range(const OverlapArgs& a, int blk) {
   __shared__ double red[kTauThreads / kWave][2 * kMaxGamma + 2];
+  __shared__ double tot[2 * kMaxGamma + 2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n = blockIdx.x * kTauThreads + tid;
+  const int n = blk * kTauThreads + tid;
   const int G = a.gamma;
   double acc[kMaxGamma], cnt[kMaxGamma];
   double tsum = 0.0, tcnt = 0.0;
@@ -139,8 +245,39 @@ __global__ __launch_bounds__(kTauThreads) void tau_blocks(OverlapArgs a) {
   if (tid < F) {
     double s = 0.0;
     for (int i = 0; i < kTauThreads / kWave; ++i) s += red[i][tid];
-    a.ws_acc[static_cast<size_t>(blockIdx.x) * F + tid] = s;
+    if (a.nblk > 1) a.ws_acc[static_cast<size_t>(blk) * F + tid] = s;
+    else tot[tid] = s;
   }
+  if (a.nblk == 1) {  // one workgroup holds every block: finish here
+    __syncthreads();
+    if (tid < G && a.accept_rate_at) a.accept_rate_at[tid] = tot[G + tid] > 0.0 ? tot[tid] / tot[G + tid] : 0.0;
+    if (tid == 0 && a.tau_mean) *a.tau_mean = tot[2 * G + 1] > 0.0 ? tot[2 * G] / tot[2 * G + 1] : 0.0;
+  }
+}
+
+__global__ __launch_bounds__(kTauThreads) void tau_blocks(OverlapArgs a) { tau_range(a, blockIdx.x); }
+
+// few rows: one workgroup finishes every row (a wave per row) and then tau
+__global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapArgs a) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rows = a.N * a.gamma;
+  for (int row = w; row < rows; row += kTauThreads / kWave) {
+    float s = 0.f;
+    if (!a.valid || a.valid[row]) {
+      if (a.draft) {
+        const float* st = a.ws_split + static_cast<size_t>(row) * a.nchunk * 5;
+        for (int c = lane; c < a.nchunk; c += kWave) s += st[c * 5 + 4];
+      } else {
+        float lt, ld;
+        row_normalisers(a, row, lt, ld);
+        s = candidate_overlap(a, row, lt);
+      }
+      s = wave_sum(s);
+    }
+    if (lane == 0) a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
+  }
+  __syncthreads();   // alpha of every row written by this workgroup
+  tau_range(a, 0);
 }
 
 __global__ __launch_bounds__(64) void tau_finish(OverlapArgs a) {
@@ -158,14 +295,35 @@ __global__ __launch_bounds__(64) void tau_finish(OverlapArgs a) {
 
 int overlap_tau_blocks(int64_t N) { return static_cast<int>((N + kTauThreads - 1) / kTauThreads); }
 
+int overlap_split_chunks(int64_t rows, int64_t V) {
+  if (rows >= kSplitRowsMax) return 1;
+  const int64_t by_size = (V + kSplitChunk - 1) / kSplitChunk;
+  const int64_t by_rows = (2 * kSplitRowsMax + rows - 1) / rows;
+  return static_cast<int>(by_size < by_rows ? by_size : by_rows);
+}
+
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s) {
   a.nblk = overlap_tau_blocks(a.N);
-  hipLaunchKernelGGL(overlap_rows, dim3(a.N * a.gamma), dim3(kOvThreads), 0, s, a);
+  const int rows = a.N * a.gamma;
+  if (a.nchunk <= 1) {
+    hipLaunchKernelGGL(overlap_rows, dim3(rows), dim3(kOvThreads), 0, s, a);
+  } else {
+    const int n4 = a.V / 4;
+    a.chunk4 = (n4 + a.nchunk - 1) / a.nchunk;
+    const dim3 grid(a.nchunk, rows);
+    hipLaunchKernelGGL(overlap_split_stats, grid, dim3(kSplitThreads), 0, s, a);
+    if (a.draft) hipLaunchKernelGGL(overlap_split_sum, grid, dim3(kSplitThreads), 0, s, a);
+    if (rows <= kFusedFinishRows && a.nblk == 1) {
+      hipLaunchKernelGGL(overlap_split_finish_tau, dim3(1), dim3(kTauThreads), 0, s, a);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(overlap_split_finish, dim3(rows), dim3(kWave), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tau_blocks, dim3(a.nblk), dim3(kTauThreads), 0, s, a);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.nblk == 1) return e;
   hipLaunchKernelGGL(tau_finish, dim3(1), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -103,7 +103,8 @@ def test_config1_tiny_fp32_end_to_end():
 def test_config2_qwen3_4b_single_request_full():
     require_gpu()
     cfg = dict(synth.CONFIGS["c2_qwen3_4b_b1"])
-    inp = synth.propose_inputs(**cfg, topk=16)  # top-16 rides along; greedy tokens unchanged
+    cfg["topk"] = 16                            # top-16 rides along; greedy tokens unchanged
+    inp = synth.propose_inputs(**cfg)
     p = _device_path(inp, "dense")
     p.run()
     torch.cuda.synchronize()

@@ -200,9 +200,11 @@ def _check_tau(got, alpha_raw, valid):
     assert abs(mean - mean_ref) < ALPHA_ABS
 
 
-@pytest.mark.parametrize("sigma", [0.5, 1.0, 2.0])
-def test_overlap_dense_parity(sigma):
-    N, V = 9, 5000
+@pytest.mark.parametrize("sigma,N", [(0.5, 9), (1.0, 9), (2.0, 9),
+                                     (1.0, 20),    # split rows, per-row finish kernel
+                                     (1.0, 200)])  # one workgroup per row, several tau blocks
+def test_overlap_dense_parity(sigma, N):
+    V = 5000
     teacher, draft = synth.overlap_inputs(N, V, sigma, seed=1)
     valid = synth.validity(N, seed=1, trunc_frac=0.4, n_dummy=1)
     got = _run_overlap(teacher, draft=draft, valid=valid)
@@ -217,9 +219,9 @@ def test_overlap_identical_rows_give_tau_eight():
     assert np.allclose(alpha, 1.0, atol=2e-5) and np.allclose(tau, 8.0, atol=2e-4)
 
 
-@pytest.mark.parametrize("k", [16, 64])
-def test_overlap_candidates_parity(k):
-    N, V = 5, 5000
+@pytest.mark.parametrize("k,N", [(16, 5), (64, 5), (16, 20), (16, 300)])
+def test_overlap_candidates_parity(k, N):
+    V = 5000
     teacher, _ = synth.overlap_inputs(N, V, 1.0, seed=3)
     teacher = teacher * 3.0                           # peakier teacher: visible overlap
     idx, prob = synth.candidates(N, V, k, seed=3)
