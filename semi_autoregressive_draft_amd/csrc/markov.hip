@@ -36,6 +36,56 @@ constexpr int kMarkovTile = 128;   // vocabulary columns per bf16 step tile
 constexpr int kMarkovTileF32 = 256;
 constexpr int kSeg = 8;            // vocabulary columns per top-k segment
 
+// ---------------------------------------------------------------------------
+// Fold of one request's per-tile partials of position j by a 256-thread
+// workgroup: thread t takes tiles t, t+256, ... (loads issued kFoldBatch at a
+// time), then a fixed xor tree and waves 0..3 in order; writes x_j, U~_j[x_j]
+// and lse_j.
+constexpr int kMergeThreads = 256;
+constexpr int kFoldBatch = 4;
+
+__device__ void fold_request(const StepArgs& a, int b) {
+  __shared__ LseState red_l[kMergeThreads / kWave];
+  __shared__ ArgState red_a[kMergeThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  LseState ls{kNegInf, 0.f};
+  ArgState as{kNegInf, 0x7fffffff, 0.f};
+  const size_t base = (static_cast<size_t>(b) * a.gamma + a.j) * a.P;
+  for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kMergeThreads) {
+    LseState l[kFoldBatch];
+    ArgState g[kFoldBatch];
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) {
+      const int p = p0 + u * kMergeThreads + tid;
+      if (p < a.Pn) {
+        l[u] = LseState{a.p_m[base + p], a.p_s[base + p]};
+        g[u] = ArgState{a.p_score[base + p], a.p_idx[base + p], a.p_x[base + p]};
+      } else {
+        l[u] = LseState{kNegInf, 0.f};
+        g[u] = ArgState{kNegInf, 0x7fffffff, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldBatch; ++u) { ls = lse_merge(ls, l[u]); as = arg_merge(as, g[u]); }
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    ls = lse_merge(ls, shfl_xor(ls, o));
+    as = arg_merge(as, shfl_xor(as, o));
+  }
+  if (lane == 0) { red_l[w] = ls; red_a[w] = as; }
+  __syncthreads();
+  if (tid == 0) {
+    LseState l = red_l[0];
+    ArgState s = red_a[0];
+    for (int i = 1; i < kMergeThreads / kWave; ++i) { l = lse_merge(l, red_l[i]); s = arg_merge(s, red_a[i]); }
+    const int row = b * a.gamma + a.j;
+    a.tokens[row] = s.idx;
+    if (a.tok_logit) a.tok_logit[row] = s.x;
+    if (a.lse) a.lse[row] = l.m + logf(l.s);
+  }
+}
+
 template <int RG, int KS>
 __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -103,17 +153,19 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
         for (int c = 0; c < 8; ++c) red[w - 1][rg][c][lane] = acc[rg][c];
     }
     __syncthreads();
-    if (w != 0) return;
+    if (w == 0) {
 #pragma unroll
-    for (int s = 0; s < KS - 1; ++s)
+      for (int s = 0; s < KS - 1; ++s)
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
+        for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[rg][c] += red[s][rg][c][lane];
+          for (int c = 0; c < 8; ++c) acc[rg][c] += red[s][rg][c][lane];
+    }
   }
 
   // ---- epilogue (wave 0): add U_j, sample noise, local stats, partials ----
   const int P = a.P;
+  if (w == 0) {
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
@@ -184,6 +236,7 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
       }
     }
   }
+  }  // w == 0
 }
 
 // ---------------------------------------------------------------------------
@@ -247,55 +300,9 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel (on the sequential path): one workgroup of 256 threads per
-// request folds the per-tile partials of position j in a fixed order (thread t
-// takes tiles t, t+256, ... with its loads issued together; then a fixed xor
-// tree and waves 0..3 in order) and writes x_j, U~_j[x_j] and lse_j.
-constexpr int kMergeThreads = 256;
-constexpr int kFoldBatch = 4;
-
-__global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.x;
-  __shared__ LseState red_l[4];
-  __shared__ ArgState red_a[4];
-  LseState ls{kNegInf, 0.f};
-  ArgState as{kNegInf, 0x7fffffff, 0.f};
-  const size_t base = (static_cast<size_t>(b) * a.gamma + a.j) * a.P;
-  for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kMergeThreads) {
-    LseState l[kFoldBatch];
-    ArgState g[kFoldBatch];
-#pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) {
-      const int p = p0 + u * kMergeThreads + tid;
-      if (p < a.Pn) {
-        l[u] = LseState{a.p_m[base + p], a.p_s[base + p]};
-        g[u] = ArgState{a.p_score[base + p], a.p_idx[base + p], a.p_x[base + p]};
-      } else {
-        l[u] = LseState{kNegInf, 0.f};
-        g[u] = ArgState{kNegInf, 0x7fffffff, 0.f};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) { ls = lse_merge(ls, l[u]); as = arg_merge(as, g[u]); }
-  }
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    ls = lse_merge(ls, shfl_xor(ls, o));
-    as = arg_merge(as, shfl_xor(as, o));
-  }
-  if (lane == 0) { red_l[w] = ls; red_a[w] = as; }
-  __syncthreads();
-  if (tid == 0) {
-    LseState l = red_l[0];
-    ArgState s = red_a[0];
-    for (int i = 1; i < 4; ++i) { l = lse_merge(l, red_l[i]); s = arg_merge(s, red_a[i]); }
-    const int row = b * a.gamma + a.j;
-    a.tokens[row] = s.idx;
-    if (a.tok_logit) a.tok_logit[row] = s.x;
-    if (a.lse) a.lse[row] = l.m + logf(l.s);
-  }
-}
+// Merge kernel (on the sequential path): one workgroup per request folds the
+// per-tile partials of position j (see fold_request).
+__global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) { fold_request(a, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // Top-k kernel (off the sequential path): one workgroup per (request,
@@ -319,7 +326,6 @@ constexpr int kTileCap = 128;
 constexpr int kCand1Cap = 512;
 constexpr int kCand2Cap = 64;
 constexpr int kSliceThreads = 16;   // threads sharing one segment's r-loop
-constexpr int kRowBatch = 8;        // Bm rows in flight per thread
 
 template <typename WT>
 __device__ float recompute_logit(const StepArgs& a, const float* arow_s, const float* urow, int v) {
@@ -330,20 +336,38 @@ __device__ float recompute_logit(const StepArgs& a, const float* arow_s, const f
   return urow[v] + bias;
 }
 
-// 8 consecutive columns v0..v0+7 of Bm row k (columns >= V read as 0)
-__device__ __forceinline__ void load_seg(const uint16_t* Bm, int k, int v0, int V, float* c) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(Bm + static_cast<size_t>(k) * V + v0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[2 * i] = __uint_as_float(w[i] << 16);
-    c[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+// 8 consecutive columns v0..v0+7 of Bm row k (columns >= V read as 0), kept
+// packed until use: one 16-byte load for bf16 (V % 8 == 0 there)
+template <typename WT> struct SegRows;
+template <> struct SegRows<uint16_t> {
+  static constexpr int kBatch = 16;
+  typedef u32x4 Raw;
+  static __device__ __forceinline__ Raw load(const uint16_t* Bm, int k, int v0, int V) {
+    return *reinterpret_cast<const u32x4*>(Bm + static_cast<size_t>(k) * V + v0);
   }
-}
-__device__ __forceinline__ void load_seg(const float* Bm, int k, int v0, int V, float* c) {
-  const float* row = Bm + static_cast<size_t>(k) * V;
+  static __device__ __forceinline__ void unpack(const Raw& w, float* c) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = (v0 + i < V) ? row[v0 + i] : 0.f;
-}
+    for (int i = 0; i < 4; ++i) {
+      c[2 * i] = __uint_as_float(w[i] << 16);
+      c[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct SegRows<float> {
+  static constexpr int kBatch = 8;
+  struct Raw { float c[8]; };
+  static __device__ __forceinline__ Raw load(const float* Bm, int k, int v0, int V) {
+    Raw r;
+    const float* row = Bm + static_cast<size_t>(k) * V;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.c[i] = (v0 + i < V) ? row[v0 + i] : 0.f;
+    return r;
+  }
+  static __device__ __forceinline__ void unpack(const Raw& w, float* c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = w.c[i];
+  }
+};
 
 __device__ __forceinline__ bool ranks_before(float xa, int ia, float xb, int ib) {
   return xa > xb || (xa == xb && ia < ib);
@@ -355,6 +379,7 @@ __device__ void kth_largest(const float* vals, int n, int k, float* out) {
   for (int i = threadIdx.x; i < n; i += kTopkThreads) {
     const float m = vals[i];
     int rank = 0;
+#pragma unroll 16
     for (int u = 0; u < n; ++u) rank += (vals[u] > m) || (vals[u] == m && u < i);
     if (rank == k - 1) *out = m;
   }
@@ -386,36 +411,36 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
   const float* pm = a.p_m + row * a.P;
   const float* sm = a.segmax + row * a.S;
   const float* urow = a.U + row * static_cast<size_t>(a.V);
+  // per-thread maximum of the tile maxima; the first kKeep of this thread's
+  // tiles stay in registers for the filter below
+  constexpr int kKeep = 8;
+  float keep[kKeep];
   float mt = kNegInf;
-  for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kTopkThreads) {
-    float v[kFoldBatch];
 #pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) {
-      const int p = p0 + u * kTopkThreads + tid;
-      v[u] = p < a.Pn ? pm[p] : kNegInf;
-    }
-#pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) mt = fmaxf(mt, v[u]);
+  for (int u = 0; u < kKeep; ++u) {
+    const int p = u * kTopkThreads + tid;
+    keep[u] = p < a.Pn ? pm[p] : kNegInf;
   }
+#pragma unroll
+  for (int u = 0; u < kKeep; ++u) mt = fmaxf(mt, keep[u]);
+  for (int p = kKeep * kTopkThreads + tid; p < a.Pn; p += kTopkThreads) mt = fmaxf(mt, pm[p]);
   tmax[tid] = mt;
   if (tid < 3) counter[tid] = 0;
   __syncthreads();
   kth_largest(tmax, kTopkThreads, k, &theta[0]);
   const float th00 = theta[0];
   // tiles that can hold a segment >= theta00
-  for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kTopkThreads) {
-    float v[kFoldBatch];
 #pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) {
-      const int p = p0 + u * kTopkThreads + tid;
-      v[u] = p < a.Pn ? pm[p] : kNegInf;
+  for (int u = 0; u < kKeep; ++u) {
+    if (keep[u] >= th00 && keep[u] != kNegInf) {
+      const int slot = atomicAdd(&counter[0], 1);
+      if (slot < kTileCap) tiles[slot] = u * kTopkThreads + tid;
     }
-#pragma unroll
-    for (int u = 0; u < kFoldBatch; ++u) {
-      if (v[u] >= th00 && v[u] != kNegInf) {
-        const int slot = atomicAdd(&counter[0], 1);
-        if (slot < kTileCap) tiles[slot] = p0 + u * kTopkThreads + tid;
-      }
+  }
+  for (int p = kKeep * kTopkThreads + tid; p < a.Pn; p += kTopkThreads) {
+    if (pm[p] >= th00) {
+      const int slot = atomicAdd(&counter[0], 1);
+      if (slot < kTileCap) tiles[slot] = p;
     }
   }
   __syncthreads();
@@ -423,13 +448,20 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
   const int spt = tile_cols / kSeg;      // segments per tile
   bool overflow = nt > kTileCap;
   if (!overflow) {
-    for (int e = tid; e < nt * spt; e += kTopkThreads) {
-      const int s = tiles[e / spt] * spt + e % spt;
-      if (s < a.S) {
-        const float v = sm[s];
-        if (v >= th00) {
+    for (int e0 = 0; e0 < nt * spt; e0 += kFoldBatch * kTopkThreads) {
+      float v[kFoldBatch];
+      int sg[kFoldBatch];
+#pragma unroll
+      for (int u = 0; u < kFoldBatch; ++u) {
+        const int e = e0 + u * kTopkThreads + tid;
+        sg[u] = e < nt * spt ? tiles[e / spt] * spt + e % spt : a.S;
+        v[u] = sg[u] < a.S ? sm[sg[u]] : kNegInf;
+      }
+#pragma unroll
+      for (int u = 0; u < kFoldBatch; ++u) {
+        if (sg[u] < a.S && v[u] >= th00) {
           const int slot = atomicAdd(&counter[1], 1);
-          if (slot < kCand1Cap) { c1s[slot] = s; c1v[slot] = v; }
+          if (slot < kCand1Cap) { c1s[slot] = sg[u]; c1v[slot] = v[u]; }
         }
       }
     }
@@ -459,24 +491,23 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
 #pragma unroll
           for (int i = 0; i < kSeg; ++i) acc[i] = 0.f;
           if (on) {
-            // rows q, q+16, ... of Bm, issued kRowBatch at a time
-            for (int k0 = q; k0 < a.r; k0 += kRowBatch * kSliceThreads) {
-              float col[kRowBatch][kSeg];
+            // rows q, q+16, ... of Bm, issued RB at a time in packed form
+            constexpr int RB = SegRows<WT>::kBatch;
+            for (int k0 = q; k0 < a.r; k0 += RB * kSliceThreads) {
+              typename SegRows<WT>::Raw raw[RB];
 #pragma unroll
-              for (int u = 0; u < kRowBatch; ++u) {
+              for (int u = 0; u < RB; ++u) {
                 const int kk = k0 + u * kSliceThreads;
-                if (kk < a.r) load_seg(Bm, kk, v0, a.V, col[u]);
-                else {
-#pragma unroll
-                  for (int i = 0; i < kSeg; ++i) col[u][i] = 0.f;
-                }
+                raw[u] = SegRows<WT>::load(Bm, kk < a.r ? kk : 0, v0, a.V);
               }
 #pragma unroll
-              for (int u = 0; u < kRowBatch; ++u) {
+              for (int u = 0; u < RB; ++u) {
                 const int kk = k0 + u * kSliceThreads;
                 const float am = kk < a.r ? arow_s[kk] : 0.f;
+                float col[kSeg];
+                SegRows<WT>::unpack(raw[u], col);
 #pragma unroll
-                for (int i = 0; i < kSeg; ++i) acc[i] = fmaf(am, col[u][i], acc[i]);
+                for (int i = 0; i < kSeg; ++i) acc[i] = fmaf(am, col[i], acc[i]);
               }
             }
           }
@@ -497,7 +528,11 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
           const float x = ev[e];
           const int ix = c2s[e / kSeg] * kSeg + e % kSeg;
           int rank = 0;
-          for (int u = 0; u < ne; ++u) rank += ranks_before(ev[u], c2s[u / kSeg] * kSeg + u % kSeg, x, ix);
+          for (int c = 0; c < n2; ++c) {       // 8 columns of one candidate segment per step
+            const int v0 = c2s[c] * kSeg;
+#pragma unroll
+            for (int i = 0; i < kSeg; ++i) rank += ranks_before(ev[c * kSeg + i], v0 + i, x, ix);
+          }
           if (rank < k) { selv[rank] = x; seli[rank] = ix; }
         }
       }
@@ -537,14 +572,14 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
     }
   }
   __syncthreads();
-  if (tid == 0) {
+  if (w == 0) {  // softmax over the k candidates at T = 1, summed in rank order
     const size_t o = row * k;
+    const float e = lane < k ? __expf(selv[lane] - selv[0]) : 0.f;
     float ssum = 0.f;
-    for (int t = 0; t < k; ++t) ssum += __expf(selv[t] - selv[0]);
-    const float inv = 1.0f / ssum;
-    for (int t = 0; t < k; ++t) {
-      a.topk_idx[o + t] = seli[t];
-      a.topk_prob[o + t] = __expf(selv[t] - selv[0]) * inv;
+    for (int t = 0; t < k; ++t) ssum += __shfl(e, t);
+    if (lane < k) {
+      a.topk_idx[o + lane] = seli[lane];
+      a.topk_prob[o + lane] = e / ssum;
     }
   }
 }

@@ -63,10 +63,11 @@ __device__ __forceinline__ float sum_exp_min4(f32x4 t, f32x4 d, float Lt, float 
          (__expf(fminf(t[2] - Lt, d[2] - Ld)) + __expf(fminf(t[3] - Lt, d[3] - Ld)));
 }
 
-// candidate-set overlap of one row: sum over the k candidates of min(p, q')
-__device__ float candidate_overlap(const OverlapArgs& a, int row, float Lt) {
+// candidate-set overlap of one row: this thread's share (candidates first,
+// first + stride, ...) of the sum over the k candidates of min(p, q')
+__device__ float candidate_overlap(const OverlapArgs& a, int row, float Lt, int first, int stride) {
   float s = 0.f;
-  for (int c = threadIdx.x; c < a.k; c += blockDim.x) {
+  for (int c = first; c < a.k; c += stride) {
     const size_t ci = static_cast<size_t>(row) * a.k + c;
     const float p = __expf(a.teacher[static_cast<size_t>(row) * a.V + a.cand_idx[ci]] - Lt);
     s += fminf(p, a.cand_prob[ci]);
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
     LseState lt{kNegInf, 0.f};
     for (int e = tid; e < n4; e += kOvThreads) online_add4(lt, tp[e]);
     const LseState rt = block_lse_state<NW>(lt, red_l);
-    total = block_sum<NW>(candidate_overlap(a, row, rt.m + logf(rt.s)), red_f);
+    total = block_sum<NW>(candidate_overlap(a, row, rt.m + logf(rt.s), tid, kOvThreads), red_f);
   }
   if (tid == 0) a.alpha[row] = fminf(fmaxf(total, 0.f), 1.f);
 }
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kWave) void overlap_split_finish(OverlapArgs a) {
   } else {
     float lt, ld;
     row_normalisers(a, row, lt, ld);
-    s = candidate_overlap(a, row, lt);
+    s = candidate_overlap(a, row, lt, lane, kWave);
   }
   s = wave_sum(s);
   if (lane == 0) a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapA
       } else {
         float lt, ld;
         row_normalisers(a, row, lt, ld);
-        s = candidate_overlap(a, row, lt);
+        s = candidate_overlap(a, row, lt, lane, kWave);
       }
       s = wave_sum(s);
     }
