@@ -86,7 +86,113 @@ __device__ void fold_request(const StepArgs& a, int b) {
   }
 }
 
-template <int RG, int KS>
+// ---------------------------------------------------------------------------
+// Step epilogue for one wave: lane (g, n) holds requests req0 + 16 rg + 4 g + ii
+// (ii < 4) for the 8 consecutive columns vcol..vcol+7 of this tile.  Per
+// request: add U_j (optionally dump U~), take the 16-lane group maximum M, sum
+// exp(U~ - M) (one exponential per element), draw the Gumbel noise when
+// sampling, reduce (best score, index, U~ there), and write one partial per
+// request plus the 8-column segment maxima for top-k.  A scheduling barrier
+// between requests keeps one request's working set live at a time.
+// U_j for the lane's requests and columns, loaded before the r-loop so that its
+// latency hides under the Bm stream: up[rg][ii][half] = U[b, j, vcol + 4 half ..]
+template <int RG>
+__device__ __forceinline__ void prefetch_u(const StepArgs& a, int req0, int vcol, bool vok, int g,
+                                           f32x4 (&up)[RG][4][2]) {
+  const size_t V = static_cast<size_t>(a.V);
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = req0 + 16 * rg + 4 * g + ii;
+      if ((b < a.B) && vok) {
+        const float* urow = a.U + (static_cast<size_t>(b) * a.gamma + a.j) * V + vcol;
+        up[rg][ii][0] = *reinterpret_cast<const f32x4*>(urow);
+        up[rg][ii][1] = *reinterpret_cast<const f32x4*>(urow + 4);
+      } else {
+        up[rg][ii][0] = up[rg][ii][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+}
+
+template <int RG, bool SAMPLE>
+__device__ __forceinline__ void epilogue_store(const StepArgs& a, const f32x4 (&acc)[RG][8],
+                                               const f32x4 (&up)[RG][4][2],
+                                               int req0, int tile, int vcol, bool vok, int g, int n) {
+  const size_t V = static_cast<size_t>(a.V);
+#pragma unroll
+  for (int q = 0; q < 4 * RG; ++q) {
+    const int b = req0 + 16 * (q >> 2) + 4 * g + (q & 3);
+    const bool live = (b < a.B) && vok;
+    float x[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = acc[q >> 2][c][q & 3];
+    const size_t row = static_cast<size_t>(b) * a.gamma + a.j;
+    if (live) {
+      const f32x4 u0 = up[q >> 2][q & 3][0], u1 = up[q >> 2][q & 3][1];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) { x[c] += u0[c]; x[c + 4] += u1[c]; }
+      if (a.logits_out) {
+        float* orow = a.logits_out + row * V + vcol;
+        *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[4], x[5], x[6], x[7]};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) x[c] = kNegInf;
+    }
+    float m8 = x[0];
+#pragma unroll
+    for (int c = 1; c < 8; ++c) m8 = fmaxf(m8, x[c]);
+    if (a.segmax && live) a.segmax[row * a.S + vcol / kSeg] = m8;   // one top-k segment
+    float M = m8;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float ssum = 0.f;
+    if (live) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ssum += __expf(x[c] - M);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ssum += __shfl_xor(ssum, o);
+
+    float score[8];
+    if constexpr (SAMPLE) {
+      if (live) {
+        const uint64_t sd = a.seeds[b];
+        const uint32_t k0 = static_cast<uint32_t>(sd), k1 = static_cast<uint32_t>(sd >> 32);
+        const Philox4 r0 = philox4x32_10(vcol >> 2, a.j, a.off_lo, a.off_hi, k0, k1);
+        const Philox4 r1 = philox4x32_10((vcol >> 2) + 1, a.j, a.off_lo, a.off_hi, k0, k1);
+        const uint32_t wd[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) score[c] = x[c] * a.inv_temp + gumbel_from_word(wd[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) score[c] = kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) score[c] = x[c];
+    }
+    ArgState as{score[0], live ? vcol : 0x7fffffff, x[0]};
+#pragma unroll
+    for (int c = 1; c < 8; ++c)
+      if (score[c] > as.score) as = ArgState{score[c], vcol + c, x[c]};
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) as = arg_merge(as, shfl_xor(as, o));
+    if (n == 0 && b < a.B) {
+      const size_t pq = row * a.P + tile;
+      a.p_m[pq] = M;
+      a.p_s[pq] = ssum;
+      a.p_score[pq] = as.score;
+      a.p_idx[pq] = as.idx;
+      a.p_x[pq] = as.x;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int RG, int KS, bool SAMPLE>
 __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -113,6 +219,8 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[rg][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 up[RG][4][2];
+  if (w == 0) prefetch_u<RG>(a, req0, vcol, vok, g, up);
 
   const int kper = a.r / KS;
   const int kbeg = w * kper;
@@ -163,80 +271,107 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
     }
   }
 
-  // ---- epilogue (wave 0): add U_j, sample noise, local stats, partials ----
-  const int P = a.P;
-  if (w == 0) {
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int b = req0 + 16 * rg + 4 * g + ii;
-      const bool live = (b < a.B) && vok;
-      float x[8];
-      if (live) {
-        const float* urow = a.U + (static_cast<size_t>(b) * a.gamma + a.j) * V + vcol;
-        const f32x4 u0 = *reinterpret_cast<const f32x4*>(urow);
-        const f32x4 u1 = *reinterpret_cast<const f32x4*>(urow + 4);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          x[c] = acc[rg][c][ii] + u0[c];
-          x[c + 4] = acc[rg][c + 4][ii] + u1[c];
-        }
-        if (a.logits_out) {
-          float* orow = a.logits_out + (static_cast<size_t>(b) * a.gamma + a.j) * V + vcol;
-          *reinterpret_cast<f32x4*>(orow) = f32x4{x[0], x[1], x[2], x[3]};
-          *reinterpret_cast<f32x4*>(orow + 4) = f32x4{x[4], x[5], x[6], x[7]};
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[c] = kNegInf;
-      }
-      float m8 = x[0];
-#pragma unroll
-      for (int c = 1; c < 8; ++c) m8 = fmaxf(m8, x[c]);
-      float s8 = 0.f;
-      if (live) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s8 += __expf(x[c] - m8);
-      }
-      LseState ls{m8, s8};
+  if (w == 0) epilogue_store<RG, SAMPLE>(a, acc, up, req0, tile, vcol, vok, g, n);
+}
 
-      float score[8];
-      if (a.sample && live) {
-        const uint64_t sd = a.seeds[b];
-        const uint32_t k0 = static_cast<uint32_t>(sd), k1 = static_cast<uint32_t>(sd >> 32);
-        const Philox4 r0 = philox4x32_10(vcol >> 2, a.j, a.off_lo, a.off_hi, k0, k1);
-        const Philox4 r1 = philox4x32_10((vcol >> 2) + 1, a.j, a.off_lo, a.off_hi, k0, k1);
-        const uint32_t wd[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) score[c] = x[c] * a.inv_temp + gumbel_from_word(wd[c]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) score[c] = x[c];
-      }
-      ArgState as{score[0], live ? vcol : 0x7fffffff, x[0]};
-#pragma unroll
-      for (int c = 1; c < 8; ++c)
-        if (score[c] > as.score) as = ArgState{score[c], vcol + c, x[c]};
+// ---------------------------------------------------------------------------
+// Batched bf16 step kernel (B > 16).  A workgroup of 4 waves owns one tile of
+// 128 columns for 64*RGW requests.  Bm is read once per tile: in each round
+// of 128 rows, wave w loads rows [32w, 32w+32) of the round for the 128 columns
+// (the same 16-byte loads as above), transposes them in registers and writes
+// the eight B operands to LDS; after a barrier every wave applies all 32 B
+// operands of the round to its RGW groups of 16 requests (A operands gathered
+// from A[x_{j-1}]).  Rounds are double-buffered in LDS with a register
+// prefetch of the next round's rows.  The epilogue is the same as above.
+template <int RGW, bool SAMPLE>
+__global__ __launch_bounds__(256) void markov_step_batched(StepArgs a) {
+  __shared__ u32x4 bop_s[2][4][8][kWave];   // [buffer][chunk][column c][lane]: 64 KB
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int tile = blockIdx.x;
+  const int vcol = tile * kMarkovTile + 8 * n;
+  const bool vok = vcol < a.V;
+  const int req0 = blockIdx.y * (64 * RGW) + w * (16 * RGW);
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm);
+  const size_t V = static_cast<size_t>(a.V);
 
-      // the lane's 8 columns are one top-k segment
-      if (a.segmax && live) a.segmax[(static_cast<size_t>(b) * a.gamma + a.j) * a.S + vcol / kSeg] = m8;
+  const uint16_t* arow[RGW];
+  bool bok[RGW];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        ls = lse_merge(ls, shfl_xor(ls, o));
-        as = arg_merge(as, shfl_xor(as, o));
-      }
-      if (n == 0 && b < a.B) {
-        const size_t q = (static_cast<size_t>(b) * a.gamma + a.j) * P + tile;
-        a.p_m[q] = ls.m;
-        a.p_s[q] = ls.s;
-        a.p_score[q] = as.score;
-        a.p_idx[q] = as.idx;
-        a.p_x[q] = as.x;
+  for (int rg = 0; rg < RGW; ++rg) {
+    const int b = req0 + 16 * rg + n;
+    bok[rg] = b < a.B;
+    const int prev = !bok[rg] ? 0 : (a.j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + a.j - 1]);
+    arow[rg] = A + static_cast<size_t>(prev) * a.r;
+  }
+  f32x4 acc[RGW][8];
+#pragma unroll
+  for (int rg = 0; rg < RGW; ++rg)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[rg][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // rows of round `rd` that this wave loads: k = 128 rd + 32 w + 8 g + i
+  const uint16_t* bcol = Bm + vcol;
+  const int nrounds = (a.r + 127) / 128;
+  auto load_round = [&](int rd, u32x4* rows) {
+    const int kc = 128 * rd + 32 * w;
+    const bool on = vok && kc < a.r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      rows[i] = on ? *reinterpret_cast<const u32x4*>(bcol + static_cast<size_t>(kc + 8 * g + i) * V)
+                   : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto store_round = [&](int buf, const u32x4* rows) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 op;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) op[p] = __builtin_amdgcn_perm(rows[2 * p + 1][c >> 1], rows[2 * p][c >> 1], sel);
+      bop_s[buf][w][c][lane] = op;
+    }
+  };
+  // A operands of chunk q (32 rows of r) for this wave's request groups;
+  // fetched one chunk ahead of their use
+  const int nchunks = a.r / 32;
+  auto load_a = [&](int q, u32x4* av) {
+#pragma unroll
+    for (int rg = 0; rg < RGW; ++rg)
+      av[rg] = (bok[rg] && q < nchunks) ? *reinterpret_cast<const u32x4*>(arow[rg] + 32 * q + 8 * g)
+                                        : u32x4{0u, 0u, 0u, 0u};
+  };
+  u32x4 rows[8];
+  u32x4 av_next[RGW];
+  load_round(0, rows);
+  load_a(0, av_next);
+  f32x4 up[RGW][4][2];
+  prefetch_u<RGW>(a, req0, vcol, vok, g, up);
+  store_round(0, rows);
+  __syncthreads();
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int buf = rd & 1;
+    if (rd + 1 < nrounds) load_round(rd + 1, rows);
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int q = 4 * rd + ch;
+      if (q >= nchunks) break;                         // uniform: r % 32 == 0
+      u32x4 av[RGW];
+#pragma unroll
+      for (int rg = 0; rg < RGW; ++rg) av[rg] = av_next[rg];
+      load_a(q + 1, av_next);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 bo = bop_s[buf][ch][c][lane];
+#pragma unroll
+        for (int rg = 0; rg < RGW; ++rg)
+          acc[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[rg]), as_bf16x8(bo), acc[rg][c], 0, 0, 0);
       }
     }
+    if (rd + 1 < nrounds) store_round(buf ^ 1, rows);
+    __syncthreads();
   }
-  }  // w == 0
+  epilogue_store<RGW, SAMPLE>(a, acc, up, req0, tile, vcol, vok, g, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -593,7 +728,15 @@ size_t markov_segments(int64_t V) { return static_cast<size_t>((V + kSeg - 1) / 
 template <int RG, int KS>
 static void launch_bf16(const StepArgs& a, hipStream_t s) {
   const dim3 grid((a.V + kMarkovTile - 1) / kMarkovTile, (a.B + 16 * RG - 1) / (16 * RG));
-  hipLaunchKernelGGL((markov_step_bf16<RG, KS>), grid, dim3(kWave * KS), 0, s, a);
+  if (a.sample) hipLaunchKernelGGL((markov_step_bf16<RG, KS, true>), grid, dim3(kWave * KS), 0, s, a);
+  else hipLaunchKernelGGL((markov_step_bf16<RG, KS, false>), grid, dim3(kWave * KS), 0, s, a);
+}
+
+template <int RGW>
+static void launch_batched(const StepArgs& a, hipStream_t s) {
+  const dim3 grid((a.V + kMarkovTile - 1) / kMarkovTile, (a.B + 64 * RGW - 1) / (64 * RGW));
+  if (a.sample) hipLaunchKernelGGL((markov_step_batched<RGW, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((markov_step_batched<RGW, false>), grid, dim3(256), 0, s, a);
 }
 
 static int partial_count(const StepArgs& a, bool bf16) {
@@ -611,11 +754,12 @@ hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
       if (a.r % 128 == 0) launch_bf16<1, 4>(a, s);
       else if (a.r % 64 == 0) launch_bf16<1, 2>(a, s);
       else launch_bf16<1, 1>(a, s);
-    } else if (a.B <= 32) {
-      if (a.r % 64 == 0) launch_bf16<2, 2>(a, s);
-      else launch_bf16<2, 1>(a, s);
+    } else if (a.B <= 64) {
+      launch_batched<1>(a, s);
+    } else if (a.B <= 128) {
+      launch_batched<2>(a, s);
     } else {
-      launch_bf16<4, 1>(a, s);
+      launch_batched<4>(a, s);
     }
   } else {
     const dim3 grid(a.Pn, a.B);
