@@ -60,7 +60,7 @@ def stage_work(B, gamma, H, V, r, topk, overlap, wbytes=2):
 
 def lm_head_kernel_name(B, gamma, H):
     M = B * gamma
-    return "lm_head_skinny_bf16" if (M <= 16 and M * (H + 8) * 2 <= 64 * 1024) else "lm_head_tiled_bf16"
+    return "lm_head_skinny_bf16" if (M <= 16 and M * (H + 8) * 2 <= 64 * 1024) else "lm_head_gemm_bf16"
 
 
 def source_digest(*names):

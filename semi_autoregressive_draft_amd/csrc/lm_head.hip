@@ -8,7 +8,7 @@
 namespace dspark {
 
 // ---------------------------------------------------------------------------
-// Skinny path, M <= 16 (one or a few requests): HBM-bound on W_lm.  The whole
+// Skinny path, M <= 12 (one or a few requests): HBM-bound on W_lm.  The whole
 // h (M rows, padded stride to spread LDS banks) sits in LDS; each wave streams
 // 16 vocabulary rows of W_lm at a time straight from HBM into the A operand of
 // v_mfma_f32_16x16x32_bf16 (row n = lane%16, 8 consecutive k per lane), with h
@@ -72,90 +72,154 @@ __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// Tiled path, M > 16: 128 (vocabulary) x 128 (rows of h) tiles, K steps of 64,
-// 4 waves in a 2 x 2 layout with 64 x 64 each (4 x 4 MFMA 16x16x32 tiles).
-// Operands are staged through LDS (rows padded by 16 bytes against bank
-// conflicts), double-buffered with a register prefetch of the next K step.
-// The A operand is W (vocabulary rows), the B operand h, so each lane stores
-// 4 consecutive vocabulary entries.
-constexpr int kTV = 128, kTM = 128, kTK = 64, kLd = kTK + 8;
+// Tiled path (larger M): the bound moves from HBM to MFMA (2MHV flops over
+// 2VH bytes of W_lm).  Workgroup tile 256 (vocabulary) x 256 (rows of h), K in
+// stages of 32, 4 waves in a 2 x 2 layout, each wave 128 x 128 as a 4 x 4 grid
+// of v_mfma_f32_32x32x16_bf16 tiles (8 LDS operand reads feed 16 MFMAs of 32
+// cycles).
+//
+// Operands move global -> LDS by DMA (global_load_lds_dwordx4: each wave
+// instruction fills 1 KB of LDS in lane order) into a ring of 4 stages, so
+// loads run 3 stages ahead of the MFMAs without staging registers.  A stage
+// holds 256 rows x 64 bytes of W_lm and of h; LDS "lines" of 128 bytes hold two
+// rows, and 16-byte chunk slots are XOR-swizzled by the line index, so that
+// both the DMA writes (8 lanes per 128 contiguous global bytes) and the MFMA
+// operand reads (8 consecutive rows per 8 lanes) touch all banks once.
+//
+// Tile order is XCD-aware: workgroup L runs on XCD L % 8, and the k-th
+// workgroup of an XCD takes vocabulary tile 8 (k / MT) + L % 8 and row tile
+// k % MT, so the MT row tiles that share one W_lm tile run back to back on the
+// same XCD and reuse it from that XCD's L2 (W_lm is read from HBM about once).
+constexpr int kGV = 256, kGM = 256, kGK = 32, kGStages = 4;
+constexpr int kGStageBytes = (kGV + kGM) * kGK * 2;                 // 32 KB
+constexpr size_t kGemmLds = static_cast<size_t>(kGStages) * kGStageBytes;
 
-__global__ __launch_bounds__(256) void lm_head_tiled_bf16(
+// LDS byte offset of (row, 16-byte chunk c < 4) inside one 256-row operand block
+__device__ __forceinline__ int swz(int row, int c) {
+  const int line = row >> 1;
+  return line * 128 + ((((row & 1) << 2) | c) ^ (line & 7)) * 16;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+__global__ __launch_bounds__(256, 1) void lm_head_gemm_bf16(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, float* __restrict__ U,
-    int M, int H, int V) {
-  __shared__ uint16_t Ws[2][kTV * kLd];
-  __shared__ uint16_t Hs[2][kTM * kLd];
+    int M, int H, int V, int VT, int MT) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char gsm[];
+  const int L = blockIdx.x, kx = L >> 3;
+  const int vt = (kx / MT) * 8 + (L & 7), mt = kx % MT;
+  if (vt >= VT) return;                                 // whole workgroup
+  const int v0 = vt * kGV, m0 = mt * kGM;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, n = lane & 15;
   const int wv = w & 1, wm = w >> 1;
-  const int v0 = blockIdx.x * kTV, m0 = blockIdx.y * kTM;
-  const int nkt = (H + kTK - 1) / kTK;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int nst = (H + kGK - 1) / kGK;
 
-  // global -> register staging: 4 chunks of 16 bytes per operand per thread
-  u32x4 rw[4], rh[4];
-  auto gload = [&](int kt) {
+  // DMA issue for stage st: wave w fills LDS lines [64 w', ...) of the W block
+  // (instructions 0..3) and of the h block (4..7); lane i of an instruction
+  // writes slot i of that 1 KB, i.e. line = 8 q + i / 8 and slot = i % 8, and
+  // loads the (row, chunk) that the swizzle places there.
+  auto issue = [&](int st) {
+    unsigned char* base = gsm + (st % kGStages) * kGStageBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int id = tid + 256 * q;
-      const int row = id >> 3, kk = kt * kTK + (id & 7) * 8;
-      const bool kok = kk < H;
-      const int vr = v0 + row, mr = m0 + row;
-      rw[q] = (kok && vr < V) ? *reinterpret_cast<const u32x4*>(W + static_cast<size_t>(vr) * H + kk)
-                              : u32x4{0u, 0u, 0u, 0u};
-      rh[q] = (kok && mr < M) ? *reinterpret_cast<const u32x4*>(h + static_cast<size_t>(mr) * H + kk)
-                              : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < 8; ++q) {
+      const bool isW = q < 4;
+      const int line = (w * 4 + (q & 3)) * 8 + (lane >> 3);        // 0..127
+      const int slot = (lane & 7) ^ (line & 7);
+      const int row = 2 * line + (slot >> 2), c = slot & 3;
+      const int k = st * kGK + 8 * c;
+      const int gr = (isW ? v0 : m0) + row;
+      const bool ok = st < nst && k < H && gr < (isW ? V : M);
+      const uint16_t* src = ok ? (isW ? W : h) + static_cast<size_t>(gr) * H + k
+                               : (isW ? W : h);                       // any valid address
+      unsigned char* dst = base + (isW ? 0 : kGV * kGK * 2) + (w * 4 + (q & 3)) * 1024;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<void*>(dst), 16, 0, 0);
+      if (!ok) {}  // zero-fill below
     }
   };
-  auto sstore = [&](int buf) {
+  // rows past V / M and chunks past H must read as zero: the DMA above loads a
+  // valid but unrelated address there, so such lanes patch their slot to zero
+  // after the data has landed (only ragged edge tiles take this path)
+  const bool edge = (v0 + kGV > V) || (m0 + kGM > M) || (H % kGK != 0);
+  auto zero_fill = [&](int st) {
+    unsigned char* base = gsm + (st % kGStages) * kGStageBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int id = tid + 256 * q;
-      const int row = id >> 3, kk = (id & 7) * 8;
-      *reinterpret_cast<u32x4*>(&Ws[buf][row * kLd + kk]) = rw[q];
-      *reinterpret_cast<u32x4*>(&Hs[buf][row * kLd + kk]) = rh[q];
+    for (int q = 0; q < 8; ++q) {
+      const bool isW = q < 4;
+      const int line = (w * 4 + (q & 3)) * 8 + (lane >> 3);
+      const int slot = (lane & 7) ^ (line & 7);
+      const int row = 2 * line + (slot >> 2), c = slot & 3;
+      const int k = st * kGK + 8 * c;
+      const int gr = (isW ? v0 : m0) + row;
+      if (!(k < H && gr < (isW ? V : M)))
+        *reinterpret_cast<u32x4*>(base + (isW ? 0 : kGV * kGK * 2) + (w * 4 + (q & 3)) * 1024 + lane * 16) =
+            u32x4{0u, 0u, 0u, 0u};
     }
   };
 
-  f32x4 acc[4][4];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
+    for (int jn = 0; jn < 4; ++jn)
 #pragma unroll
-    for (int ks = 0; ks < kTK / 32; ++ks) {
-      u32x4 a[4], bb[4];
+      for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.f;
+
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int st = 0; st < nst; ++st) {
+    // this wave's DMA for stage st has landed once at most the later stages'
+    // 8 instructions each are outstanding
+    if (st + 2 < nst) wait_vmcnt<16>();
+    else if (st + 1 < nst) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    if (edge) {
+      zero_fill(st);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    // every wave's part of stage st landed (each waited for its own DMA above);
+    // stage st-1 fully consumed (its LDS reads fed MFMAs issued before this
+    // point).  A bare barrier: a fenced one would also drain the DMA of the
+    // stages still in flight.
+    asm volatile("s_barrier" ::: "memory");
+    if (st + 3 < nst) issue(st + 3);
+    const unsigned char* wbase = gsm + (st % kGStages) * kGStageBytes;
+    const unsigned char* hbase = wbase + kGV * kGK * 2;
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      u32x4 a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(&Ws[buf][(wv * 64 + i * 16 + n) * kLd + ks * 32 + 8 * g]);
+        a[i] = *reinterpret_cast<const u32x4*>(wbase + swz(wv * 128 + i * 32 + l32, 2 * ks + hi));
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn)
-        bb[jn] = *reinterpret_cast<const u32x4*>(&Hs[buf][(wm * 64 + jn * 16 + n) * kLd + ks * 32 + 8 * g]);
+        b[jn] = *reinterpret_cast<const u32x4*>(hbase + swz(wm * 128 + jn * 32 + l32, 2 * ks + hi));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn)
-          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i]), as_bf16x8(bb[jn]),
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[jn]),
                                                                acc[i][jn], 0, 0, 0);
     }
-    if (kt + 1 < nkt) sstore(buf ^ 1);
-    __syncthreads();
   }
-  // D[4g + ii][n]: vocabulary v0 + wv*64 + i*16 + 4g + ii, row m0 + wm*64 + jn*16 + n
+  // D[row][col] of a 32x32 tile: lane holds rows 8 (e/4) + 4 hi + (e%4), column l32.
+  // Rows are vocabulary entries, columns are rows of h: each group of 4
+  // accumulators is one 16-byte store of 4 consecutive vocabulary entries.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int vo = v0 + wv * 64 + i * 16 + 4 * g;
-    if (vo >= V) continue;
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
-      const int m = m0 + wm * 64 + jn * 16 + n;
-      if (m < M) *reinterpret_cast<f32x4*>(U + static_cast<size_t>(m) * V + vo) = acc[i][jn];
+      const int m = m0 + wm * 128 + jn * 32 + l32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int v = v0 + wv * 128 + i * 32 + 8 * e4 + 4 * hi;
+        if (v < V)
+          *reinterpret_cast<f32x4*>(U + static_cast<size_t>(m) * V + v) =
+              f32x4{acc[i][jn][4 * e4], acc[i][jn][4 * e4 + 1], acc[i][jn][4 * e4 + 2], acc[i][jn][4 * e4 + 3]};
+      }
     }
   }
 }
@@ -209,9 +273,16 @@ hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, in
                        lm_head_skinny_lds(M, H), s, static_cast<const uint16_t*>(h),
                        static_cast<const uint16_t*>(w), U, (int)M, (int)H, (int)V);
   } else {
-    const dim3 grid((V + kTV - 1) / kTV, (M + kTM - 1) / kTM);
-    hipLaunchKernelGGL(lm_head_tiled_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(h),
-                       static_cast<const uint16_t*>(w), U, (int)M, (int)H, (int)V);
+    const int VT = static_cast<int>((V + kGV - 1) / kGV), MT = static_cast<int>((M + kGM - 1) / kGM);
+    const int grid = 8 * ((VT + 7) / 8) * MT;
+    // opt in to more than 64 KB of dynamic LDS (a host-side attribute call)
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(lm_head_gemm_bf16),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(kGemmLds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lm_head_gemm_bf16, dim3(grid), dim3(256), kGemmLds, s,
+                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w), U, (int)M,
+                       (int)H, (int)V, VT, MT);
   }
   return hipGetLastError();
 }

@@ -23,6 +23,7 @@ pytestmark = pytest.mark.gpu
     (13, 2560, 1000, "bf16"),     # tiled path, ragged M
     (130, 296, 5000, "bf16"),     # tiled, ragged M/K/V tiles
     (448, 320, 3000, "bf16"),
+    (600, 136, 2104, "bf16"),     # several row tiles, K tail, vocabulary tail inside an XCD group
 ])
 def test_lm_head_parity(M, H, V, wdtype):
     dev = require_gpu()
