@@ -81,10 +81,10 @@ __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
 // Operands move global -> LDS by DMA (global_load_lds_dwordx4: each wave
 // instruction fills 1 KB of LDS in lane order) into a ring of 4 stages, so
 // loads run 3 stages ahead of the MFMAs without staging registers.  A stage
-// holds 256 rows x 64 bytes of W_lm and of h; LDS "lines" of 128 bytes hold two
-// rows, and 16-byte chunk slots are XOR-swizzled by the line index, so that
-// both the DMA writes (8 lanes per 128 contiguous global bytes) and the MFMA
-// operand reads (8 consecutive rows per 8 lanes) touch all banks once.
+// holds 256 rows x 64 bytes of W_lm and of h; LDS lines of 256 bytes hold four
+// rows, and 16-byte chunk slots are XOR-swizzled by the line index, so that the
+// DMA writes stay contiguous and the MFMA operand reads (16 consecutive rows
+// per 16 lanes) touch every bank once.
 //
 // Tile order is XCD-aware: workgroup L runs on XCD L % 8, and the k-th
 // workgroup of an XCD takes vocabulary tile 8 (k / MT) + L % 8 and row tile
@@ -94,10 +94,13 @@ constexpr int kGV = 256, kGM = 256, kGK = 32, kGStages = 4;
 constexpr int kGStageBytes = (kGV + kGM) * kGK * 2;                 // 32 KB
 constexpr size_t kGemmLds = static_cast<size_t>(kGStages) * kGStageBytes;
 
-// LDS byte offset of (row, 16-byte chunk c < 4) inside one 256-row operand block
+// LDS byte offset of (row, 16-byte chunk c < 4) inside one 256-row operand
+// block: 256-byte lines of 4 rows, slots XOR-swizzled by the line index so that
+// 16 consecutive rows at one chunk fall in 16 distinct 16-byte bank groups
+// (64 banks of 4 bytes)
 __device__ __forceinline__ int swz(int row, int c) {
-  const int line = row >> 1;
-  return line * 128 + ((((row & 1) << 2) | c) ^ (line & 7)) * 16;
+  const int line = row >> 2;
+  return line * 256 + ((((row & 3) << 2) | c) ^ (line & 3)) * 16;
 }
 
 template <int N>
@@ -116,18 +119,18 @@ __global__ __launch_bounds__(256, 1) void lm_head_gemm_bf16(
   const int l32 = lane & 31, hi = lane >> 5;
   const int nst = (H + kGK - 1) / kGK;
 
-  // DMA issue for stage st: wave w fills LDS lines [64 w', ...) of the W block
-  // (instructions 0..3) and of the h block (4..7); lane i of an instruction
-  // writes slot i of that 1 KB, i.e. line = 8 q + i / 8 and slot = i % 8, and
-  // loads the (row, chunk) that the swizzle places there.
+  // DMA issue for stage st: wave w fills 1 KB blocks w*4 .. w*4+3 of the W
+  // operand block (instructions 0..3) and of the h block (4..7); lane i of an
+  // instruction writes byte 16 i of its 1 KB, i.e. line 4 blk + i / 16 and slot
+  // i % 16, and loads the (row, chunk) that the swizzle places there.
   auto issue = [&](int st) {
     unsigned char* base = gsm + (st % kGStages) * kGStageBytes;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const bool isW = q < 4;
-      const int line = (w * 4 + (q & 3)) * 8 + (lane >> 3);        // 0..127
-      const int slot = (lane & 7) ^ (line & 7);
-      const int row = 2 * line + (slot >> 2), c = slot & 3;
+      const int line = (w * 4 + (q & 3)) * 4 + (lane >> 4);        // 0..63
+      const int slot = (lane & 15) ^ (line & 3);
+      const int row = 4 * line + (slot >> 2), c = slot & 3;
       const int k = st * kGK + 8 * c;
       const int gr = (isW ? v0 : m0) + row;
       const bool ok = st < nst && k < H && gr < (isW ? V : M);
@@ -147,9 +150,9 @@ __global__ __launch_bounds__(256, 1) void lm_head_gemm_bf16(
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const bool isW = q < 4;
-      const int line = (w * 4 + (q & 3)) * 8 + (lane >> 3);
-      const int slot = (lane & 7) ^ (line & 7);
-      const int row = 2 * line + (slot >> 2), c = slot & 3;
+      const int line = (w * 4 + (q & 3)) * 4 + (lane >> 4);
+      const int slot = (lane & 15) ^ (line & 3);
+      const int row = 4 * line + (slot >> 2), c = slot & 3;
       const int k = st * kGK + 8 * c;
       const int gr = (isW ? v0 : m0) + row;
       if (!(k < H && gr < (isW ? V : M)))
