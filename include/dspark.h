@@ -90,6 +90,19 @@ dspark_status_t dspark_markov_propose_workspace(int64_t B, int64_t gamma, int64_
                                                 int32_t topk, size_t* bytes);
 
 /*
+ * How dspark_markov_propose will run the chain for these sizes on the current
+ * device: *resident_workgroups > 0 when one cooperative kernel keeps Bm on chip
+ * for all positions with that many workgroups (bf16, B = 1 with r = 64, 128 or
+ * 256, or B <= 16 with r = 256, when the share of Bm fits in registers and
+ * LDS), 0 when it runs one step kernel per position.  Environment:
+ * DSPARK_MARKOV_RESIDENT=0 disables the resident chain, DSPARK_MARKOV_WORKGROUPS=n
+ * caps its workgroups (each then holds more of Bm).  Results agree with the
+ * per-position path up to float32 summation order.  No device work.
+ */
+dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int64_t r, dspark_dtype_t wdt,
+                                           int32_t* resident_workgroups);
+
+/*
  * S2-S4 -- sequential Vanilla-Markov proposal.  [P1] Markov 顺序修正:
  * m_i = W_1[t_{i-1}], b_i = W_2 m_i, l_i = l_i^0 + b_i, with t_0 the anchor;
  * inference selects each token from l_i and feeds it to the next position.

@@ -26,6 +26,7 @@ _SIGNATURES = {
     "dspark_version": (C.c_char_p, []),
     "dspark_lm_head": (C.c_int, [_vp, _vp, C.c_int, _i64, _i64, _i64, _vp, _vp]),
     "dspark_markov_propose_workspace": (C.c_int, [_i64, _i64, _i64, _i32, C.POINTER(_sz)]),
+    "dspark_markov_propose_plan": (C.c_int, [_i64, _i64, _i64, C.c_int, C.POINTER(_i32)]),
     "dspark_markov_propose": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64,
                                         _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
@@ -117,6 +118,13 @@ def dspark_lm_head(h, w_lm, U, stream=None) -> None:
 def dspark_markov_propose_workspace(B: int, gamma: int, V: int, topk: int = 0) -> int:
     n = _sz(0)
     _check(lib().dspark_markov_propose_workspace(B, gamma, V, topk, C.byref(n)))
+    return n.value
+
+
+def dspark_markov_propose_plan(B: int, V: int, r: int, wdtype: int = BF16) -> int:
+    """Workgroups of the resident chain for these sizes (0: one step kernel per position)."""
+    n = _i32(0)
+    _check(lib().dspark_markov_propose_plan(B, V, r, wdtype, C.byref(n)))
     return n.value
 
 

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstdint>
 
 #include "dspark.h"
@@ -33,12 +34,22 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 constexpr int64_t kI32Max = 2147483647;
 
 // per (request, position): 5 partial arrays of one entry per vocabulary tile,
-// plus the segment maxima when top-k is asked for
+// one 8-byte argmax key, plus the segment maxima when top-k is asked for; one
+// block for the resident chain's wait tree
 size_t markov_ws_bytes(int64_t B, int64_t gamma, int64_t V, int32_t topk) {
   const size_t rows = static_cast<size_t>(B) * gamma;
-  size_t s = 5 * align_up(rows * markov_partials(V) * 4);
+  size_t s = 5 * align_up(rows * markov_partials(V) * 4) + align_up(rows * 8) + kSyncWords * 4;
   if (topk > 0) s += align_up(rows * markov_segments(V) * 4);
   return s;
+}
+
+// The resident chain where it applies (DSPARK_MARKOV_RESIDENT=0 turns it off,
+// DSPARK_MARKOV_WORKGROUPS caps its workgroups), else one launch per position.
+bool resident_chain(bool bf16, int B, int V, int r, int* nwg, size_t* lds) {
+  const char* res_env = std::getenv("DSPARK_MARKOV_RESIDENT");
+  const char* wg_env = std::getenv("DSPARK_MARKOV_WORKGROUPS");
+  return bf16 && !(res_env && res_env[0] == '0') &&
+         markov_resident_plan(B, V, r, wg_env ? std::atoi(wg_env) : 0, nwg, lds);
 }
 
 size_t overlap_ws_tau_bytes(int64_t N, int64_t gamma) {
@@ -87,6 +98,19 @@ extern "C" dspark_status_t dspark_markov_propose_workspace(int64_t B, int64_t ga
     return fail(DSPARK_EINVAL, "dspark_markov_propose_workspace: B, gamma, V must be positive, topk >= 0");
   if (V > kI32Max || B > kI32Max) return fail(DSPARK_EINVAL, "dspark_markov_propose_workspace: sizes too large");
   *bytes = markov_ws_bytes(B, gamma, V, topk);
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int64_t r,
+                                                      dspark_dtype_t wdt, int32_t* resident_workgroups) {
+  if (!resident_workgroups) return fail(DSPARK_EINVAL, "dspark_markov_propose_plan: resident_workgroups is NULL");
+  if (B <= 0 || V <= 0 || r <= 0 || V > kI32Max || B > kI32Max)
+    return fail(DSPARK_EINVAL, "dspark_markov_propose_plan: B, V, r must be positive");
+  int nwg = 0;
+  size_t lds = 0;
+  const bool res = resident_chain(wdt == DSPARK_BF16, static_cast<int>(B), static_cast<int>(V),
+                                  static_cast<int>(r), &nwg, &lds);
+  *resident_workgroups = res ? nwg : 0;
   return DSPARK_OK;
 }
 
@@ -152,20 +176,31 @@ extern "C" dspark_status_t dspark_markov_propose(
   a.p_s = reinterpret_cast<float*>(base + 4 * arr);
   a.P = static_cast<int>(P);
   a.S = static_cast<int>(markov_segments(V));
-  a.segmax = topk > 0 ? reinterpret_cast<float*>(base + 5 * arr) : nullptr;
+  const size_t keys = align_up(static_cast<size_t>(B) * gamma * 8);
+  a.best = reinterpret_cast<unsigned long long*>(base + 5 * arr);
+  a.sync = reinterpret_cast<unsigned*>(base + 5 * arr + keys);
+  a.segmax = topk > 0 ? reinterpret_cast<float*>(base + 5 * arr + keys + kSyncWords * 4) : nullptr;
   a.logits_out = logits_out;
   a.tok_logit = tok_logit;
   a.lse = lse;
   a.topk = topk;
   a.topk_idx = topk_idx;
   a.topk_prob = topk_prob;
-  for (int j = 0; j < gamma; ++j) {
-    a.j = j;
-    const hipError_t e = launch_markov_position(a, bf16, stream);
-    if (e != hipSuccess) return hip_status(e, fn);
+  int nwg = 0;
+  size_t lds = 0;
+  const bool resident = resident_chain(bf16, a.B, a.V, a.r, &nwg, &lds);
+  a.tile_cols = resident ? 64 : markov_tile_cols(bf16);
+  hipError_t e = launch_markov_begin(a, stream);
+  if (resident) {
+    if (e == hipSuccess) e = launch_markov_resident(a, a.sync, nwg, lds, stream);
+  } else {
+    for (int j = 0; j < gamma && e == hipSuccess; ++j) {
+      a.j = j;
+      e = launch_markov_position(a, bf16, stream);
+    }
   }
-  if (topk > 0) return hip_status(launch_markov_topk(a, bf16, stream), fn);
-  return DSPARK_OK;
+  if (e == hipSuccess) e = launch_markov_finish(a, bf16, stream);
+  return hip_status(e, fn);
 }
 
 // ---------------------------------------------------------------------------

@@ -12,12 +12,19 @@ constexpr int kMaxTopk = 32;
 constexpr int kMaxGamma = 16;
 constexpr int kMaxCand = 64;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
+constexpr int kSyncWords = 12 * 1024;   // 48 KB: the resident chain's wait tree (zero at launch)
 
 // Arguments of one Markov position (step + merge kernels).
 struct StepArgs {
   const float* U;          // [B, gamma, V]
   const int32_t* anchor;   // [B]
-  int32_t* tokens;         // [B, gamma] (read for j > 0, written by the merge)
+  int32_t* tokens;         // [B, gamma] (written after the chain)
+  // [B, gamma] running argmax keys: (orderable score << 32) | ~index, raised
+  // with atomic max by every (request, tile) of position j; the step kernel of
+  // position j+1 decodes its previous token from entry j
+  unsigned long long* best;
+  unsigned* sync;          // [kSyncWords] counters, flags and group keys of the resident chain
+  int tile_cols;           // vocabulary columns per partial (64 resident, 128 bf16, 256 f32)
   const void* A;           // [V, r]
   const void* Bm;          // [r, V]
   int B, gamma, V, r, j;
@@ -45,8 +52,12 @@ struct StepArgs {
 
 size_t markov_partials(int64_t V);
 size_t markov_segments(int64_t V);
+int markov_tile_cols(bool bf16);
+hipError_t launch_markov_begin(StepArgs a, hipStream_t s);
+bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg, size_t* lds);
+hipError_t launch_markov_resident(StepArgs a, unsigned* sync, int nwg, size_t lds, hipStream_t s);
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s);
-hipError_t launch_markov_topk(StepArgs a, bool bf16, hipStream_t s);
+hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s);
 
 hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
                           int64_t V, float* U, hipStream_t s);

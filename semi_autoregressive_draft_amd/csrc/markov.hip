@@ -9,14 +9,17 @@
 // (m_i = W_1[t_{i-1}], b_i = W_2 m_i, l_i = l_i^0 + b_i); "DSpark 论文精读", §2.2
 // (U~_j = U_j + b(x_{j-1}), x_j ~ softmax(U~_j)).
 //
-// One position is two launches: a step kernel that streams Bm and U_j once
-// for all requests and leaves one partial (max, sum-exp, best score/index) per
-// (request, vocabulary tile), and a merge kernel with one workgroup per
-// request that combines the partials in a fixed order and writes x_j (plus the
-// top-k candidate set when asked).  The merge of position j is what position
-// j+1's step kernel reads as its previous token.
+// One launch per position: the step kernel streams Bm and U_j once for all
+// requests and leaves one partial (max, sum-exp, best score/index) per
+// (request, vocabulary tile).  The argmax that the next position needs is also
+// folded on the fly: every (request, tile) raises a 64-bit key (orderable
+// score, inverted index) with an atomic max, so position j+1 reads x_j from
+// that key and no merge kernel sits between two steps.  After the chain one
+// kernel per (request, position) folds the partials in a fixed order into
+// lse_j and U~_j[x_j] and selects the top-k candidates.
 #include "common.h"
 #include "internal.h"
+#include "markov_dev.h"
 
 namespace dspark {
 
@@ -39,18 +42,19 @@ constexpr int kSeg = 8;            // vocabulary columns per top-k segment
 // ---------------------------------------------------------------------------
 // Fold of one request's per-tile partials of position j by a 256-thread
 // workgroup: thread t takes tiles t, t+256, ... (loads issued kFoldBatch at a
-// time), then a fixed xor tree and waves 0..3 in order; writes x_j, U~_j[x_j]
-// and lse_j.
+// time), then a fixed xor tree and waves 0..3 in order; writes U~_j[x_j] and
+// lse_j, and x_j from the chain's key (the same element: both orders rank by
+// score, then lowest index).
 constexpr int kMergeThreads = 256;
 constexpr int kFoldBatch = 4;
 
-__device__ void fold_request(const StepArgs& a, int b) {
+__device__ void fold_request(const StepArgs& a, int b, int j) {
   __shared__ LseState red_l[kMergeThreads / kWave];
   __shared__ ArgState red_a[kMergeThreads / kWave];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   LseState ls{kNegInf, 0.f};
   ArgState as{kNegInf, 0x7fffffff, 0.f};
-  const size_t base = (static_cast<size_t>(b) * a.gamma + a.j) * a.P;
+  const size_t base = (static_cast<size_t>(b) * a.gamma + j) * a.P;
   for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kMergeThreads) {
     LseState l[kFoldBatch];
     ArgState g[kFoldBatch];
@@ -79,8 +83,8 @@ __device__ void fold_request(const StepArgs& a, int b) {
     LseState l = red_l[0];
     ArgState s = red_a[0];
     for (int i = 1; i < kMergeThreads / kWave; ++i) { l = lse_merge(l, red_l[i]); s = arg_merge(s, red_a[i]); }
-    const int row = b * a.gamma + a.j;
-    a.tokens[row] = s.idx;
+    const int row = b * a.gamma + j;
+    a.tokens[row] = best_index(a.best[row]);
     if (a.tok_logit) a.tok_logit[row] = s.x;
     if (a.lse) a.lse[row] = l.m + logf(l.s);
   }
@@ -187,6 +191,7 @@ __device__ __forceinline__ void epilogue_store(const StepArgs& a, const f32x4 (&
       a.p_score[pq] = as.score;
       a.p_idx[pq] = as.idx;
       a.p_x[pq] = as.x;
+      push_best(a.best + row, as.score, as.idx);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
   for (int rg = 0; rg < RG; ++rg) {
     const int b = req0 + 16 * rg + n;
     bok[rg] = b < a.B;
-    const int prev = !bok[rg] ? 0 : (a.j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + a.j - 1]);
+    const int prev = bok[rg] ? prev_token(a, b, a.j) : 0;
     arow[rg] = A + static_cast<size_t>(prev) * a.r;
   }
 
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(256) void markov_step_batched(StepArgs a) {
   for (int rg = 0; rg < RGW; ++rg) {
     const int b = req0 + 16 * rg + n;
     bok[rg] = b < a.B;
-    const int prev = !bok[rg] ? 0 : (a.j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + a.j - 1]);
+    const int prev = bok[rg] ? prev_token(a, b, a.j) : 0;
     arow[rg] = A + static_cast<size_t>(prev) * a.r;
   }
   f32x4 acc[RGW][8];
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
   const int tile = blockIdx.x, b = blockIdx.y;
   const float* A = static_cast<const float*>(a.A);
   const float* Bm = static_cast<const float*>(a.Bm);
-  const int prev = a.j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + a.j - 1];
+  const int prev = prev_token(a, b, a.j);
   for (int k = tid; k < a.r; k += 256) arow[k] = A[static_cast<size_t>(prev) * a.r + k];
   __syncthreads();
 
@@ -431,17 +436,28 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
     a.p_score[q] = red_a[0].score;
     a.p_idx[q] = red_a[0].idx;
     a.p_x[q] = red_a[0].x;
+    push_best(a.best + static_cast<size_t>(b) * a.gamma + a.j, red_a[0].score, red_a[0].idx);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge kernel (on the sequential path): one workgroup per request folds the
-// per-tile partials of position j (see fold_request).
-__global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) { fold_request(a, blockIdx.x); }
+// Zeroing of the argmax keys before position 0 (a kernel, so that the chain can
+// be captured in a graph), and the fold of every (request, position) after the
+// chain when no top-k is asked for.
+__global__ __launch_bounds__(256) void markov_begin(unsigned long long* best, int n, unsigned* sync) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) best[i] = 0ull;
+  if (i < kSyncWords) sync[i] = 0u;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void markov_fold(StepArgs a) {
+  fold_request(a, blockIdx.x, blockIdx.y);
+}
 
 // ---------------------------------------------------------------------------
 // Top-k kernel (off the sequential path): one workgroup per (request,
-// position), launched once after the chain.  Exact for k <= 32.
+// position), launched once after the chain; it first folds the position's
+// partials (fold_request).  Exact for k <= 32.
 //
 // Bounds used (each holds because k distinct tiles or segments reach them):
 //  theta00 = k-th largest of the 256 per-thread maxima of the tile maxima
@@ -540,7 +556,8 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
   __shared__ float selv[kMaxTopk];
   __shared__ int seli[kMaxTopk];
 
-  const int prev = j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + j - 1];
+  fold_request(a, b, j);
+  const int prev = prev_token(a, b, j);
   const WT* A = static_cast<const WT*>(a.A);
   for (int i = tid; i < a.r; i += kTopkThreads) arow_s[i] = to_f32(A[static_cast<size_t>(prev) * a.r + i]);
   const float* pm = a.p_m + row * a.P;
@@ -722,7 +739,8 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
 // ---------------------------------------------------------------------------
 // host-side launchers
 
-size_t markov_partials(int64_t V) { return static_cast<size_t>((V + kMarkovTile - 1) / kMarkovTile); }
+// partial stride: enough for the narrowest tiles (64 columns, resident chain)
+size_t markov_partials(int64_t V) { return static_cast<size_t>((V + 63) / 64); }
 size_t markov_segments(int64_t V) { return static_cast<size_t>((V + kSeg - 1) / kSeg); }
 
 template <int RG, int KS>
@@ -739,13 +757,12 @@ static void launch_batched(const StepArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL((markov_step_batched<RGW, false>), grid, dim3(256), 0, s, a);
 }
 
-static int partial_count(const StepArgs& a, bool bf16) {
-  return static_cast<int>(bf16 ? (a.V + kMarkovTile - 1) / kMarkovTile
-                               : (a.V + kMarkovTileF32 - 1) / kMarkovTileF32);
-}
+static int partial_count(const StepArgs& a) { return (a.V + a.tile_cols - 1) / a.tile_cols; }
+
+int markov_tile_cols(bool bf16) { return bf16 ? kMarkovTile : kMarkovTileF32; }
 
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
-  a.Pn = partial_count(a, bf16);
+  a.Pn = partial_count(a);
   if (bf16) {
     // request blocking and r-split: small batches split r over 4 waves so a
     // step has enough waves in flight; large batches reuse each transposed Bm
@@ -765,19 +782,25 @@ hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
     const dim3 grid(a.Pn, a.B);
     hipLaunchKernelGGL(markov_step_f32, grid, dim3(256), 0, s, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(markov_merge, dim3(a.B), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_markov_topk(StepArgs a, bool bf16, hipStream_t s) {
-  a.Pn = partial_count(a, bf16);
+hipError_t launch_markov_begin(StepArgs a, hipStream_t s) {
+  const int n = a.B * a.gamma;
+  const int m = n > kSyncWords ? n : kSyncWords;
+  hipLaunchKernelGGL(markov_begin, dim3((m + 255) / 256), dim3(256), 0, s, a.best, n, a.sync);
+  return hipGetLastError();
+}
+
+hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s) {
+  a.Pn = partial_count(a);
   const dim3 grid(a.B, a.gamma);
-  if (bf16)
-    hipLaunchKernelGGL(markov_topk<uint16_t>, grid, dim3(kTopkThreads), 0, s, a, kMarkovTile);
+  if (a.topk == 0)
+    hipLaunchKernelGGL(markov_fold, grid, dim3(kMergeThreads), 0, s, a);
+  else if (bf16)
+    hipLaunchKernelGGL(markov_topk<uint16_t>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
   else
-    hipLaunchKernelGGL(markov_topk<float>, grid, dim3(kTopkThreads), 0, s, a, kMarkovTileF32);
+    hipLaunchKernelGGL(markov_topk<float>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
   return hipGetLastError();
 }
 

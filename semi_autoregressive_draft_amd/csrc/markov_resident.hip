@@ -1,0 +1,438 @@
+// Resident Markov chain for small batches (bf16; B = 1 with r = 64, 128 or 256,
+// or 1 < B <= 16 with r = 256).
+//
+// Same computation as the per-position step kernels (markov.hip):
+//   U~_j[v] = U[b, j, v] + sum_k A[x_{j-1}, k] * Bm[k, v],  x_j = argmax (or
+//   Gumbel-max) of U~_j, with one (max, sum-exp, best) partial per
+//   (request, position, 64-column group) for the fold after the chain.
+// "Qwen3.8-Flash-Next DSpark 训练实验", Baseline 架构/Markov 顺序修正;
+// "DSpark 论文精读", §2.2.
+//
+// At small B each position is bound by streaming all of Bm (r x V bf16) from
+// HBM, gamma times.  Bm fits on chip instead: one persistent workgroup per
+// compute unit loads its share of Bm once, already transposed into MFMA B
+// operands, keeps it in registers (8 groups of 64 columns per workgroup) and in
+// LDS (the rest), and runs all gamma positions.  Between positions the
+// workgroups meet at a grid-wide wait: each one raises the argmax keys of its
+// requests (atomic max), then adds one arrival to a counter and waits until all
+// workgroups have arrived; the next position's previous token is the final key.
+// The wait is a two-level tree so that no address sees more than 16
+// workgroups: each workgroup raises its group's key and counter (groups of 16
+// workgroups); the last arriver of a group, known from the counter's old
+// value, raises the request's final key and the top counter; the last group to
+// arrive there writes one release flag per group, and each workgroup polls its
+// group's flag.  Every step uses atomics or loads at device scope and waits
+// for their return before the next, so a key is final when its counter says
+// so.  The launch is cooperative, so every workgroup is resident and every wait
+// ends; each wait is also bounded in time so that every wave terminates
+// whatever happens (a wait that runs out sets a flag word).
+//
+// Group layout: group G covers columns 64G .. 64G+63 and belongs to workgroup
+// G mod nwg.  For each 32-row chunk q of r, lane (g = lane/16, n = lane%16)
+// holds four B operands (c = 0..3): rows 32q+8g .. 32q+8g+7 of column
+// 64G+4n+c, built from eight 8-byte row loads by byte permutes.  With the A
+// operand "request n, rows 32q+8g..+7 of A[x_{j-1}]", accumulator c of lane
+// (g, n) holds requests 4g..4g+3 for column 64G+4n+c.
+#include "common.h"
+#include "internal.h"
+#include "markov_dev.h"
+
+namespace dspark {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kResThreads = 512;
+constexpr int kResWaves = kResThreads / kWave;
+constexpr int kResCols = 64;                  // vocabulary columns per group
+constexpr int kResMaxB = 16;
+constexpr size_t kResLdsMax = 150 * 1024;     // dynamic LDS: LDS groups + U_j rows
+
+struct ResidentArgs {
+  int nwg;             // workgroups (one per compute unit)
+  int G;               // groups: ceil(V / 64)
+  int T;               // groups per workgroup: ceil(G / nwg)
+  int nreg;            // groups per workgroup held in registers (kResWaves * RGW)
+  int nlds;            // groups per workgroup held in LDS
+  unsigned* sync;      // wait tree, kSyncWords words (zero at launch)
+  unsigned long long wait_ticks;   // bound of one grid-wide wait, wall-clock ticks
+};
+
+// Four B operands (columns c = 0..3) from eight rows of four bf16 columns:
+// operand c, dword p = (row 2p+1, column c) << 16 | (row 2p, column c).
+__device__ __forceinline__ void transpose_rows4(const u32x2 (&rows)[8], u32x4 (&op)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) op[c][p] = __builtin_amdgcn_perm(rows[2 * p + 1][c >> 1], rows[2 * p][c >> 1], sel);
+  }
+}
+
+// Operands of chunk q of group column base `col` (= 64G + 4n), zero past V.
+template <int KCH>
+__device__ __forceinline__ void load_chunk(const uint16_t* Bm, size_t V, int col, bool cok, int q, int g,
+                                           u32x4 (&op)[4]) {
+  u32x2 rows[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    rows[i] = cok ? *reinterpret_cast<const u32x2*>(Bm + static_cast<size_t>(32 * q + 8 * g + i) * V + col)
+                  : u32x2{0u, 0u};
+  transpose_rows4(rows, op);
+}
+
+// Wait-tree layout in the sync block (32-bit words; counters and flags each on
+// their own 256-byte line): time-out flag, group counters, top counter, group
+// release flags, then the group keys [position][group][request] (64-bit).
+constexpr int kFanIn = 16;
+constexpr int kSyncTimeout = 0;
+constexpr int kSyncGroupCnt = 64;                       // + 64 * group
+constexpr int kSyncTopCnt = kSyncGroupCnt + 64 * kFanIn;
+constexpr int kSyncRelease = kSyncTopCnt + 64;          // + 64 * group
+constexpr int kSyncKeys = 4096;                         // word offset of the group keys
+static_assert(kSyncRelease + 64 * kFanIn <= kSyncKeys, "wait-tree layout");
+static_assert(kSyncKeys + 2 * kMaxGamma * kFanIn * kResMaxB <= kSyncWords, "wait-tree size");
+
+__device__ __forceinline__ unsigned atomic_add_dev(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long atomic_max_dev(unsigned long long* p, unsigned long long v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// keep the value live so that the wave waits for the atomic's return here
+__device__ __forceinline__ void returned(unsigned long long v) { asm volatile("" ::"v"(v) : "memory"); }
+
+// Position j's keys (lanes b < B of wave 0 hold request b's workgroup key)
+// into the tree; returns after the final keys a.best[., j] are known to this
+// workgroup (j + 1 < gamma) or after its part is done (last position).
+__device__ void chain_tree(const StepArgs& a, const ResidentArgs& ra, int wg, int j,
+                           unsigned long long key, int lane, bool wait) {
+  unsigned* sy = ra.sync;
+  unsigned long long* gkeys = reinterpret_cast<unsigned long long*>(sy + kSyncKeys);
+  const int grp = wg / kFanIn, ng = (ra.nwg + kFanIn - 1) / kFanIn;
+  const unsigned gsize = static_cast<unsigned>(min(kFanIn, ra.nwg - kFanIn * grp));
+  unsigned long long* gk = gkeys + (j * kFanIn + grp) * kResMaxB;
+  unsigned long long r0 = 0;
+  if (lane < a.B) r0 = atomic_max_dev(gk + lane, key);
+  returned(r0);
+  int last = 0;
+  if (lane == 0) last = atomic_add_dev(sy + kSyncGroupCnt + 64 * grp, 1u) == gsize * (j + 1) - 1;
+  last = __shfl(last, 0);
+  if (last) {                                            // group complete: push its key
+    unsigned long long r1 = 0;
+    if (lane < a.B) r1 = atomic_max_dev(a.best + lane * a.gamma + j, load_dev(gk + lane));
+    returned(r1);
+    int top = 0;
+    if (lane == 0) top = atomic_add_dev(sy + kSyncTopCnt, 1u) == static_cast<unsigned>(ng) * (j + 1) - 1;
+    top = __shfl(top, 0);
+    if (top && lane < ng)                                // all groups in: release them
+      __hip_atomic_store(sy + kSyncRelease + 64 * lane, static_cast<unsigned>(j + 1), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!wait) return;
+  if (lane == 0) {
+    const unsigned long long t0 = wall_clock64();
+    while (load_dev(sy + kSyncRelease + 64 * grp) < static_cast<unsigned>(j + 1)) {
+      if (wall_clock64() - t0 > ra.wait_ticks) {
+        __hip_atomic_store(sy + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
+// Epilogue of one group for the lane's requests 4g + ii (ii < QN): add U_j
+// (from LDS), optional U~ dump, segment maxima, the 16-lane max / sum-exp /
+// argmax of the group, one partial per request, and the wave's running best.
+template <int QN, bool SAMPLE>
+__device__ __forceinline__ void resident_epilogue(const StepArgs& a, const f32x4 (&acc)[4], const float* urows,
+                                                  int gid, int g, int n, ArgState (&best)[QN]) {
+  const size_t V = static_cast<size_t>(a.V);
+  const int col = gid * kResCols + 4 * n;
+  const bool cok = col < a.V;
+#pragma unroll
+  for (int ii = 0; ii < QN; ++ii) {
+    const int b = 4 * g + ii;
+    const bool live = b < a.B && cok;
+    const size_t row = static_cast<size_t>(b) * a.gamma + a.j;
+    float x[4];
+    if (live) {
+      const f32x4 u = *reinterpret_cast<const f32x4*>(urows + b * kResCols + 4 * n);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = acc[c][ii] + u[c];
+      if (a.logits_out) *reinterpret_cast<f32x4*>(a.logits_out + row * V + col) = f32x4{x[0], x[1], x[2], x[3]};
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = kNegInf;
+    }
+    const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    const float m8 = fmaxf(m4, __shfl_xor(m4, 1));       // lanes 2s, 2s+1 form one segment
+    if (a.segmax && live && (n & 1) == 0) a.segmax[row * a.S + col / 8] = m8;
+    float M = m8;
+#pragma unroll
+    for (int o = 2; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float ssum = 0.f;
+    if (live) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ssum += __expf(x[c] - M);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ssum += __shfl_xor(ssum, o);
+
+    float score[4];
+    if constexpr (SAMPLE) {
+      if (live) {
+        const uint64_t sd = a.seeds[b];
+        const Philox4 r = philox4x32_10(col >> 2, a.j, a.off_lo, a.off_hi, static_cast<uint32_t>(sd),
+                                        static_cast<uint32_t>(sd >> 32));
+        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) score[c] = x[c] * a.inv_temp + gumbel_from_word(wd[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) score[c] = kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) score[c] = x[c];
+    }
+    ArgState as{score[0], live ? col : 0x7fffffff, x[0]};
+#pragma unroll
+    for (int c = 1; c < 4; ++c)
+      if (score[c] > as.score) as = ArgState{score[c], col + c, x[c]};
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) as = arg_merge(as, shfl_xor(as, o));
+    if (n == 0 && b < a.B) {
+      const size_t pq = row * a.P + gid;
+      a.p_m[pq] = M;
+      a.p_s[pq] = ssum;
+      a.p_score[pq] = as.score;
+      a.p_idx[pq] = as.idx;
+      a.p_x[pq] = as.x;
+      best[ii] = arg_merge(best[ii], as);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int KCH, int QN, bool SAMPLE>
+__global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, ResidentArgs ra) {
+  constexpr int RGW = 8 / KCH;   // register groups per wave (128 VGPRs of operands)
+  extern __shared__ __align__(16) unsigned char res_lds[];
+  __shared__ ArgState wbest[kResWaves][kResMaxB];
+  __shared__ int prev_s[kResMaxB];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int wg = blockIdx.x;
+  const size_t V = static_cast<size_t>(a.V);
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm);
+  u32x4* lds_ops = reinterpret_cast<u32x4*>(res_lds);                       // [nlds][KCH][4][64]
+  float* lds_u = reinterpret_cast<float*>(res_lds + static_cast<size_t>(ra.nlds) * KCH * 4 * kWave * 16);
+  auto gid_of = [&](int t) { return wg + ra.nwg * t; };
+  auto has = [&](int t) { return t < ra.T && gid_of(t) < ra.G; };
+
+  // U_j rows of this workgroup's groups, [t][b][64] floats, by DMA: each wave
+  // instruction moves 4 rows of 256 bytes (lane i: row 4k + i/16, bytes 16 (i%16))
+  const int nrows = ra.T * a.B;
+  auto issue_u = [&](int j) {
+    for (int k = w; 4 * k < nrows; k += kResWaves) {
+      const int rr = 4 * k + (lane >> 4);
+      const int t = rr / a.B, b = rr - t * a.B;
+      const int col = gid_of(t) * kResCols + 4 * (lane & 15);
+      if (rr < nrows && has(t) && col < a.V) {
+        const float* src = a.U + (static_cast<size_t>(b) * a.gamma + j) * V + col;
+        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<void*>(lds_u + 4 * k * kResCols), 16, 0, 0);
+      }
+    }
+  };
+  issue_u(0);
+
+  // Bm share: register groups t = w*RGW + s, LDS group t = nreg + w
+  u32x4 dreg[RGW][KCH][4];
+#pragma unroll
+  for (int s = 0; s < RGW; ++s) {
+    const int t = w * RGW + s;
+    const bool on = has(t);
+    const int col = gid_of(t) * kResCols + 4 * n;
+#pragma unroll
+    for (int q = 0; q < KCH; ++q) load_chunk<KCH>(Bm, V, col, on && col < a.V, q, g, dreg[s][q]);
+  }
+  if (w < ra.nlds && has(ra.nreg + w)) {
+    const int col = gid_of(ra.nreg + w) * kResCols + 4 * n;
+#pragma unroll
+    for (int q = 0; q < KCH; ++q) {
+      u32x4 op[4];
+      load_chunk<KCH>(Bm, V, col, col < a.V, q, g, op);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lds_ops[((w * KCH + q) * 4 + c) * kWave + lane] = op[c];
+    }
+  }
+  __syncthreads();   // LDS operands written, U_0 landed (the barrier waits for all loads)
+
+  for (int j = 0; j < a.gamma; ++j) {
+    a.j = j;
+    int prev = n < a.B ? (j == 0 ? a.anchor[n] : prev_s[n]) : 0;
+    prev = min(max(prev, 0), a.V - 1);              // guard of the gathered row
+    u32x4 av[KCH];
+#pragma unroll
+    for (int q = 0; q < KCH; ++q)
+      av[q] = n < a.B ? *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(prev) * a.r + 32 * q + 8 * g)
+                      : u32x4{0u, 0u, 0u, 0u};
+    ArgState best[QN];
+#pragma unroll
+    for (int ii = 0; ii < QN; ++ii) best[ii] = ArgState{kNegInf, 0x7fffffff, 0.f};
+
+    // products of the register groups and the LDS group; with one register
+    // group per wave both accumulators are formed before either epilogue, so
+    // the A operands are dead during the epilogues
+    auto mfma_reg = [&](int s, f32x4 (&acc)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < KCH; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[q]), as_bf16x8(dreg[s][q][c]), acc[c], 0, 0, 0);
+    };
+    auto mfma_lds = [&](f32x4 (&acc)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < KCH; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(av[q]), as_bf16x8(lds_ops[((w * KCH + q) * 4 + c) * kWave + lane]), acc[c], 0, 0, 0);
+    };
+    const int tl = ra.nreg + w;
+    const bool lds_on = w < ra.nlds && has(tl);
+    if constexpr (RGW == 1) {
+      const int t = w;
+      f32x4 acc0[4], acc1[4];
+      if (has(t)) mfma_reg(0, acc0);
+      if (lds_on) mfma_lds(acc1);
+      if (has(t)) resident_epilogue<QN, SAMPLE>(a, acc0, lds_u + t * a.B * kResCols, gid_of(t), g, n, best);
+      if (lds_on) resident_epilogue<QN, SAMPLE>(a, acc1, lds_u + tl * a.B * kResCols, gid_of(tl), g, n, best);
+    } else {
+#pragma unroll
+      for (int s = 0; s < RGW; ++s) {
+        const int t = w * RGW + s;
+        if (!has(t)) continue;                        // uniform per wave
+        f32x4 acc[4];
+        mfma_reg(s, acc);
+        resident_epilogue<QN, SAMPLE>(a, acc, lds_u + t * a.B * kResCols, gid_of(t), g, n, best);
+      }
+      if (lds_on) {
+        f32x4 acc[4];
+        mfma_lds(acc);
+        resident_epilogue<QN, SAMPLE>(a, acc, lds_u + tl * a.B * kResCols, gid_of(tl), g, n, best);
+      }
+    }
+    if (n == 0) {
+#pragma unroll
+      for (int ii = 0; ii < QN; ++ii)
+        if (4 * g + ii < a.B) wbest[w][4 * g + ii] = best[ii];
+    }
+    __syncthreads();                                  // wave bests in LDS; U_j no longer read
+    if (j + 1 < a.gamma) issue_u(j + 1);
+    if (w == 0) {
+      unsigned long long key = 0;
+      if (lane < a.B) {
+        ArgState s = wbest[0][lane];
+        for (int v = 1; v < kResWaves; ++v) s = arg_merge(s, wbest[v][lane]);
+        key = best_key(s.score, s.idx);
+      }
+      const bool more = j + 1 < a.gamma;
+      chain_tree(a, ra, wg, j, key, lane, more);
+      if (more && lane < a.B) prev_s[lane] = best_index(load_dev(a.best + lane * a.gamma + j));
+    }
+    __syncthreads();                                  // prev_s visible; U_{j+1} landed
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+namespace {
+struct DeviceInfo { int cus = 0; int coop = 0; int clock_khz = 0; };
+DeviceInfo device_info() {
+  static thread_local DeviceInfo cache[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return DeviceInfo{};
+  DeviceInfo& d = cache[dev];
+  if (d.cus == 0) {
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&d.clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      d = DeviceInfo{};
+  }
+  return d;
+}
+
+template <int KCH, int QN, bool SAMPLE>
+hipError_t launch_res(StepArgs a, ResidentArgs ra, size_t lds, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&markov_resident<KCH, QN, SAMPLE>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  void* args[] = {&a, &ra};
+  return hipLaunchCooperativeKernel(fn, dim3(ra.nwg), dim3(kResThreads), args, static_cast<unsigned>(lds), s);
+}
+
+template <int KCH>
+hipError_t launch_b1(const StepArgs& a, const ResidentArgs& ra, size_t lds, hipStream_t s) {
+  return a.sample ? launch_res<KCH, 1, true>(a, ra, lds, s) : launch_res<KCH, 1, false>(a, ra, lds, s);
+}
+}  // namespace
+
+// Plan of the resident chain for these sizes; false when it does not apply
+// (the caller then runs the per-position kernels).  `max_wg` > 0 caps the
+// number of workgroups (more groups per workgroup, as on a smaller device).
+bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg_out, size_t* lds_out) {
+  // the register budget of one wave (operands, accumulators, epilogue) holds
+  // without spills for these shapes
+  if (B < 1 || B > kResMaxB) return false;
+  if (B == 1 ? (r != 64 && r != 128 && r != 256) : r != 256) return false;
+  const DeviceInfo d = device_info();
+  if (d.cus <= 0 || !d.coop || d.clock_khz <= 0) return false;
+  const int KCH = r / 32, nreg = kResWaves * (8 / KCH);
+  const int G = (V + kResCols - 1) / kResCols;
+  int nwg = d.cus;
+  if (max_wg > 0 && max_wg < nwg) nwg = max_wg;
+  if (nwg > G) nwg = G;
+  const int T = (G + nwg - 1) / nwg;
+  const int nlds = T > nreg ? T - nreg : 0;
+  if (nlds > kResWaves) return false;
+  const size_t lds = static_cast<size_t>(nlds) * KCH * 4 * kWave * 16 + static_cast<size_t>(T) * B * kResCols * 4;
+  if (lds > kResLdsMax) return false;
+  *nwg_out = nwg;
+  *lds_out = lds;
+  return true;
+}
+
+hipError_t launch_markov_resident(StepArgs a, unsigned* sync, int nwg, size_t lds, hipStream_t s) {
+  const DeviceInfo d = device_info();
+  ResidentArgs ra{};
+  ra.nwg = nwg;
+  ra.G = (a.V + kResCols - 1) / kResCols;
+  ra.T = (ra.G + nwg - 1) / nwg;
+  const int KCH = a.r / 32;
+  ra.nreg = kResWaves * (8 / KCH);
+  ra.nlds = ra.T > ra.nreg ? ra.T - ra.nreg : 0;
+  ra.sync = sync;
+  ra.wait_ticks = static_cast<unsigned long long>(d.clock_khz) * 100;   // 100 ms
+  a.j = 0;
+  if (a.B > 1) return a.sample ? launch_res<8, 4, true>(a, ra, lds, s) : launch_res<8, 4, false>(a, ra, lds, s);
+  switch (KCH) {
+    case 2: return launch_b1<2>(a, ra, lds, s);
+    case 4: return launch_b1<4>(a, ra, lds, s);
+    default: return launch_b1<8>(a, ra, lds, s);
+  }
+}
+
+}  // namespace dspark

@@ -70,8 +70,17 @@ def _markov_case(B, V, r, wdtype, seed=3, mstd=0.25):
     return U, anchor, A, Bm
 
 
+@pytest.fixture(params=["resident", "per_position"])
+def chain_path(request, monkeypatch):
+    """Run each Markov case through both chain implementations (the resident
+    chain only where it applies)."""
+    if request.param == "per_position":
+        monkeypatch.setenv("DSPARK_MARKOV_RESIDENT", "0")
+    return request.param
+
+
 @pytest.mark.parametrize("B,V,r,wdtype,T,topk", [
-    (1, 5000, 256, "bf16", 0.0, 0),     # one request, r split over 4 waves
+    (1, 5000, 256, "bf16", 0.0, 0),     # one request (per position: r split over 4 waves)
     (3, 5000, 64, "bf16", 0.0, 0),      # r split over 2 waves
     (5, 4096, 32, "bf16", 0.7, 0),      # sampled, no r split
     (17, 5000, 128, "bf16", 0.0, 0),    # 2 request groups per wave, ragged request block
@@ -82,7 +91,7 @@ def _markov_case(B, V, r, wdtype, seed=3, mstd=0.25):
     (1, 4096, 32, "f32", 0.0, 0),       # tiny reference config
     (3, 1000, 48, "f32", 1.0, 5),       # float32 tables, any rank
 ])
-def test_markov_parity(B, V, r, wdtype, T, topk):
+def test_markov_parity(B, V, r, wdtype, T, topk, chain_path):
     U, anchor, A, Bm = _markov_case(B, V, r, wdtype)
     seeds = np.arange(B, dtype=np.uint64) * 7919 + 3 if T > 0 else None
     gpu = _run_markov(U, anchor, A, Bm, wdtype, T=T, seeds=seeds, offset=5, topk=topk)
@@ -90,7 +99,41 @@ def test_markov_parity(B, V, r, wdtype, T, topk):
                 temperature=T, seeds=seeds, offset=5, topk=topk)
 
 
-def test_markov_walks_a_permutation():
+@pytest.mark.parametrize("B,V,r,T,topk,wg", [
+    (1, 5000, 256, 0.0, 16, 0),         # one group per workgroup
+    (1, 5000, 256, 0.0, 0, 8),          # 10 groups per workgroup: 8 in registers, 2 in LDS
+    (1, 3000, 128, 1.0, 8, 4),          # r = 128: 2 register groups per wave, sampled
+    (1, 2504, 64, 0.0, 16, 1),          # r = 64, one workgroup: 32 register + 8 LDS groups, ragged
+    (5, 5000, 256, 0.0, 8, 8),          # several requests, LDS groups
+    (16, 4104, 256, 0.7, 0, 6),         # 16 requests, sampled, ragged last group
+])
+def test_markov_resident_chain(B, V, r, T, topk, wg, monkeypatch):
+    # the resident chain with the operand share spread as on smaller devices
+    # (a workgroup cap puts more groups, and LDS-held groups, in each workgroup)
+    require_gpu()
+    if wg:
+        monkeypatch.setenv("DSPARK_MARKOV_WORKGROUPS", str(wg))
+    n = bd.dspark_markov_propose_plan(B, V, r)
+    assert n > 0 and (wg == 0 or n == wg)
+    U, anchor, A, Bm = _markov_case(B, V, r, "bf16", seed=6)
+    seeds = np.arange(B, dtype=np.uint64) * 104729 + 1 if T > 0 else None
+    gpu = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=2, topk=topk)
+    check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"),
+                temperature=T, seeds=seeds, offset=2, topk=topk)
+
+
+def test_markov_plan_follows_the_shape_rules(monkeypatch):
+    require_gpu()
+    assert bd.dspark_markov_propose_plan(1, 151936, 256) > 0
+    assert bd.dspark_markov_propose_plan(16, 151936, 256) > 0
+    assert bd.dspark_markov_propose_plan(17, 151936, 256) == 0    # batched step kernels
+    assert bd.dspark_markov_propose_plan(2, 5000, 64) == 0        # B > 1 needs r = 256
+    assert bd.dspark_markov_propose_plan(1, 5000, 48, bd.F32) == 0
+    monkeypatch.setenv("DSPARK_MARKOV_RESIDENT", "0")
+    assert bd.dspark_markov_propose_plan(1, 151936, 256) == 0
+
+
+def test_markov_walks_a_permutation(chain_path):
     # A = identity rows, Bm = 4 * permutation, |U| < 1.6: x_j = pi^{j+1}(anchor).
     # All values are exact in bf16, so this checks the previous-token wiring
     # (anchor at slot 0, token j-1 at slot j) independently of rounding.
@@ -110,7 +153,7 @@ def test_markov_walks_a_permutation():
             assert gpu["tokens"][b, j] == t
 
 
-def test_markov_ties_take_lowest_index_and_slow_topk_path():
+def test_markov_ties_take_lowest_index_and_slow_topk_path(chain_path):
     # constant logits and zero transitions: every column ties, so the token is
     # column 0 and the top-k candidate lists overflow into the exact slow path
     B, V, r, k = 2, 1024, 32, 16
@@ -132,9 +175,10 @@ def test_markov_zero_transition_is_parallel_argmax():
     assert np.array_equal(gpu["tokens"], U.argmax(axis=-1))
 
 
-def test_markov_is_deterministic():
-    U, anchor, A, Bm = _markov_case(33, 5000, 256, "bf16", seed=4)
-    seeds = np.arange(33, dtype=np.uint64)
+@pytest.mark.parametrize("B", [1, 33])
+def test_markov_is_deterministic(B):
+    U, anchor, A, Bm = _markov_case(B, 5000, 256, "bf16", seed=4)
+    seeds = np.arange(B, dtype=np.uint64)
     a = _run_markov(U, anchor, A, Bm, "bf16", T=1.0, seeds=seeds, topk=16)
     b = _run_markov(U, anchor, A, Bm, "bf16", T=1.0, seeds=seeds, topk=16)
     for key in a:
