@@ -84,6 +84,49 @@ __device__ __forceinline__ ArgState shfl_xor(ArgState v, int mask) {
   return {__shfl_xor(v.score, mask), __shfl_xor(v.idx, mask), __shfl_xor(v.x, mask)};
 }
 
+// -------------------------------------------------------------------------
+// Reductions over rows of 16 lanes through DPP lane permutes (VALU, no LDS):
+// xor 1 and xor 2 within quads, then the half-row mirror (lane i <-> 7 - i)
+// and the row mirror (i <-> 15 - i); in this order each step pairs lanes whose
+// partial results cover disjoint lane sets, so after four steps every lane of
+// a row holds the same, complete result.
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1, 0, 3, 2)
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2, 3, 0, 1)
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+template <int CTRL>
+__device__ __forceinline__ ArgState arg_step(ArgState a) {
+  return arg_merge(a, ArgState{dpp_f<CTRL>(a.score), dpp_i<CTRL>(a.idx), dpp_f<CTRL>(a.x)});
+}
+__device__ __forceinline__ ArgState row16_arg(ArgState a) {
+  a = arg_step<kDppXor1>(a);
+  a = arg_step<kDppXor2>(a);
+  a = arg_step<kDppHalfMirror>(a);
+  return arg_step<kDppMirror>(a);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

@@ -34,12 +34,18 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 constexpr int64_t kI32Max = 2147483647;
 
 // per (request, position): 5 partial arrays of one entry per vocabulary tile,
-// one 8-byte argmax key, plus the segment maxima when top-k is asked for; one
-// block for the resident chain's wait tree
+// one 8-byte argmax key; one block for the resident chain's wait tree; with
+// top-k, the segment maxima (per-position chain) and, when the batch is small
+// enough for the resident chain, its per-workgroup candidate lists
+size_t markov_cand_bytes(int64_t B, int64_t gamma, int32_t topk) {
+  return align_up(static_cast<size_t>(B) * gamma * kMaxLists * topk * 8);
+}
+
 size_t markov_ws_bytes(int64_t B, int64_t gamma, int64_t V, int32_t topk) {
   const size_t rows = static_cast<size_t>(B) * gamma;
   size_t s = 5 * align_up(rows * markov_partials(V) * 4) + align_up(rows * 8) + kSyncWords * 4;
   if (topk > 0) s += align_up(rows * markov_segments(V) * 4);
+  if (topk > 0 && B <= kResidentMaxB) s += markov_cand_bytes(B, gamma, topk);
   return s;
 }
 
@@ -177,9 +183,9 @@ extern "C" dspark_status_t dspark_markov_propose(
   a.P = static_cast<int>(P);
   a.S = static_cast<int>(markov_segments(V));
   const size_t keys = align_up(static_cast<size_t>(B) * gamma * 8);
+  char* tail = base + 5 * arr + keys + kSyncWords * 4;
   a.best = reinterpret_cast<unsigned long long*>(base + 5 * arr);
   a.sync = reinterpret_cast<unsigned*>(base + 5 * arr + keys);
-  a.segmax = topk > 0 ? reinterpret_cast<float*>(base + 5 * arr + keys + kSyncWords * 4) : nullptr;
   a.logits_out = logits_out;
   a.tok_logit = tok_logit;
   a.lse = lse;
@@ -190,6 +196,13 @@ extern "C" dspark_status_t dspark_markov_propose(
   size_t lds = 0;
   const bool resident = resident_chain(bf16, a.B, a.V, a.r, &nwg, &lds);
   a.tile_cols = resident ? 64 : markov_tile_cols(bf16);
+  a.resident = resident;
+  a.nlist = nwg;
+  if (topk > 0) {
+    const size_t seg = align_up(static_cast<size_t>(B) * gamma * markov_segments(V) * 4);
+    a.segmax = resident ? nullptr : reinterpret_cast<float*>(tail);
+    if (resident) a.cand_key = reinterpret_cast<unsigned long long*>(tail + seg);
+  }
   hipError_t e = launch_markov_begin(a, stream);
   if (resident) {
     if (e == hipSuccess) e = launch_markov_resident(a, a.sync, nwg, lds, stream);

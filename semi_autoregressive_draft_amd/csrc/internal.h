@@ -11,6 +11,8 @@ constexpr int kMaxRank = 1024;
 constexpr int kMaxTopk = 32;
 constexpr int kMaxGamma = 16;
 constexpr int kMaxCand = 64;
+constexpr int kMaxLists = 256;   // workgroups of the resident chain
+constexpr int kResidentMaxB = 16;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
 constexpr int kSyncWords = 12 * 1024;   // 48 KB: the resident chain's wait tree (zero at launch)
 
@@ -25,6 +27,11 @@ struct StepArgs {
   unsigned long long* best;
   unsigned* sync;          // [kSyncWords] counters, flags and group keys of the resident chain
   int tile_cols;           // vocabulary columns per partial (64 resident, 128 bf16, 256 f32)
+  int resident;            // 1: the chain ran as the resident kernel
+  // resident chain with top-k: each workgroup's k largest order keys of U~_j
+  // (value desc, index asc), sorted, [B][gamma][nlist][topk]; 0 pads
+  unsigned long long* cand_key;
+  int nlist;
   const void* A;           // [V, r]
   const void* Bm;          // [r, V]
   int B, gamma, V, r, j;

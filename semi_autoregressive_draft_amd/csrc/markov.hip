@@ -9,14 +9,13 @@
 // (m_i = W_1[t_{i-1}], b_i = W_2 m_i, l_i = l_i^0 + b_i); "DSpark 论文精读", §2.2
 // (U~_j = U_j + b(x_{j-1}), x_j ~ softmax(U~_j)).
 //
-// One launch per position: the step kernel streams Bm and U_j once for all
+// Two launches per position: the step kernel streams Bm and U_j once for all
 // requests and leaves one partial (max, sum-exp, best score/index) per
-// (request, vocabulary tile).  The argmax that the next position needs is also
-// folded on the fly: every (request, tile) raises a 64-bit key (orderable
-// score, inverted index) with an atomic max, so position j+1 reads x_j from
-// that key and no merge kernel sits between two steps.  After the chain one
-// kernel per (request, position) folds the partials in a fixed order into
-// lse_j and U~_j[x_j] and selects the top-k candidates.
+// (request, vocabulary tile); a merge kernel with one workgroup per request
+// folds them in a fixed order into x_j, U~_j[x_j] and lse_j, and stores x_j
+// also as a 64-bit argmax key (the form in which the resident chain of
+// markov_resident.hip hands tokens between positions).  The top-k candidates
+// are selected after the chain, off the sequential path.
 #include "common.h"
 #include "internal.h"
 #include "markov_dev.h"
@@ -43,12 +42,13 @@ constexpr int kSeg = 8;            // vocabulary columns per top-k segment
 // Fold of one request's per-tile partials of position j by a 256-thread
 // workgroup: thread t takes tiles t, t+256, ... (loads issued kFoldBatch at a
 // time), then a fixed xor tree and waves 0..3 in order; writes U~_j[x_j] and
-// lse_j, and x_j from the chain's key (the same element: both orders rank by
-// score, then lowest index).
+// lse_j.  x_j is the fold's own argmax (per-position chain, which also stores
+// its key) or, after the resident chain, the chain's final key (the same
+// element: both rank by score, then lowest index).
 constexpr int kMergeThreads = 256;
 constexpr int kFoldBatch = 4;
 
-__device__ void fold_request(const StepArgs& a, int b, int j) {
+__device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
   __shared__ LseState red_l[kMergeThreads / kWave];
   __shared__ ArgState red_a[kMergeThreads / kWave];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -84,7 +84,12 @@ __device__ void fold_request(const StepArgs& a, int b, int j) {
     ArgState s = red_a[0];
     for (int i = 1; i < kMergeThreads / kWave; ++i) { l = lse_merge(l, red_l[i]); s = arg_merge(s, red_a[i]); }
     const int row = b * a.gamma + j;
-    a.tokens[row] = best_index(a.best[row]);
+    if (from_key) {
+      a.tokens[row] = best_index(a.best[row]);
+    } else {
+      a.tokens[row] = s.idx;
+      a.best[row] = best_key(s.score, s.idx);
+    }
     if (a.tok_logit) a.tok_logit[row] = s.x;
     if (a.lse) a.lse[row] = l.m + logf(l.s);
   }
@@ -150,15 +155,13 @@ __device__ __forceinline__ void epilogue_store(const StepArgs& a, const f32x4 (&
     for (int c = 1; c < 8; ++c) m8 = fmaxf(m8, x[c]);
     if (a.segmax && live) a.segmax[row * a.S + vcol / kSeg] = m8;   // one top-k segment
     float M = m8;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    M = row16_max(M);
     float ssum = 0.f;
     if (live) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) ssum += __expf(x[c] - M);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) ssum += __shfl_xor(ssum, o);
+    ssum = row16_sum(ssum);
 
     float score[8];
     if constexpr (SAMPLE) {
@@ -182,8 +185,7 @@ __device__ __forceinline__ void epilogue_store(const StepArgs& a, const f32x4 (&
 #pragma unroll
     for (int c = 1; c < 8; ++c)
       if (score[c] > as.score) as = ArgState{score[c], vcol + c, x[c]};
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) as = arg_merge(as, shfl_xor(as, o));
+    as = row16_arg(as);
     if (n == 0 && b < a.B) {
       const size_t pq = row * a.P + tile;
       a.p_m[pq] = M;
@@ -191,7 +193,6 @@ __device__ __forceinline__ void epilogue_store(const StepArgs& a, const f32x4 (&
       a.p_score[pq] = as.score;
       a.p_idx[pq] = as.idx;
       a.p_x[pq] = as.x;
-      push_best(a.best + row, as.score, as.idx);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -436,28 +437,32 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
     a.p_score[q] = red_a[0].score;
     a.p_idx[q] = red_a[0].idx;
     a.p_x[q] = red_a[0].x;
-    push_best(a.best + static_cast<size_t>(b) * a.gamma + a.j, red_a[0].score, red_a[0].idx);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Zeroing of the argmax keys before position 0 (a kernel, so that the chain can
-// be captured in a graph), and the fold of every (request, position) after the
-// chain when no top-k is asked for.
+// Zeroing of the argmax keys and the resident chain's wait tree before
+// position 0 (a kernel, so that the chain can be captured in a graph); the
+// per-position merge; the fold of every (request, position) after the
+// resident chain.
 __global__ __launch_bounds__(256) void markov_begin(unsigned long long* best, int n, unsigned* sync) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) best[i] = 0ull;
   if (i < kSyncWords) sync[i] = 0u;
 }
 
+__global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
+  fold_request(a, blockIdx.x, a.j, false);
+}
+
 __global__ __launch_bounds__(kMergeThreads) void markov_fold(StepArgs a) {
-  fold_request(a, blockIdx.x, blockIdx.y);
+  fold_request(a, blockIdx.x, blockIdx.y, true);
 }
 
 // ---------------------------------------------------------------------------
-// Top-k kernel (off the sequential path): one workgroup per (request,
-// position), launched once after the chain; it first folds the position's
-// partials (fold_request).  Exact for k <= 32.
+// Top-k kernel of the per-position chain (off the sequential path): one
+// workgroup per (request, position), launched once after the chain.  Exact for
+// k <= 32.
 //
 // Bounds used (each holds because k distinct tiles or segments reach them):
 //  theta00 = k-th largest of the 256 per-thread maxima of the tile maxima
@@ -520,10 +525,6 @@ template <> struct SegRows<float> {
   }
 };
 
-__device__ __forceinline__ bool ranks_before(float xa, int ia, float xb, int ib) {
-  return xa > xb || (xa == xb && ia < ib);
-}
-
 // value of rank k-1 among the n values of `vals` (ties ranked by position);
 // every thread calls it, the result is broadcast through `out`
 __device__ void kth_largest(const float* vals, int n, int k, float* out) {
@@ -556,7 +557,6 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
   __shared__ float selv[kMaxTopk];
   __shared__ int seli[kMaxTopk];
 
-  fold_request(a, b, j);
   const int prev = prev_token(a, b, j);
   const WT* A = static_cast<const WT*>(a.A);
   for (int i = tid; i < a.r; i += kTopkThreads) arow_s[i] = to_f32(A[static_cast<size_t>(prev) * a.r + i]);
@@ -737,6 +737,84 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
 }
 
 // ---------------------------------------------------------------------------
+// Top-k after the resident chain: one workgroup per (request, position) folds
+// the per-workgroup partials (fold_request), then merges the per-workgroup
+// candidate lists (each the k largest order keys of one workgroup's columns,
+// sorted descending; best_key orders by value descending, then index
+// ascending, and 0 pads short lists).  Exact: let list L's head rank r_L among
+// the live heads.  Entry p of list L is preceded by the p entries before it in
+// L and by the r_L heads larger than L's head, so it can be among the k
+// largest only if p + r_L < k.  That leaves at most k(k+1)/2 candidates, each
+// ranked by counting the larger ones (live keys are distinct; padding, equal
+// to 0, ranks after every live key and never reaches the first k, since
+// k <= V).
+constexpr int kMaxMergeCand = kMaxTopk * (kMaxTopk + 1) / 2;
+
+__global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.x, j = blockIdx.y;
+  const int k = a.topk, L = a.nlist;
+  const size_t row = static_cast<size_t>(b) * a.gamma + j;
+  __shared__ unsigned long long hk[kMaxLists];
+  __shared__ int act[kMaxTopk];
+  __shared__ int nlive;
+  __shared__ unsigned long long mk[kMaxMergeCand];
+  __shared__ unsigned long long sel[kMaxTopk];
+
+  const unsigned long long* ck = a.cand_key + row * L * k;
+  const unsigned long long head = tid < L ? ck[static_cast<size_t>(tid) * k] : 0ull;
+  if (tid == 0) nlive = 0;
+  hk[tid] = head;
+  fold_request(a, b, j, true);                        // ends with a barrier: hk complete
+  if (head != 0ull) {
+    int rank = 0, u = 0;
+    for (; u + 8 <= L; u += 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rank += hk[u + q] > head;
+    }
+    for (; u < L; ++u) rank += hk[u] > head;
+    if (rank < k) {
+      act[rank] = tid;
+      atomicAdd(&nlive, 1);
+    }
+  }
+  __syncthreads();
+  // candidates of the list of head rank r: entries p < k - r, stored from
+  // offset r k - r (r - 1) / 2
+  const int na = nlive;
+  const int nc = na * k - na * (na - 1) / 2;
+  for (int e = tid; e < nc; e += kTopkThreads) {
+    int r = 0;
+    while ((r + 1) * k - (r + 1) * r / 2 <= e) ++r;
+    const int p = e - (r * k - r * (r - 1) / 2);
+    mk[e] = ck[static_cast<size_t>(act[r]) * k + p];
+  }
+  __syncthreads();
+  for (int e = tid; e < nc; e += kTopkThreads) {
+    const unsigned long long key = mk[e];
+    int rank = 0, f = 0;
+    for (; f + 8 <= nc; f += 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rank += mk[f + q] > key;
+    }
+    for (; f < nc; ++f) rank += mk[f] > key;
+    if (rank < k && key != 0ull) sel[rank] = key;
+  }
+  __syncthreads();
+  if (w == 0) {  // softmax over the k candidates at T = 1, summed in rank order
+    const size_t o = row * k;
+    const float v = lane < k ? best_value(sel[lane]) : 0.f;
+    const float e = lane < k ? __expf(v - __shfl(v, 0)) : 0.f;
+    float ssum = 0.f;
+    for (int t = 0; t < k; ++t) ssum += __shfl(e, t);
+    if (lane < k) {
+      a.topk_idx[o + lane] = best_index(sel[lane]);
+      a.topk_prob[o + lane] = e / ssum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers
 
 // partial stride: enough for the narrowest tiles (64 columns, resident chain)
@@ -782,6 +860,9 @@ hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
     const dim3 grid(a.Pn, a.B);
     hipLaunchKernelGGL(markov_step_f32, grid, dim3(256), 0, s, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(markov_merge, dim3(a.B), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -795,9 +876,14 @@ hipError_t launch_markov_begin(StepArgs a, hipStream_t s) {
 hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s) {
   a.Pn = partial_count(a);
   const dim3 grid(a.B, a.gamma);
-  if (a.topk == 0)
-    hipLaunchKernelGGL(markov_fold, grid, dim3(kMergeThreads), 0, s, a);
-  else if (bf16)
+  if (a.resident) {                        // resident chain: fold, then merge its candidate lists
+    a.Pn = a.nlist;                        // one partial per workgroup
+    if (a.topk == 0) hipLaunchKernelGGL(markov_fold, grid, dim3(kMergeThreads), 0, s, a);
+    else hipLaunchKernelGGL(markov_topk_lists, grid, dim3(kTopkThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.topk == 0) return hipSuccess;
+  if (bf16)
     hipLaunchKernelGGL(markov_topk<uint16_t>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
   else
     hipLaunchKernelGGL(markov_topk<float>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);

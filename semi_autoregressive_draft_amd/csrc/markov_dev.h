@@ -22,12 +22,15 @@ __device__ __forceinline__ int best_index(unsigned long long key) {
   return static_cast<int>(~static_cast<uint32_t>(key));
 }
 
-// Raise the key; the relaxed read first skips atomics that cannot change it
-// (keys only grow, so a stale read only costs an unneeded atomic).
-__device__ __forceinline__ void push_best(unsigned long long* slot, float score, int idx) {
-  const unsigned long long k = best_key(score, idx);
-  const unsigned long long cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (k > cur) atomicMax(slot, k);
+// the score of a key (inverse of the order map; -0 comes back as +0)
+__device__ __forceinline__ float best_value(unsigned long long key) {
+  const uint32_t u = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// (value descending, index ascending): the order of the top-k candidates
+__device__ __forceinline__ bool ranks_before(float xa, int ia, float xb, int ib) {
+  return xa > xb || (xa == xb && ia < ib);
 }
 
 // x_{j-1} of request b: the anchor for j == 0, else the final key of j-1

@@ -4,7 +4,7 @@
 // Same computation as the per-position step kernels (markov.hip):
 //   U~_j[v] = U[b, j, v] + sum_k A[x_{j-1}, k] * Bm[k, v],  x_j = argmax (or
 //   Gumbel-max) of U~_j, with one (max, sum-exp, best) partial per
-//   (request, position, 64-column group) for the fold after the chain.
+//   (request, position, workgroup) for the fold after the chain.
 // "Qwen3.8-Flash-Next DSpark 训练实验", Baseline 架构/Markov 顺序修正;
 // "DSpark 论文精读", §2.2.
 //
@@ -27,6 +27,13 @@
 // ends; each wait is also bounded in time so that every wave terminates
 // whatever happens (a wait that runs out sets a flag word).
 //
+// With top-k, the epilogue leaves U~_j in LDS (over the U_j rows it read, two
+// buffers alternating by position), and while wave 0 walks the wait tree the
+// other seven waves select this workgroup's k best U~_j per request into a
+// sorted list of 64-bit order keys (best_key: value descending, index
+// ascending; 0 pads lists of workgroups with fewer than k live columns); the
+// finish kernel merges the lists exactly.
+//
 // Group layout: group G covers columns 64G .. 64G+63 and belongs to workgroup
 // G mod nwg.  For each 32-row chunk q of r, lane (g = lane/16, n = lane%16)
 // holds four B operands (c = 0..3): rows 32q+8g .. 32q+8g+7 of column
@@ -44,8 +51,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / kWave;
 constexpr int kResCols = 64;                  // vocabulary columns per group
-constexpr int kResMaxB = 16;
-constexpr size_t kResLdsMax = 150 * 1024;     // dynamic LDS: LDS groups + U_j rows
+constexpr int kResMaxB = kResidentMaxB;
+constexpr size_t kResLdsMax = 148 * 1024;     // dynamic LDS: LDS groups + U_j rows (static: ~11 KB)
 
 struct ResidentArgs {
   int nwg;             // workgroups (one per compute unit)
@@ -146,11 +153,13 @@ __device__ void chain_tree(const StepArgs& a, const ResidentArgs& ra, int wg, in
 }
 
 // Epilogue of one group for the lane's requests 4g + ii (ii < QN): add U_j
-// (from LDS), optional U~ dump, segment maxima, the 16-lane max / sum-exp /
-// argmax of the group, one partial per request, and the wave's running best.
+// (from LDS, replaced there by U~_j), optional U~ dump, the 16-lane max /
+// sum-exp / argmax of the group, folded into the wave's running states (the
+// same in all 16 lanes of a row).
 template <int QN, bool SAMPLE>
-__device__ __forceinline__ void resident_epilogue(const StepArgs& a, const f32x4 (&acc)[4], const float* urows,
-                                                  int gid, int g, int n, ArgState (&best)[QN]) {
+__device__ __forceinline__ void resident_epilogue(const StepArgs& a, const f32x4 (&acc)[4], float* urows,
+                                                  int gid, int g, int n, LseState (&run)[QN],
+                                                  ArgState (&best)[QN]) {
   const size_t V = static_cast<size_t>(a.V);
   const int col = gid * kResCols + 4 * n;
   const bool cok = col < a.V;
@@ -161,27 +170,25 @@ __device__ __forceinline__ void resident_epilogue(const StepArgs& a, const f32x4
     const size_t row = static_cast<size_t>(b) * a.gamma + a.j;
     float x[4];
     if (live) {
-      const f32x4 u = *reinterpret_cast<const f32x4*>(urows + b * kResCols + 4 * n);
+      f32x4* up = reinterpret_cast<f32x4*>(urows + b * kResCols + 4 * n);
+      const f32x4 u = *up;
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = acc[c][ii] + u[c];
-      if (a.logits_out) *reinterpret_cast<f32x4*>(a.logits_out + row * V + col) = f32x4{x[0], x[1], x[2], x[3]};
+      const f32x4 xv{x[0], x[1], x[2], x[3]};
+      *up = xv;
+      if (a.logits_out) *reinterpret_cast<f32x4*>(a.logits_out + row * V + col) = xv;
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = kNegInf;
     }
-    const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    const float m8 = fmaxf(m4, __shfl_xor(m4, 1));       // lanes 2s, 2s+1 form one segment
-    if (a.segmax && live && (n & 1) == 0) a.segmax[row * a.S + col / 8] = m8;
-    float M = m8;
-#pragma unroll
-    for (int o = 2; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float M = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    M = row16_max(M);
     float ssum = 0.f;
     if (live) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) ssum += __expf(x[c] - M);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) ssum += __shfl_xor(ssum, o);
+    ssum = row16_sum(ssum);
 
     float score[4];
     if constexpr (SAMPLE) {
@@ -204,18 +211,118 @@ __device__ __forceinline__ void resident_epilogue(const StepArgs& a, const f32x4
 #pragma unroll
     for (int c = 1; c < 4; ++c)
       if (score[c] > as.score) as = ArgState{score[c], col + c, x[c]};
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) as = arg_merge(as, shfl_xor(as, o));
-    if (n == 0 && b < a.B) {
-      const size_t pq = row * a.P + gid;
-      a.p_m[pq] = M;
-      a.p_s[pq] = ssum;
-      a.p_score[pq] = as.score;
-      a.p_idx[pq] = as.idx;
-      a.p_x[pq] = as.x;
-      best[ii] = arg_merge(best[ii], as);
-    }
+    as = row16_arg(as);
+    run[ii] = lse_merge(run[ii], LseState{M, ssum});
+    best[ii] = arg_merge(best[ii], as);
     __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// This workgroup's k best U~_j of request b as sorted order keys, by one wave.
+// Lane l owns the workgroup's columns l, l + 64, ... (in group order); dead
+// columns (past V, or groups this workgroup does not have) take no part.
+//
+// theta, the k-th largest of the 64 lane maxima (with multiplicity), bounds
+// the k-th largest element from below (k lanes each hold an element >= theta),
+// so the k best lie among the elements >= theta.  Their keys are compacted
+// into LDS (ballot prefix) and each is ranked by counting the larger keys
+// (keys of live columns are distinct).  If more than kLocCap elements reach
+// theta (many equal values), a serial selection takes over: k rounds of
+// "largest key below the last one taken".
+constexpr int kLocCap = 128;
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = row16_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ void local_topk(const StepArgs& a, const ResidentArgs& ra, const float* xs, int b, int wg, int lane,
+                           float* lmx, unsigned long long* ck) {
+  const int ncol = ra.T * kResCols, k = a.topk;
+  unsigned long long* out = a.cand_key + ((static_cast<size_t>(b) * a.gamma + a.j) * ra.nwg + wg) * k;
+  // U~ of the lane's i-th column (kNegInf and column -1 when dead)
+  auto get = [&](int i, float& v, int& col) {
+    const int gid = wg + ra.nwg * i;
+    col = gid * kResCols + lane;
+    const bool live = i < ra.T && gid < ra.G && col < a.V;
+    v = live ? xs[(i * a.B + b) * kResCols + lane] : kNegInf;
+    if (!live) col = -1;
+  };
+  float lm = kNegInf;
+  int i = 0;
+  for (; i + 4 <= ra.T; i += 4) {
+    float v[4];
+    int c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) get(i + u, v[u], c[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lm = fmaxf(lm, v[u]);
+  }
+  for (; i < ra.T; ++i) {
+    float v;
+    int c;
+    get(i, v, c);
+    lm = fmaxf(lm, v);
+  }
+  lmx[lane] = lm;
+  __builtin_amdgcn_wave_barrier();
+  int cnt = 0;
+#pragma unroll 16
+  for (int l = 0; l < kWave; ++l) cnt += lmx[l] >= lm;
+  const float theta = wave_max_dpp(cnt >= k ? lm : kNegInf);
+
+  int m = 0;
+  for (int t = 0; t < ra.T; ++t) {
+    float v;
+    int col;
+    get(t, v, col);
+    const bool take = col >= 0 && v >= theta;
+    const unsigned long long bal = __ballot(take);
+    const int pos = m + __popcll(bal & ((1ull << lane) - 1ull));
+    if (take && pos < kLocCap) ck[pos] = best_key(v, col);
+    m += __popcll(bal);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (m <= kLocCap) {
+    for (int e = lane; e < m; e += kWave) {
+      const unsigned long long key = ck[e];
+      int rank = 0, f = 0;
+      for (; f + 8 <= m; f += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += ck[f + u] > key;
+      }
+      for (; f < m; ++f) rank += ck[f] > key;
+      if (rank < k) out[rank] = key;
+    }
+    for (int t = m + lane; t < k; t += kWave) out[t] = 0ull;
+    return;
+  }
+  // serial selection over keys: the lane's largest key below the last taken
+  auto scan = [&](unsigned long long last) {
+    unsigned long long bk = 0;
+    for (int t = 0; t < ra.T; ++t) {
+      float v;
+      int col;
+      get(t, v, col);
+      const unsigned long long key = col >= 0 ? best_key(v, col) : 0ull;
+      if (key < last && key > bk) bk = key;
+    }
+    return bk;
+  };
+  unsigned long long mine = scan(~0ull);
+  for (int t = 0; t < k; ++t) {
+    unsigned long long wk = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const unsigned long long ok = __shfl_xor(wk, o);
+      wk = ok > wk ? ok : wk;
+    }
+    if (lane == 0) out[t] = wk;
+    if (mine == wk && wk != 0ull) mine = scan(wk);
   }
 }
 
@@ -224,7 +331,10 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
   constexpr int RGW = 8 / KCH;   // register groups per wave (128 VGPRs of operands)
   extern __shared__ __align__(16) unsigned char res_lds[];
   __shared__ ArgState wbest[kResWaves][kResMaxB];
+  __shared__ LseState wlse[kResWaves][kResMaxB];
   __shared__ int prev_s[kResMaxB];
+  __shared__ float ltk_max[kResWaves - 1][kWave];        // local top-k scratch of waves 1..7
+  __shared__ unsigned long long ltk_key[kResWaves - 1][kLocCap];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -233,14 +343,17 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm);
   u32x4* lds_ops = reinterpret_cast<u32x4*>(res_lds);                       // [nlds][KCH][4][64]
-  float* lds_u = reinterpret_cast<float*>(res_lds + static_cast<size_t>(ra.nlds) * KCH * 4 * kWave * 16);
+  float* lds_u0 = reinterpret_cast<float*>(res_lds + static_cast<size_t>(ra.nlds) * KCH * 4 * kWave * 16);
+  const int ubuf = ra.T * a.B * kResCols;            // floats per buffer; [2][T][B][64]
   auto gid_of = [&](int t) { return wg + ra.nwg * t; };
   auto has = [&](int t) { return t < ra.T && gid_of(t) < ra.G; };
 
-  // U_j rows of this workgroup's groups, [t][b][64] floats, by DMA: each wave
-  // instruction moves 4 rows of 256 bytes (lane i: row 4k + i/16, bytes 16 (i%16))
+  // U_j rows of this workgroup's groups, [t][b][64] floats, into buffer j % 2
+  // by DMA: each wave instruction moves 4 rows of 256 bytes (lane i: row
+  // 4k + i/16, bytes 16 (i%16))
   const int nrows = ra.T * a.B;
   auto issue_u = [&](int j) {
+    float* lds_u = lds_u0 + (j & 1) * ubuf;
     for (int k = w; 4 * k < nrows; k += kResWaves) {
       const int rr = 4 * k + (lane >> 4);
       const int t = rr / a.B, b = rr - t * a.B;
@@ -277,6 +390,7 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
 
   for (int j = 0; j < a.gamma; ++j) {
     a.j = j;
+    float* lds_u = lds_u0 + (j & 1) * ubuf;
     int prev = n < a.B ? (j == 0 ? a.anchor[n] : prev_s[n]) : 0;
     prev = min(max(prev, 0), a.V - 1);              // guard of the gathered row
     u32x4 av[KCH];
@@ -285,8 +399,12 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
       av[q] = n < a.B ? *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(prev) * a.r + 32 * q + 8 * g)
                       : u32x4{0u, 0u, 0u, 0u};
     ArgState best[QN];
+    LseState run[QN];
 #pragma unroll
-    for (int ii = 0; ii < QN; ++ii) best[ii] = ArgState{kNegInf, 0x7fffffff, 0.f};
+    for (int ii = 0; ii < QN; ++ii) {
+      best[ii] = ArgState{kNegInf, 0x7fffffff, 0.f};
+      run[ii] = LseState{kNegInf, 0.f};
+    }
 
     // products of the register groups and the LDS group; with one register
     // group per wave both accumulators are formed before either epilogue, so
@@ -317,8 +435,8 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
       f32x4 acc0[4], acc1[4];
       if (has(t)) mfma_reg(0, acc0);
       if (lds_on) mfma_lds(acc1);
-      if (has(t)) resident_epilogue<QN, SAMPLE>(a, acc0, lds_u + t * a.B * kResCols, gid_of(t), g, n, best);
-      if (lds_on) resident_epilogue<QN, SAMPLE>(a, acc1, lds_u + tl * a.B * kResCols, gid_of(tl), g, n, best);
+      if (has(t)) resident_epilogue<QN, SAMPLE>(a, acc0, lds_u + t * a.B * kResCols, gid_of(t), g, n, run, best);
+      if (lds_on) resident_epilogue<QN, SAMPLE>(a, acc1, lds_u + tl * a.B * kResCols, gid_of(tl), g, n, run, best);
     } else {
 #pragma unroll
       for (int s = 0; s < RGW; ++s) {
@@ -326,33 +444,50 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
         if (!has(t)) continue;                        // uniform per wave
         f32x4 acc[4];
         mfma_reg(s, acc);
-        resident_epilogue<QN, SAMPLE>(a, acc, lds_u + t * a.B * kResCols, gid_of(t), g, n, best);
+        resident_epilogue<QN, SAMPLE>(a, acc, lds_u + t * a.B * kResCols, gid_of(t), g, n, run, best);
       }
       if (lds_on) {
         f32x4 acc[4];
         mfma_lds(acc);
-        resident_epilogue<QN, SAMPLE>(a, acc, lds_u + tl * a.B * kResCols, gid_of(tl), g, n, best);
+        resident_epilogue<QN, SAMPLE>(a, acc, lds_u + tl * a.B * kResCols, gid_of(tl), g, n, run, best);
       }
     }
     if (n == 0) {
 #pragma unroll
       for (int ii = 0; ii < QN; ++ii)
-        if (4 * g + ii < a.B) wbest[w][4 * g + ii] = best[ii];
+        if (4 * g + ii < a.B) {
+          wbest[w][4 * g + ii] = best[ii];
+          wlse[w][4 * g + ii] = run[ii];
+        }
     }
     __syncthreads();                                  // wave bests in LDS; U_j no longer read
     if (j + 1 < a.gamma) issue_u(j + 1);
+    if (a.topk > 0 && w > 0) {                       // local candidate lists, beside the wait
+      for (int b = w - 1; b < a.B; b += kResWaves - 1)
+        local_topk(a, ra, lds_u, b, wg, lane, ltk_max[w - 1], ltk_key[w - 1]);
+    }
     if (w == 0) {
       unsigned long long key = 0;
-      if (lane < a.B) {
+      if (lane < a.B) {                               // this workgroup's partial, waves in order
         ArgState s = wbest[0][lane];
-        for (int v = 1; v < kResWaves; ++v) s = arg_merge(s, wbest[v][lane]);
+        LseState l = wlse[0][lane];
+        for (int v = 1; v < kResWaves; ++v) {
+          s = arg_merge(s, wbest[v][lane]);
+          l = lse_merge(l, wlse[v][lane]);
+        }
         key = best_key(s.score, s.idx);
+        const size_t pq = (static_cast<size_t>(lane) * a.gamma + j) * a.P + wg;
+        a.p_m[pq] = l.m;
+        a.p_s[pq] = l.s;
+        a.p_score[pq] = s.score;
+        a.p_idx[pq] = s.idx;
+        a.p_x[pq] = s.x;
       }
       const bool more = j + 1 < a.gamma;
       chain_tree(a, ra, wg, j, key, lane, more);
       if (more && lane < a.B) prev_s[lane] = best_index(load_dev(a.best + lane * a.gamma + j));
     }
-    __syncthreads();                                  // prev_s visible; U_{j+1} landed
+    __syncthreads();                                  // prev_s visible; U_{j+1} landed; lists done
   }
 }
 
@@ -397,18 +532,19 @@ bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg_out, size_t*
   // the register budget of one wave (operands, accumulators, epilogue) holds
   // without spills for these shapes
   if (B < 1 || B > kResMaxB) return false;
+  static_assert(kMaxLists >= 256, "one candidate list per workgroup");
   if (B == 1 ? (r != 64 && r != 128 && r != 256) : r != 256) return false;
   const DeviceInfo d = device_info();
   if (d.cus <= 0 || !d.coop || d.clock_khz <= 0) return false;
   const int KCH = r / 32, nreg = kResWaves * (8 / KCH);
   const int G = (V + kResCols - 1) / kResCols;
-  int nwg = d.cus;
+  int nwg = d.cus < kMaxLists ? d.cus : kMaxLists;
   if (max_wg > 0 && max_wg < nwg) nwg = max_wg;
   if (nwg > G) nwg = G;
   const int T = (G + nwg - 1) / nwg;
   const int nlds = T > nreg ? T - nreg : 0;
   if (nlds > kResWaves) return false;
-  const size_t lds = static_cast<size_t>(nlds) * KCH * 4 * kWave * 16 + static_cast<size_t>(T) * B * kResCols * 4;
+  const size_t lds = static_cast<size_t>(nlds) * KCH * 4 * kWave * 16 + 2 * static_cast<size_t>(T) * B * kResCols * 4;
   if (lds > kResLdsMax) return false;
   *nwg_out = nwg;
   *lds_out = lds;

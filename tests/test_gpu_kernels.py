@@ -105,7 +105,8 @@ def test_markov_parity(B, V, r, wdtype, T, topk, chain_path):
     (1, 3000, 128, 1.0, 8, 4),          # r = 128: 2 register groups per wave, sampled
     (1, 2504, 64, 0.0, 16, 1),          # r = 64, one workgroup: 32 register + 8 LDS groups, ragged
     (5, 5000, 256, 0.0, 8, 8),          # several requests, LDS groups
-    (16, 4104, 256, 0.7, 0, 6),         # 16 requests, sampled, ragged last group
+    (16, 4104, 256, 0.7, 16, 8),        # 16 requests, sampled, top-16, ragged last group
+    (2, 5000, 256, 0.0, 32, 0),         # top-32; the last workgroup has 8 live columns
 ])
 def test_markov_resident_chain(B, V, r, T, topk, wg, monkeypatch):
     # the resident chain with the operand share spread as on smaller devices
