@@ -68,6 +68,9 @@ hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s);
 
 hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
                           int64_t V, float* U, hipStream_t s);
+bool lm_head_skinny_fits(int64_t M, int64_t H);
+hipError_t launch_lm_head_skinny(const uint16_t* h, const uint16_t* w, int64_t M, int64_t H, int64_t V,
+                                 float* U, hipStream_t s);
 
 hipError_t launch_confidence(const void* h, bool bf16, int B, int gamma, int H,
                              const void* w_c, float b_c, const void* w_m, const void* A, int r,

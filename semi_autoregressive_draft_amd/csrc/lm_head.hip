@@ -1,4 +1,5 @@
-// LM-head contraction U[m, v] = sum_k h[m, k] * W_lm[v, k], float32 out.
+// LM-head contraction U[m, v] = sum_k h[m, k] * W_lm[v, k], float32 out (the
+// few-row path lives in lm_head_skinny.hip).
 // "DSpark 论文精读", §2.2: U_1..U_gamma = W_lm [h_1..h_gamma]; "DeepSpec 训练全流程详解",
 // §4.3 compute_logits(block_hidden).  Both operands are K-contiguous ("NT"),
 // which is exactly the per-lane layout of the MFMA operands.
@@ -6,70 +7,6 @@
 #include "internal.h"
 
 namespace dspark {
-
-// ---------------------------------------------------------------------------
-// Skinny path, M <= 12 (one or a few requests): HBM-bound on W_lm.  The whole
-// h (M rows, padded stride to spread LDS banks) sits in LDS; each wave streams
-// 16 vocabulary rows of W_lm at a time straight from HBM into the A operand of
-// v_mfma_f32_16x16x32_bf16 (row n = lane%16, 8 consecutive k per lane), with h
-// as the B operand (zero for columns >= M).  The output tile D[v][m] leaves each
-// lane 4 consecutive vocabulary entries of one row m: one 16-byte store.
-constexpr int kSkinnyWaves = 4;
-constexpr int kSkinnyTilesPerWave = 1;
-constexpr int kSkinnyUnroll = 8;
-
-__global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, float* __restrict__ U,
-    int M, int H, int V) {
-  extern __shared__ uint16_t hs[];  // [M][H + 8]
-  const int ld = H + 8;
-  for (int e = threadIdx.x; e < M * (H / 8); e += blockDim.x) {
-    const int m = e / (H / 8), kk = (e % (H / 8)) * 8;
-    *reinterpret_cast<u32x4*>(hs + m * ld + kk) =
-        *reinterpret_cast<const u32x4*>(h + static_cast<size_t>(m) * H + kk);
-  }
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, n = lane & 15;
-  const bool hcol = n < M;
-  const uint16_t* hrow = hs + n * ld;
-  const int nk = H / 32;           // full 32-wide k chunks
-  const bool ktail = (H % 32) != 0;
-
-  for (int t = 0; t < kSkinnyTilesPerWave; ++t) {
-    const int v0 = ((blockIdx.x * kSkinnyWaves + w) * kSkinnyTilesPerWave + t) * 16;
-    if (v0 >= V) break;
-    const int vr = v0 + n;
-    const bool vok = vr < V;
-    const uint16_t* wrow = W + static_cast<size_t>(vok ? vr : 0) * H + 8 * g;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int kc = 0;
-    for (; kc + kSkinnyUnroll <= nk; kc += kSkinnyUnroll) {
-      u32x4 wa[kSkinnyUnroll];
-#pragma unroll
-      for (int u = 0; u < kSkinnyUnroll; ++u)
-        wa[u] = vok ? *reinterpret_cast<const u32x4*>(wrow + (kc + u) * 32) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < kSkinnyUnroll; ++u) {
-        const u32x4 hb = hcol ? *reinterpret_cast<const u32x4*>(hrow + (kc + u) * 32 + 8 * g)
-                              : u32x4{0u, 0u, 0u, 0u};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u]), as_bf16x8(hb), acc, 0, 0, 0);
-      }
-    }
-    for (; kc < nk + (ktail ? 1 : 0); ++kc) {
-      const int k = kc * 32 + 8 * g;
-      const bool kok = k < H;
-      const u32x4 wa = (vok && kok) ? *reinterpret_cast<const u32x4*>(wrow + kc * 32) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 hb = (hcol && kok) ? *reinterpret_cast<const u32x4*>(hrow + k) : u32x4{0u, 0u, 0u, 0u};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa), as_bf16x8(hb), acc, 0, 0, 0);
-    }
-    // D[4g + i][n] = U[m = n][v0 + 4g + i]
-    const int vo = v0 + 4 * g;
-    if (hcol && vo < V)
-      *reinterpret_cast<f32x4*>(U + static_cast<size_t>(n) * V + vo) = acc;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Tiled path (larger M): the bound moves from HBM to MFMA (2MHV flops over
@@ -260,21 +197,14 @@ __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ h,
   }
 }
 
-size_t lm_head_skinny_lds(int64_t M, int64_t H) { return static_cast<size_t>(M) * (H + 8) * 2; }
-
 hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
                           int64_t V, float* U, hipStream_t s) {
   if (!bf16) {
     const dim3 grid((V + 63) / 64, (M + 63) / 64);
     hipLaunchKernelGGL(lm_head_f32, grid, dim3(256), 0, s, static_cast<const float*>(h),
                        static_cast<const float*>(w), U, (int)M, (int)H, (int)V);
-  } else if (M <= 16 && lm_head_skinny_lds(M, H) <= kSkinnyMaxLds) {
-    const int64_t tiles = (V + 15) / 16;
-    const int64_t per_block = kSkinnyWaves * kSkinnyTilesPerWave;
-    const dim3 grid((tiles + per_block - 1) / per_block);
-    hipLaunchKernelGGL(lm_head_skinny_bf16, grid, dim3(kWave * kSkinnyWaves),
-                       lm_head_skinny_lds(M, H), s, static_cast<const uint16_t*>(h),
-                       static_cast<const uint16_t*>(w), U, (int)M, (int)H, (int)V);
+  } else if (lm_head_skinny_fits(M, H)) {
+    return launch_lm_head_skinny(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w), M, H, V, U, s);
   } else {
     const int VT = static_cast<int>((V + kGV - 1) / kGV), MT = static_cast<int>((M + kGM - 1) / kGM);
     const int grid = 8 * ((VT + 7) / 8) * MT;
