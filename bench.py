@@ -84,7 +84,7 @@ def traffic_for(kernel, workload, launches_per_step):
     return t["hbm_bytes_per_launch"]
 
 
-def cpu_baseline(inp, overlap, budget_s=10.0, max_reps=30):
+def cpu_baseline(inp, overlap, budget_s=10.0, max_reps=100000):
     """The fp64 oracle timed on this host on a bounded sample: repetitions of
     the first block of the workload (the full path for one request)."""
     import numpy as np
