@@ -7,11 +7,14 @@
 //   the full-vocabulary teacher softmax.
 // "DSpark 论文精读", §3.1 and the clamp to [0, 1] in its loss code.
 //
-// One workgroup per (block, slot) row.  Pass 1 streams both logit rows once and
-// keeps per-thread online (max, sum-exp) states; a fixed-order tree gives the
-// two log-normalisers L_p, L_q.  Pass 2 adds exp(min(t - L_p, d - L_q)) (one
-// exponential per element, as exp is monotone) and walks the row backwards so
-// that its first reads hit what pass 1 touched last.
+// Many rows: one workgroup per (block, slot) row.  Pass 1 streams both logit
+// rows once and keeps per-thread online (max, sum-exp) states; a fixed-order
+// tree gives the two log-normalisers L_p, L_q.  Pass 2 adds
+// exp(min(t - L_p, d - L_q)) (one exponential per element, as exp is
+// monotone) and walks the row backwards so that its first reads hit what pass
+// 1 touched last.  Few rows (below kSplitRowsMax): each row is split into
+// chunks over several workgroups (statistics, then sums, then a fixed-order
+// finish that also computes tau when one workgroup can).
 #include "common.h"
 #include "internal.h"
 
