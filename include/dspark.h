@@ -85,6 +85,9 @@ dspark_status_t dspark_lm_head(const void* h, const void* w_lm, dspark_dtype_t d
 
 /*
  * Workspace size (bytes) needed by dspark_markov_propose for these sizes.
+ * The workspace must be zero-filled before its first use (e.g. one
+ * hipMemsetAsync at allocation); every call leaves the part that must start
+ * at zero zeroed again.  One call at a time per workspace.
  */
 dspark_status_t dspark_markov_propose_workspace(int64_t B, int64_t gamma, int64_t V,
                                                 int32_t topk, size_t* bytes);
@@ -133,7 +136,12 @@ dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int64_t r, dspa
  *   topk_prob  [B, gamma, topk] float32 softmax of U~ over the candidates
  *   logits_out [B, gamma, V] float32   U~ itself (may be NULL; costs B*gamma*V*4
  *                                      bytes of extra writes)
- *   ws, ws_bytes  workspace of at least dspark_markov_propose_workspace() bytes
+ *   ws, ws_bytes  workspace of at least dspark_markov_propose_workspace() bytes,
+ *                 zero-filled before its first use (see above)
+ * A token of -1 marks a call whose resident chain (see
+ * dspark_markov_propose_plan) waited past its time bound (100 ms per
+ * position) for a workgroup that had not started, which only other long
+ * work on the device can cause; that call's outputs are invalid.
  * Requirements: B, gamma, V, r > 0; gamma <= 16; topk <= 32 and topk <= V;
  * V <= 2^31 - 1.  DSPARK_BF16: r % 32 == 0, r <= 1024, V % 8 == 0.
  * DSPARK_F32: r <= 1024.  Otherwise EUNSUPPORTED.  T must be finite and >= 0.

@@ -136,7 +136,7 @@ def dspark_markov_propose(U, anchor, A, Bm, tokens, *, temperature: float = 0.0,
     B, gamma, V = U.shape
     r = A.shape[1]
     if ws is None:
-        ws = torch.empty(dspark_markov_propose_workspace(B, gamma, V, topk), dtype=torch.uint8,
+        ws = torch.zeros(dspark_markov_propose_workspace(B, gamma, V, topk), dtype=torch.uint8,
                          device=U.device)
     _check(lib().dspark_markov_propose(
         _ptr(U), B, gamma, V, _ptr(anchor), _ptr(A), _ptr(Bm), _dtype(A), r, float(temperature),

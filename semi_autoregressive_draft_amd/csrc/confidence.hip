@@ -51,8 +51,9 @@ __global__ __launch_bounds__(kWave* kMaxGamma) void confidence_survival_kernel(
   const int b = blockIdx.x, lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   float s = dot_row(h + (static_cast<size_t>(b) * gamma + j) * H, w_c, H, lane, vec_h);
   if (w_m) {
+    // a -1 token (a chain that timed out) contributes no Markov term
     const int prev = j == 0 ? anchor[b] : tokens[b * gamma + j - 1];
-    s += dot_row(A + static_cast<size_t>(prev) * r, w_m, r, lane, vec_r);
+    if (prev >= 0) s += dot_row(A + static_cast<size_t>(prev) * r, w_m, r, lane, vec_r);
   }
   s = wave_sum(s);
   if (lane == 0) part[j] = s;

@@ -1,5 +1,6 @@
 // C ABI of the DSpark draft-proposal hot path: argument checks, workspace
 // carving and kernel dispatch.  Every check runs before anything is enqueued.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -29,6 +30,14 @@ dspark_status_t hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// number of a resident-chain call (never 0, the zero-filled workspace's value)
+unsigned next_epoch() {
+  static std::atomic<unsigned> counter{0};
+  unsigned e = counter.fetch_add(1u) + 1u;
+  if (e == 0u) e = counter.fetch_add(1u) + 1u;
+  return e;
+}
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 constexpr int64_t kI32Max = 2147483647;
@@ -41,9 +50,14 @@ size_t markov_cand_bytes(int64_t B, int64_t gamma, int32_t topk) {
   return align_up(static_cast<size_t>(B) * gamma * kMaxLists * topk * 8);
 }
 
+// The part that must be zero when a call starts (the resident chain's wait tree
+// and its keys, sized for the largest resident batch) sits at a fixed offset,
+// the start, so that calls of any shape find it where the last call cleared it.
+constexpr size_t kZeroHead = kSyncWords * 4 + static_cast<size_t>(kResidentMaxB) * kMaxGamma * 8;
+
 size_t markov_ws_bytes(int64_t B, int64_t gamma, int64_t V, int32_t topk) {
   const size_t rows = static_cast<size_t>(B) * gamma;
-  size_t s = 5 * align_up(rows * markov_partials(V) * 4) + align_up(rows * 8) + kSyncWords * 4;
+  size_t s = kZeroHead + 5 * align_up(rows * markov_partials(V) * 4);
   if (topk > 0) s += align_up(rows * markov_segments(V) * 4);
   if (topk > 0 && B <= kResidentMaxB) s += markov_cand_bytes(B, gamma, topk);
   return s;
@@ -174,7 +188,10 @@ extern "C" dspark_status_t dspark_markov_propose(
   a.off_hi = static_cast<uint32_t>(offset >> 32);
   const size_t P = markov_partials(V);
   const size_t arr = align_up(static_cast<size_t>(B) * gamma * P * 4);
-  char* base = static_cast<char*>(ws);
+  char* const head = static_cast<char*>(ws);
+  a.sync = reinterpret_cast<unsigned*>(head);
+  a.best = reinterpret_cast<unsigned long long*>(head + kSyncWords * 4);
+  char* base = head + kZeroHead;
   a.p_score = reinterpret_cast<float*>(base);
   a.p_idx = reinterpret_cast<int32_t*>(base + arr);
   a.p_x = reinterpret_cast<float*>(base + 2 * arr);
@@ -182,10 +199,7 @@ extern "C" dspark_status_t dspark_markov_propose(
   a.p_s = reinterpret_cast<float*>(base + 4 * arr);
   a.P = static_cast<int>(P);
   a.S = static_cast<int>(markov_segments(V));
-  const size_t keys = align_up(static_cast<size_t>(B) * gamma * 8);
-  char* tail = base + 5 * arr + keys + kSyncWords * 4;
-  a.best = reinterpret_cast<unsigned long long*>(base + 5 * arr);
-  a.sync = reinterpret_cast<unsigned*>(base + 5 * arr + keys);
+  char* tail = base + 5 * arr;
   a.logits_out = logits_out;
   a.tok_logit = tok_logit;
   a.lse = lse;
@@ -203,9 +217,10 @@ extern "C" dspark_status_t dspark_markov_propose(
     a.segmax = resident ? nullptr : reinterpret_cast<float*>(tail);
     if (resident) a.cand_key = reinterpret_cast<unsigned long long*>(tail + seg);
   }
-  hipError_t e = launch_markov_begin(a, stream);
+  hipError_t e = hipSuccess;
   if (resident) {
-    if (e == hipSuccess) e = launch_markov_resident(a, a.sync, nwg, lds, stream);
+    a.epoch = next_epoch();
+    e = launch_markov_resident(a, a.sync, nwg, lds, stream);
   } else {
     for (int j = 0; j < gamma && e == hipSuccess; ++j) {
       a.j = j;

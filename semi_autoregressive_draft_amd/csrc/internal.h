@@ -21,11 +21,12 @@ struct StepArgs {
   const float* U;          // [B, gamma, V]
   const int32_t* anchor;   // [B]
   int32_t* tokens;         // [B, gamma] (written after the chain)
-  // [B, gamma] running argmax keys: (orderable score << 32) | ~index, raised
-  // with atomic max by every (request, tile) of position j; the step kernel of
-  // position j+1 decodes its previous token from entry j
+  // [B, gamma] argmax keys of the resident chain: (orderable score << 32) |
+  // ~index, raised with atomic max; zero between calls (the finish kernel
+  // clears them after reading)
   unsigned long long* best;
   unsigned* sync;          // [kSyncWords] counters, flags and group keys of the resident chain
+  unsigned epoch;          // number of this call (marks a timed-out resident chain)
   int tile_cols;           // vocabulary columns per partial (64 resident, 128 bf16, 256 f32)
   int resident;            // 1: the chain ran as the resident kernel
   // resident chain with top-k: each workgroup's k largest order keys of U~_j
@@ -60,7 +61,6 @@ struct StepArgs {
 size_t markov_partials(int64_t V);
 size_t markov_segments(int64_t V);
 int markov_tile_cols(bool bf16);
-hipError_t launch_markov_begin(StepArgs a, hipStream_t s);
 bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg, size_t* lds);
 hipError_t launch_markov_resident(StepArgs a, unsigned* sync, int nwg, size_t lds, hipStream_t s);
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s);

@@ -12,10 +12,9 @@
 // Two launches per position: the step kernel streams Bm and U_j once for all
 // requests and leaves one partial (max, sum-exp, best score/index) per
 // (request, vocabulary tile); a merge kernel with one workgroup per request
-// folds them in a fixed order into x_j, U~_j[x_j] and lse_j, and stores x_j
-// also as a 64-bit argmax key (the form in which the resident chain of
-// markov_resident.hip hands tokens between positions).  The top-k candidates
-// are selected after the chain, off the sequential path.
+// folds them in a fixed order into x_j, U~_j[x_j] and lse_j.  The top-k
+// candidates are selected after the chain, off the sequential path.  (Small
+// batches run the whole chain in one kernel instead: markov_resident.hip.)
 #include "common.h"
 #include "internal.h"
 #include "markov_dev.h"
@@ -42,9 +41,10 @@ constexpr int kSeg = 8;            // vocabulary columns per top-k segment
 // Fold of one request's per-tile partials of position j by a 256-thread
 // workgroup: thread t takes tiles t, t+256, ... (loads issued kFoldBatch at a
 // time), then a fixed xor tree and waves 0..3 in order; writes U~_j[x_j] and
-// lse_j.  x_j is the fold's own argmax (per-position chain, which also stores
-// its key) or, after the resident chain, the chain's final key (the same
-// element: both rank by score, then lowest index).
+// lse_j.  x_j is the fold's own argmax (per-position chain) or, after the
+// resident chain, the chain's final key (the same element: both rank by
+// score, then lowest index), which the fold then clears; -1 marks a resident
+// chain whose grid-wide wait ran out of time in this call.
 constexpr int kMergeThreads = 256;
 constexpr int kFoldBatch = 4;
 
@@ -85,10 +85,11 @@ __device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
     for (int i = 1; i < kMergeThreads / kWave; ++i) { l = lse_merge(l, red_l[i]); s = arg_merge(s, red_a[i]); }
     const int row = b * a.gamma + j;
     if (from_key) {
-      a.tokens[row] = best_index(a.best[row]);
+      const bool timed_out = a.sync[0] == a.epoch;
+      a.tokens[row] = timed_out ? -1 : best_index(a.best[row]);
+      a.best[row] = 0ull;
     } else {
       a.tokens[row] = s.idx;
-      a.best[row] = best_key(s.score, s.idx);
     }
     if (a.tok_logit) a.tok_logit[row] = s.x;
     if (a.lse) a.lse[row] = l.m + logf(l.s);
@@ -441,14 +442,14 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Zeroing of the argmax keys and the resident chain's wait tree before
-// position 0 (a kernel, so that the chain can be captured in a graph); the
-// per-position merge; the fold of every (request, position) after the
-// resident chain.
-__global__ __launch_bounds__(256) void markov_begin(unsigned long long* best, int n, unsigned* sync) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) best[i] = 0ull;
-  if (i < kSyncWords) sync[i] = 0u;
+// The per-position merge, and the fold of every (request, position) after the
+// resident chain.  After the resident chain the finish kernels (markov_fold,
+// markov_topk_lists) leave the wait tree zeroed for the next call: their
+// workgroups clear it in slices (all of its readers have finished); word 0,
+// the time-out mark, holds a call number and is never cleared.
+__device__ __forceinline__ void clear_wait_tree(const StepArgs& a) {
+  const int L = blockIdx.x * a.gamma + blockIdx.y, n = a.B * a.gamma;
+  for (int i = L * blockDim.x + threadIdx.x + 1; i < kSyncWords; i += n * blockDim.x) a.sync[i] = 0u;
 }
 
 __global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
@@ -457,6 +458,7 @@ __global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
 
 __global__ __launch_bounds__(kMergeThreads) void markov_fold(StepArgs a) {
   fold_request(a, blockIdx.x, blockIdx.y, true);
+  clear_wait_tree(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -766,6 +768,7 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
   if (tid == 0) nlive = 0;
   hk[tid] = head;
   fold_request(a, b, j, true);                        // ends with a barrier: hk complete
+  clear_wait_tree(a);
   if (head != 0ull) {
     int rank = 0, u = 0;
     for (; u + 8 <= L; u += 8) {
@@ -863,13 +866,6 @@ hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(markov_merge, dim3(a.B), dim3(kMergeThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_markov_begin(StepArgs a, hipStream_t s) {
-  const int n = a.B * a.gamma;
-  const int m = n > kSyncWords ? n : kSyncWords;
-  hipLaunchKernelGGL(markov_begin, dim3((m + 255) / 256), dim3(256), 0, s, a.best, n, a.sync);
   return hipGetLastError();
 }
 

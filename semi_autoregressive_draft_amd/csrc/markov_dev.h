@@ -33,9 +33,10 @@ __device__ __forceinline__ bool ranks_before(float xa, int ia, float xb, int ib)
   return xa > xb || (xa == xb && ia < ib);
 }
 
-// x_{j-1} of request b: the anchor for j == 0, else the final key of j-1
+// x_{j-1} of request b on the per-position chain: the anchor for j == 0, else
+// the token the merge of position j-1 wrote
 __device__ __forceinline__ int prev_token(const StepArgs& a, int b, int j) {
-  return j == 0 ? a.anchor[b] : best_index(a.best[b * a.gamma + j - 1]);
+  return j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + j - 1];
 }
 
 }  // namespace dspark

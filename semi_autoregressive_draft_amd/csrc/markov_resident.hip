@@ -23,9 +23,18 @@
 // arrive there writes one release flag per group, and each workgroup polls its
 // group's flag.  Every step uses atomics or loads at device scope and waits
 // for their return before the next, so a key is final when its counter says
-// so.  The launch is cooperative, so every workgroup is resident and every wait
-// ends; each wait is also bounded in time so that every wave terminates
-// whatever happens (a wait that runs out sets a flag word).
+// so.  The grid is one workgroup per compute unit, and the launcher checks
+// with the occupancy query that a compute unit holds one: on a device running
+// nothing else every workgroup is resident at once, and work on other streams
+// can only delay a workgroup's start (its own workgroups finish without
+// waiting for this kernel).  Each wait is bounded in time, so every wave
+// terminates whatever happens; a wait that runs out writes the call's number
+// into word 0 of the wait tree, and the fold then returns -1 tokens.  (A
+// cooperative launch would give the same residency guarantee but costs about
+// 11 us of dispatch gap on each side of the kernel.)
+//
+// The wait tree and the keys are zero when a call starts: the workspace is
+// zero-filled before its first use and the finish kernels clear both again.
 //
 // With top-k, the epilogue leaves U~_j in LDS (over the U_j rows it read, two
 // buffers alternating by position), and while wave 0 walks the wait tree the
@@ -144,7 +153,7 @@ __device__ void chain_tree(const StepArgs& a, const ResidentArgs& ra, int wg, in
     const unsigned long long t0 = wall_clock64();
     while (load_dev(sy + kSyncRelease + 64 * grp) < static_cast<unsigned>(j + 1)) {
       if (wall_clock64() - t0 > ra.wait_ticks) {
-        __hip_atomic_store(sy + kSyncTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sy + kSyncTimeout, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -495,7 +504,7 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
 // host side
 
 namespace {
-struct DeviceInfo { int cus = 0; int coop = 0; int clock_khz = 0; };
+struct DeviceInfo { int cus = 0; int clock_khz = 0; };
 DeviceInfo device_info() {
   static thread_local DeviceInfo cache[16];
   int dev = 0;
@@ -503,7 +512,6 @@ DeviceInfo device_info() {
   DeviceInfo& d = cache[dev];
   if (d.cus == 0) {
     if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
         hipDeviceGetAttribute(&d.clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
       d = DeviceInfo{};
   }
@@ -515,8 +523,13 @@ hipError_t launch_res(StepArgs a, ResidentArgs ra, size_t lds, hipStream_t s) {
   const void* fn = reinterpret_cast<const void*>(&markov_resident<KCH, QN, SAMPLE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
+  // every workgroup must fit at once: at most one per compute unit is asked for
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kResThreads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorLaunchOutOfResources;
   void* args[] = {&a, &ra};
-  return hipLaunchCooperativeKernel(fn, dim3(ra.nwg), dim3(kResThreads), args, static_cast<unsigned>(lds), s);
+  return hipLaunchKernel(fn, dim3(ra.nwg), dim3(kResThreads), args, lds, s);
 }
 
 template <int KCH>
@@ -535,7 +548,7 @@ bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg_out, size_t*
   static_assert(kMaxLists >= 256, "one candidate list per workgroup");
   if (B == 1 ? (r != 64 && r != 128 && r != 256) : r != 256) return false;
   const DeviceInfo d = device_info();
-  if (d.cus <= 0 || !d.coop || d.clock_khz <= 0) return false;
+  if (d.cus <= 0 || d.clock_khz <= 0) return false;
   const int KCH = r / 32, nreg = kResWaves * (8 / KCH);
   const int G = (V + kResCols - 1) / kResCols;
   int nwg = d.cus < kMaxLists ? d.cus : kMaxLists;

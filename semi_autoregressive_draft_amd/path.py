@@ -39,7 +39,8 @@ class DraftPath:
         self.topk_idx = torch.empty((B, gamma, topk), dtype=torch.int32, device=dev) if topk else None
         self.topk_prob = torch.empty((B, gamma, topk), **f32) if topk else None
         self.logits = torch.empty((B, gamma, V), **f32) if overlap == "dense" else None
-        self.ws_markov = torch.empty(bd.dspark_markov_propose_workspace(B, gamma, V, topk),
+        # zero-filled once; every propose call leaves it ready for the next
+        self.ws_markov = torch.zeros(bd.dspark_markov_propose_workspace(B, gamma, V, topk),
                                      dtype=torch.uint8, device=dev)
         self.conf = torch.empty((B, gamma), **f32)
         self.survival = torch.empty((B, gamma), **f32)

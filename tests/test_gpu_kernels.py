@@ -123,6 +123,33 @@ def test_markov_resident_chain(B, V, r, T, topk, wg, monkeypatch):
                 temperature=T, seeds=seeds, offset=2, topk=topk)
 
 
+def test_markov_workspace_is_left_ready_for_the_next_call(monkeypatch):
+    # one zero-filled workspace serves resident and per-position calls of
+    # different shapes in turn: each call must leave it as the next expects
+    dev = require_gpu()
+    ws = torch.zeros(bd.dspark_markov_propose_workspace(3, 7, 5000, 16), dtype=torch.uint8, device=dev)
+    for B, r, resident, T in [(1, 256, True, 0.0), (3, 256, True, 1.0), (1, 64, False, 0.0),
+                              (2, 256, True, 0.0), (1, 256, True, 0.0)]:
+        monkeypatch.setenv("DSPARK_MARKOV_RESIDENT", "1" if resident else "0")
+        assert (bd.dspark_markov_propose_plan(B, 5000, r) > 0) == resident
+        U, anchor, A, Bm = _markov_case(B, 5000, r, "bf16", seed=B + r)
+        seeds = np.arange(B, dtype=np.uint64) + 11 if T > 0 else None
+        Ud = to_dev(U)
+        tokens = torch.empty((B, 7), dtype=torch.int32, device=dev)
+        tl = torch.empty((B, 7), dtype=torch.float32, device=dev)
+        ls = torch.empty_like(tl)
+        ti = torch.empty((B, 7, 16), dtype=torch.int32, device=dev)
+        tp = torch.empty((B, 7, 16), dtype=torch.float32, device=dev)
+        bd.dspark_markov_propose(Ud, to_dev(anchor), to_dev(A, "bf16"), to_dev(Bm, "bf16"), tokens,
+                                 temperature=T, seeds=to_dev(seeds) if seeds is not None else None,
+                                 topk=16, tok_logit=tl, lse=ls, topk_idx=ti, topk_prob=tp, ws=ws)
+        torch.cuda.synchronize()
+        gpu = dict(tokens=tokens.cpu().numpy(), tok_logit=tl.cpu().numpy(), lse=ls.cpu().numpy(),
+                   topk_idx=ti.cpu().numpy(), topk_prob=tp.cpu().numpy())
+        check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"),
+                    temperature=T, seeds=seeds, topk=16)
+
+
 def test_markov_plan_follows_the_shape_rules(monkeypatch):
     require_gpu()
     assert bd.dspark_markov_propose_plan(1, 151936, 256) > 0
