@@ -205,7 +205,13 @@ dspark_status_t dspark_overlap_tau_workspace(int64_t N, int64_t gamma, int64_t V
  *   tau            [N] float32         tau_prob; 0 for a block with no valid slot
  *   accept_rate_at [gamma] float64 or NULL   sum valid*alpha / sum valid (0 if none)
  *   tau_mean       [1] float64 or NULL       mean tau over blocks with a valid slot
- *   ws, ws_bytes   workspace of at least dspark_overlap_tau_workspace() bytes
+ *   ws, ws_bytes   workspace of at least dspark_overlap_tau_workspace() bytes,
+ *                  zero-filled before its first use; every call leaves the
+ *                  part that must start at zero zeroed again (one call at a
+ *                  time per workspace).  Few rows (N * gamma <= 64) run as one
+ *                  launch whose chunks wait for their row's normalisers; if
+ *                  such a wait runs past its bound (100 ms, only possible when
+ *                  other long work occupies the device) tau and tau_mean are NaN.
  * Requirements: N, gamma, V > 0; gamma <= 16; V % 4 == 0 (16-byte rows);
  * dense mode: k == 0 and cand_* NULL; candidate mode: 1 <= k <= 64 and cand_*
  * non-NULL.

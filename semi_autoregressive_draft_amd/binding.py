@@ -167,7 +167,7 @@ def dspark_overlap_tau(teacher, alpha, tau, *, draft=None, cand_idx=None, cand_p
     N, gamma, V = teacher.shape
     k = 0 if cand_idx is None else cand_idx.shape[-1]
     if ws is None:
-        ws = torch.empty(dspark_overlap_tau_workspace(N, gamma, V), dtype=torch.uint8,
+        ws = torch.zeros(dspark_overlap_tau_workspace(N, gamma, V), dtype=torch.uint8,
                          device=teacher.device)
     _check(lib().dspark_overlap_tau(
         _ptr(teacher), _ptr(draft), _ptr(cand_idx), _ptr(cand_prob), k, _ptr(valid), N, gamma, V,

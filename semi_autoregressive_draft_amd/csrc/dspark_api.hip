@@ -1,6 +1,5 @@
 // C ABI of the DSpark draft-proposal hot path: argument checks, workspace
 // carving and kernel dispatch.  Every check runs before anything is enqueued.
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -31,13 +30,6 @@ dspark_status_t hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// number of a resident-chain call (never 0, the zero-filled workspace's value)
-unsigned next_epoch() {
-  static std::atomic<unsigned> counter{0};
-  unsigned e = counter.fetch_add(1u) + 1u;
-  if (e == 0u) e = counter.fetch_add(1u) + 1u;
-  return e;
-}
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 constexpr int64_t kI32Max = 2147483647;
@@ -76,10 +68,18 @@ size_t overlap_ws_tau_bytes(int64_t N, int64_t gamma) {
   return align_up(static_cast<size_t>(overlap_tau_blocks(N)) * (2 * gamma + 2) * sizeof(double));
 }
 
+// zero head (the single-launch path's counters, fixed offset 0), tau
+// partials, chunk states of the split path, and for the single-launch path
+// the row normalisers and 64-bit chunk slots
 size_t overlap_ws_bytes(int64_t N, int64_t gamma, int64_t V) {
-  const int nchunk = overlap_split_chunks(N * gamma, V);
-  const size_t split = nchunk > 1 ? align_up(static_cast<size_t>(N * gamma) * nchunk * 5 * sizeof(float)) : 0;
-  return overlap_ws_tau_bytes(N, gamma) + split;
+  const int64_t rows = N * gamma;
+  const int nchunk = overlap_split_chunks(rows, V);
+  size_t s = kOvSyncWords * 4 + overlap_ws_tau_bytes(N, gamma);
+  if (nchunk > 1) {
+    s += align_up(static_cast<size_t>(rows) * nchunk * 5 * sizeof(float));
+    s += align_up(static_cast<size_t>(rows) * 16) + align_up(static_cast<size_t>(rows) * nchunk * 3 * 8);
+  }
+  return s;
 }
 
 }  // namespace
@@ -300,10 +300,19 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
   a.tau = tau;
   a.accept_rate_at = accept_rate_at;
   a.tau_mean = tau_mean;
-  a.ws_acc = static_cast<double*>(ws);
+  char* p = static_cast<char*>(ws);
+  a.sync = reinterpret_cast<unsigned*>(p);
+  p += kOvSyncWords * 4;
+  a.ws_acc = reinterpret_cast<double*>(p);
+  p += overlap_ws_tau_bytes(N, gamma);
   a.nchunk = overlap_split_chunks(N * gamma, V);
-  a.ws_split = a.nchunk > 1
-      ? reinterpret_cast<float*>(static_cast<char*>(ws) + overlap_ws_tau_bytes(N, gamma))
-      : nullptr;
+  if (a.nchunk > 1) {
+    const size_t rows = static_cast<size_t>(N * gamma);
+    a.ws_split = reinterpret_cast<float*>(p);
+    p += align_up(rows * a.nchunk * 5 * sizeof(float));
+    a.ws_norm = reinterpret_cast<unsigned long long*>(p);
+    p += align_up(rows * 16);
+    a.ws_fused = reinterpret_cast<unsigned long long*>(p);
+  }
   return hip_status(launch_overlap_tau(a, stream), fn);
 }

@@ -7,6 +7,11 @@
 
 namespace dspark {
 
+// compute units and wall-clock rate (kHz) of the current device; zeros when
+// there is none
+struct DeviceInfo { int cus = 0; int clock_khz = 0; };
+DeviceInfo device_info();
+
 constexpr int kMaxRank = 1024;
 constexpr int kMaxTopk = 32;
 constexpr int kMaxGamma = 16;
@@ -15,6 +20,7 @@ constexpr int kMaxLists = 256;   // workgroups of the resident chain
 constexpr int kResidentMaxB = 16;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
 constexpr int kSyncWords = 12 * 1024;   // 48 KB: the resident chain's wait tree (zero at launch)
+constexpr int kOvSyncWords = 8192;      // 32 KB: the single-launch overlap's counters (zero at launch)
 
 // Arguments of one Markov position (step + merge kernels).
 struct StepArgs {
@@ -92,6 +98,14 @@ struct OverlapArgs {
   double* ws_acc;        // [nblk][2*gamma + 2] per-workgroup partial sums
   int nblk;
   float* ws_split;       // [rows][nchunk][5] chunk states (split path only)
+  // single-launch path for few rows: [rows][nchunk][3] 64-bit slots (teacher
+  // state, draft state, chunk sum), [rows][2] tagged row normalisers, the
+  // wait words
+  unsigned long long* ws_fused;
+  unsigned long long* ws_norm;
+  unsigned* sync;        // kOvSyncWords words, zero when a call starts
+  unsigned epoch;        // number of this call
+  unsigned long long wait_ticks;
   int nchunk;            // workgroups per row (1: one workgroup per row)
   int chunk4;            // float4 elements per chunk (set by the launcher)
 };
@@ -99,5 +113,6 @@ struct OverlapArgs {
 int overlap_tau_blocks(int64_t N);
 int overlap_split_chunks(int64_t rows, int64_t V);
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s);
+unsigned next_epoch();
 
 }  // namespace dspark

@@ -504,19 +504,6 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
 // host side
 
 namespace {
-struct DeviceInfo { int cus = 0; int clock_khz = 0; };
-DeviceInfo device_info() {
-  static thread_local DeviceInfo cache[16];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return DeviceInfo{};
-  DeviceInfo& d = cache[dev];
-  if (d.cus == 0) {
-    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&d.clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
-      d = DeviceInfo{};
-  }
-  return d;
-}
 
 template <int KCH, int QN, bool SAMPLE>
 hipError_t launch_res(StepArgs a, ResidentArgs ra, size_t lds, hipStream_t s) {

@@ -205,7 +205,10 @@ __global__ __launch_bounds__(kWave) void overlap_split_finish(OverlapArgs a) {
 }
 
 // tau per block and per-workgroup partial sums for the aggregates (a full
-// workgroup of kTauThreads threads calls it for its range of blocks)
+// workgroup of kTauThreads threads calls it for its range of blocks).  DEV:
+// alpha was written by other workgroups of the same launch, so it is read at
+// device scope.
+template <bool DEV = false>
 __device__ void tau_range(const OverlapArgs& a, int blk) {
   __shared__ double red[kTauThreads / kWave][2 * kMaxGamma + 2];
   __shared__ double tot[2 * kMaxGamma + 2];
@@ -222,7 +225,8 @@ __device__ void tau_range(const OverlapArgs& a, int blk) {
 #pragma unroll
     for (int i = 0; i < kMaxGamma; ++i) {
       if (i < G) {
-        const float al = a.alpha[n * G + i];
+        const float al = DEV ? __hip_atomic_load(a.alpha + n * G + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : a.alpha[n * G + i];
         const bool v = a.valid ? a.valid[n * G + i] != 0 : true;
         has |= v;
         run *= al;
@@ -259,7 +263,7 @@ __device__ void tau_range(const OverlapArgs& a, int blk) {
   }
 }
 
-__global__ __launch_bounds__(kTauThreads) void tau_blocks(OverlapArgs a) { tau_range(a, blockIdx.x); }
+__global__ __launch_bounds__(kTauThreads) void tau_blocks(OverlapArgs a) { tau_range<false>(a, blockIdx.x); }
 
 // few rows: one workgroup finishes every row (a wave per row) and then tau
 __global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapArgs a) {
@@ -281,7 +285,234 @@ __global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapA
     if (lane == 0) a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
   }
   __syncthreads();   // alpha of every row written by this workgroup
-  tau_range(a, 0);
+  tau_range<false>(a, 0);
+}
+
+// ---- one launch for few rows ----------------------------------------------
+// Grid (chunk, row) with the chunk's teacher (and draft) values held in
+// registers across both passes.  Each chunk publishes its online states with
+// device-scope atomics; the last chunk of a row to arrive (known from the
+// row counter's old value) folds them in chunk order into the normalisers
+// and, in dense mode, publishes them tagged with this call's number (the tag
+// releases the row); every chunk of the row then adds its sum of exp(min(t - L_p,
+// d - L_q)), and the last of those folds the sums into alpha.  In candidate
+// mode the row's last arriver gathers the candidates instead and no chunk
+// waits.  The last row to finish computes tau and the aggregates, and clears
+// the counters for the next call.  Dense mode needs every chunk resident at
+// once (the launcher checks the occupancy); the wait is bounded in time, and
+// a wait that runs out marks the call, which then reports NaN for tau.
+constexpr int kFusedPer = 4;                    // float4 per thread and array
+constexpr int kOvTimeout = 0;                   // word 0: call number of a timed-out wait
+constexpr int kOvRowsDone = 32;
+constexpr int kOvCnt1 = 64;                     // + 32 * row: chunk states published
+constexpr int kOvCnt2 = kOvCnt1 + 32 * kFusedFinishRows;   // + 32 * row: chunk sums published
+static_assert(kOvCnt2 + 32 * kFusedFinishRows <= kOvSyncWords, "overlap wait words");
+
+__device__ __forceinline__ unsigned long long pack2(float x, float y) {
+  return (static_cast<unsigned long long>(__float_as_uint(y)) << 32) | __float_as_uint(x);
+}
+__device__ __forceinline__ float lo_f(unsigned long long v) { return __uint_as_float(static_cast<uint32_t>(v)); }
+__device__ __forceinline__ float hi_f(unsigned long long v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
+__device__ __forceinline__ unsigned long long xchg_dev(unsigned long long* p, unsigned long long v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned add_dev(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// keep the value live so that the wave waits for the atomic's return here
+__device__ __forceinline__ void wait_for(unsigned long long v) { asm volatile("" ::"v"(v) : "memory"); }
+
+template <bool DENSE>
+__global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
+  constexpr int NW = kSplitThreads / kWave;
+  __shared__ LseState red_l[NW];
+  __shared__ float red_f[NW];
+  __shared__ int flag_s;
+  __shared__ float L_s[2];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rows = a.N * a.gamma;
+  const bool valid = !a.valid || a.valid[row];
+  const size_t V = static_cast<size_t>(a.V);
+  const int e0 = c * a.chunk4, e1 = min(e0 + a.chunk4, a.V / 4);
+  const f32x4* tp = reinterpret_cast<const f32x4*>(a.teacher + row * V);
+  const f32x4* dp = reinterpret_cast<const f32x4*>(DENSE ? a.draft + row * V : a.teacher + row * V);
+  unsigned* sy = a.sync;
+  unsigned long long* slot = a.ws_fused + (static_cast<size_t>(row) * a.nchunk + c) * 3;
+
+  f32x4 tv[kFusedPer], dv[kFusedPer];
+  LseState lt{kNegInf, 0.f}, ld{kNegInf, 0.f};
+#pragma unroll
+  for (int i = 0; i < kFusedPer; ++i) {
+    const int e = e0 + tid + i * kSplitThreads;
+    const bool on = valid && e < e1;
+    tv[i] = on ? tp[e] : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    dv[i] = (DENSE && on) ? dp[e] : f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+  }
+#pragma unroll
+  for (int i = 0; i < kFusedPer; ++i) {
+    if (valid && e0 + tid + i * kSplitThreads < e1) {
+      online_add4(lt, tv[i]);
+      if (DENSE) online_add4(ld, dv[i]);
+    }
+  }
+  const LseState rt = block_lse_state<NW>(lt, red_l);
+  const LseState rd = block_lse_state<NW>(ld, red_l);
+
+  // 1. publish the chunk states; the row's last arriver folds them
+  if (tid == 0) {
+    wait_for(xchg_dev(slot, pack2(rt.m, rt.s)));
+    wait_for(xchg_dev(slot + 1, pack2(rd.m, rd.s)));
+    flag_s = add_dev(sy + kOvCnt1 + 32 * row, 1u) == static_cast<unsigned>(a.nchunk) - 1u;
+  }
+  __syncthreads();
+  bool row_done = false;                   // this workgroup has written alpha[row]
+  if (flag_s && w == 0) {
+    LseState t{kNegInf, 0.f}, d{kNegInf, 0.f};
+    const unsigned long long* rs = a.ws_fused + static_cast<size_t>(row) * a.nchunk * 3;
+    unsigned long long st[2] = {0ull, 0ull}, sd[2] = {0ull, 0ull};   // all loads issued first
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = lane + u * kWave;
+      if (k < a.nchunk) { st[u] = ld_dev(rs + 3 * k); sd[u] = ld_dev(rs + 3 * k + 1); }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (lane + u * kWave < a.nchunk) {
+        t = lse_merge(t, LseState{lo_f(st[u]), hi_f(st[u])});
+        d = lse_merge(d, LseState{lo_f(sd[u]), hi_f(sd[u])});
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      t = lse_merge(t, shfl_xor(t, o));
+      d = lse_merge(d, shfl_xor(d, o));
+    }
+    const float Lt = t.m + logf(t.s), Ld = d.m + logf(d.s);
+    if constexpr (DENSE) {
+      // each normaliser travels with this call's number in one 64-bit word,
+      // so the word is its own release flag
+      if (lane < 2) {
+        const unsigned long long tagged =
+            (static_cast<unsigned long long>(a.epoch) << 32) | __float_as_uint(lane == 0 ? Lt : Ld);
+        __hip_atomic_store(a.ws_norm + 2 * row + lane, tagged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      float sc = valid ? candidate_overlap(a, row, Lt, lane, kWave) : 0.f;
+      sc = wave_sum(sc);
+      if (lane == 0) {
+        const float al = valid ? fminf(fmaxf(sc, 0.f), 1.f) : 0.f;
+        wait_for(__hip_atomic_exchange(reinterpret_cast<unsigned*>(a.alpha) + row, __float_as_uint(al),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
+      row_done = true;
+    }
+  }
+  if constexpr (DENSE) {
+    // 2. wait for the row's normalisers, add this chunk's overlap sum
+    if (tid == 0) {
+      const unsigned long long t0 = wall_clock64();
+      unsigned long long nt, nd;
+      while (true) {
+        nt = ld_dev(a.ws_norm + 2 * row);
+        nd = ld_dev(a.ws_norm + 2 * row + 1);
+        if (static_cast<unsigned>(nt >> 32) == a.epoch && static_cast<unsigned>(nd >> 32) == a.epoch) break;
+        if (wall_clock64() - t0 > a.wait_ticks) {
+          __hip_atomic_store(sy + kOvTimeout, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      L_s[0] = __uint_as_float(static_cast<uint32_t>(nt));
+      L_s[1] = __uint_as_float(static_cast<uint32_t>(nd));
+    }
+    __syncthreads();
+    const float Lt = L_s[0], Ld = L_s[1];
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i)
+      if (valid && e0 + tid + i * kSplitThreads < e1) sm += sum_exp_min4(tv[i], dv[i], Lt, Ld);
+    const float tot = block_sum<NW>(sm, red_f);
+    if (tid == 0) {
+      wait_for(xchg_dev(slot + 2, __float_as_uint(tot)));
+      flag_s = add_dev(sy + kOvCnt2 + 32 * row, 1u) == static_cast<unsigned>(a.nchunk) - 1u;
+    }
+    __syncthreads();
+    if (flag_s && w == 0) {
+      const unsigned long long* rs = a.ws_fused + static_cast<size_t>(row) * a.nchunk * 3;
+      unsigned long long sv[2] = {0ull, 0ull};                       // all loads issued first
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (lane + u * kWave < a.nchunk) sv[u] = ld_dev(rs + 3 * (lane + u * kWave) + 2);
+      float s2 = __uint_as_float(static_cast<uint32_t>(sv[0])) + __uint_as_float(static_cast<uint32_t>(sv[1]));
+      s2 = wave_sum(s2);
+      if (lane == 0) {
+        const float al = valid ? fminf(fmaxf(s2, 0.f), 1.f) : 0.f;
+        wait_for(__hip_atomic_exchange(reinterpret_cast<unsigned*>(a.alpha) + row, __float_as_uint(al),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
+      row_done = true;
+    }
+  }
+  // 3. the last row to finish computes tau and clears the counters
+  __syncthreads();
+  if (tid == 0) flag_s = 0;
+  __syncthreads();
+  if (row_done && tid == 0) flag_s = add_dev(sy + kOvRowsDone, 1u) == static_cast<unsigned>(rows) - 1u;
+  __syncthreads();
+  if (!flag_s) return;
+  // tau of every block (rows <= 64: one alpha per thread, all loaded at once)
+  __shared__ float al_s[kFusedFinishRows];
+  __shared__ unsigned char va_s[kFusedFinishRows];
+  const int G = a.gamma;
+  if (tid < rows) {
+    al_s[tid] = __uint_as_float(ld_dev(reinterpret_cast<const unsigned*>(a.alpha) + tid));
+    va_s[tid] = a.valid ? a.valid[tid] : 1;
+  }
+  __syncthreads();
+  const bool timed_out = ld_dev(sy + kOvTimeout) == a.epoch;     // a wait ran out: results invalid
+  const float nan = __builtin_nanf("");
+  float tau_n = 0.f;
+  bool has = false;
+  if (tid < a.N) {
+    float run = 1.f;
+    tau_n = 1.f;
+    for (int i = 0; i < G; ++i) {
+      has |= va_s[tid * G + i] != 0;
+      run *= al_s[tid * G + i];
+      tau_n += run;
+    }
+    a.tau[tid] = timed_out ? nan : (has ? tau_n : 0.f);
+  }
+  if (tid < G) {   // accept_rate@i over valid slots, blocks in order
+    double s1 = 0.0, s2 = 0.0;
+    for (int n = 0; n < a.N; ++n)
+      if (va_s[n * G + tid]) { s1 += al_s[n * G + tid]; s2 += 1.0; }
+    if (a.accept_rate_at) a.accept_rate_at[tid] = s2 > 0.0 ? s1 / s2 : 0.0;
+  }
+  if (tid == 0 && a.tau_mean) {   // mean tau over blocks with a valid slot, in order
+    double s1 = 0.0, s2 = 0.0;
+    for (int n = 0; n < a.N; ++n) {
+      float run = 1.f, tn = 1.f;
+      bool hv = false;
+      for (int i = 0; i < G; ++i) {
+        hv |= va_s[n * G + i] != 0;
+        run *= al_s[n * G + i];
+        tn += run;
+      }
+      if (hv) { s1 += tn; s2 += 1.0; }
+    }
+    *a.tau_mean = timed_out ? static_cast<double>(nan) : (s2 > 0.0 ? s1 / s2 : 0.0);
+  }
+  // clear the counters used by this call (the release flags hold call numbers)
+  if (tid < rows) {
+    sy[kOvCnt1 + 32 * tid] = 0u;
+    sy[kOvCnt2 + 32 * tid] = 0u;
+  }
+  if (tid == 0) sy[kOvRowsDone] = 0u;
 }
 
 __global__ __launch_bounds__(64) void tau_finish(OverlapArgs a) {
@@ -306,9 +537,33 @@ int overlap_split_chunks(int64_t rows, int64_t V) {
   return static_cast<int>(by_size < by_rows ? by_size : by_rows);
 }
 
+// whether every (chunk, row) workgroup of the single-launch path fits at once
+static bool fused_fits(const OverlapArgs& a, int rows) {
+  const DeviceInfo d = device_info();
+  if (d.cus <= 0 || d.clock_khz <= 0) return false;
+  if (!a.draft) return true;                     // candidate mode: nothing waits
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(overlap_fused<true>),
+                                                   kSplitThreads, 0) != hipSuccess)
+    return false;
+  return static_cast<long long>(per_cu) * d.cus >= static_cast<long long>(a.nchunk) * rows;
+}
+
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s) {
   a.nblk = overlap_tau_blocks(a.N);
   const int rows = a.N * a.gamma;
+  if (a.nchunk > 1 && rows <= kFusedFinishRows && a.nblk == 1 && a.sync) {
+    const int n4 = a.V / 4;
+    a.chunk4 = (n4 + a.nchunk - 1) / a.nchunk;
+    if (a.chunk4 <= kFusedPer * kSplitThreads && a.nchunk <= 2 * kWave && fused_fits(a, rows)) {
+      a.epoch = next_epoch();
+      a.wait_ticks = static_cast<unsigned long long>(device_info().clock_khz) * 100;   // 100 ms
+      const dim3 grid(a.nchunk, rows);
+      if (a.draft) hipLaunchKernelGGL(overlap_fused<true>, grid, dim3(kSplitThreads), 0, s, a);
+      else hipLaunchKernelGGL(overlap_fused<false>, grid, dim3(kSplitThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (a.nchunk <= 1) {
     hipLaunchKernelGGL(overlap_rows, dim3(rows), dim3(kOvThreads), 0, s, a);
   } else {

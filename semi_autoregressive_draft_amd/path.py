@@ -51,7 +51,7 @@ class DraftPath:
             self.tau = torch.empty((B,), **f32)
             self.accept_rate = torch.empty((gamma,), dtype=torch.float64, device=dev)
             self.tau_mean = torch.empty((1,), dtype=torch.float64, device=dev)
-            self.ws_overlap = torch.empty(bd.dspark_overlap_tau_workspace(B, gamma, V),
+            self.ws_overlap = torch.zeros(bd.dspark_overlap_tau_workspace(B, gamma, V),
                                           dtype=torch.uint8, device=dev)
 
     def lm_head(self, stream=None):

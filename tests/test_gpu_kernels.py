@@ -292,6 +292,41 @@ def test_overlap_identical_rows_give_tau_eight():
     assert np.allclose(alpha, 1.0, atol=2e-5) and np.allclose(tau, 8.0, atol=2e-4)
 
 
+def test_overlap_single_launch_leaves_its_workspace_ready():
+    # few rows run as one launch that counts arrivals in the workspace; one
+    # zero-filled workspace serves dense and candidate calls of several shapes
+    # (and a many-row call on the split path) in turn
+    dev = require_gpu()
+    cases = [("dense", 9, 5000, 4), ("cand", 5, 5000, 5), ("dense", 2, 151936, 6),
+             ("dense", 20, 5000, 7), ("cand", 9, 151936, 8), ("dense", 9, 5000, 9)]
+    size = max(bd.dspark_overlap_tau_workspace(N, 7, V) for _, N, V, _ in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+    for mode, N, V, seed in cases:
+        teacher, draft = synth.overlap_inputs(N, V, 1.0, seed=seed)
+        valid = synth.validity(N, seed=seed, trunc_frac=0.4, n_dummy=1 if N > 2 else 0)
+        alpha = torch.empty((N, 7), dtype=torch.float32, device=dev)
+        tau = torch.empty((N,), dtype=torch.float32, device=dev)
+        acc = torch.empty((7,), dtype=torch.float64, device=dev)
+        mean = torch.empty((1,), dtype=torch.float64, device=dev)
+        t64 = teacher.astype(np.float64)
+        if mode == "dense":
+            bd.dspark_overlap_tau(to_dev(teacher), alpha, tau, draft=to_dev(draft), valid=to_dev(valid),
+                                  accept_rate_at=acc, tau_mean=mean, ws=ws)
+            a_raw, _ = o.overlap_dense(t64, draft.astype(np.float64))
+        else:
+            teacher = teacher * 3.0
+            t64 = teacher.astype(np.float64)
+            idx = np.argsort(-t64, axis=-1)[..., :16].astype(np.int32)
+            _, prob = synth.candidates(N, V, 16, seed=seed)
+            bd.dspark_overlap_tau(to_dev(teacher.astype(np.float32)), alpha, tau, cand_idx=to_dev(idx),
+                                  cand_prob=to_dev(prob), valid=to_dev(valid), accept_rate_at=acc,
+                                  tau_mean=mean, ws=ws)
+            a_raw = o.overlap_sparse(t64, idx, prob.astype(np.float64))
+        torch.cuda.synchronize()
+        got = (alpha.cpu().numpy(), tau.cpu().numpy(), acc.cpu().numpy(), float(mean.cpu()[0]))
+        _check_tau(got, a_raw, valid)
+
+
 @pytest.mark.parametrize("k,N", [(16, 5), (64, 5), (16, 20), (16, 300)])
 def test_overlap_candidates_parity(k, N):
     V = 5000
