@@ -209,7 +209,7 @@ extern "C" dspark_status_t dspark_markov_propose(
   int nwg = 0;
   size_t lds = 0;
   const bool resident = resident_chain(bf16, a.B, a.V, a.r, &nwg, &lds);
-  a.tile_cols = resident ? 64 : markov_tile_cols(bf16);
+  a.tile_cols = resident ? 64 : markov_tile_cols(bf16, a.sample, a.B, a.r, a.V);
   a.resident = resident;
   a.nlist = nwg;
   if (topk > 0) {

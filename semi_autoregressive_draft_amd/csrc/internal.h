@@ -33,7 +33,7 @@ struct StepArgs {
   unsigned long long* best;
   unsigned* sync;          // [kSyncWords] counters, flags and group keys of the resident chain
   unsigned epoch;          // number of this call (marks a timed-out resident chain)
-  int tile_cols;           // vocabulary columns per partial (64 resident, 128 bf16, 256 f32)
+  int tile_cols;           // vocabulary columns per partial (64 resident, 128 narrow bf16, a multiple of 64 wide bf16, 256 f32)
   int resident;            // 1: the chain ran as the resident kernel
   // resident chain with top-k: each workgroup's k largest order keys of U~_j
   // (value desc, index asc), sorted, [B][gamma][nlist][topk]; 0 pads
@@ -66,7 +66,7 @@ struct StepArgs {
 
 size_t markov_partials(int64_t V);
 size_t markov_segments(int64_t V);
-int markov_tile_cols(bool bf16);
+int markov_tile_cols(bool bf16, bool sample, int B, int r, int V);
 bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg, size_t* lds);
 hipError_t launch_markov_resident(StepArgs a, unsigned* sync, int nwg, size_t lds, hipStream_t s);
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s);

@@ -15,6 +15,11 @@
 // folds them in a fixed order into x_j, U~_j[x_j] and lse_j.  The top-k
 // candidates are selected after the chain, off the sequential path.  (Small
 // batches run the whole chain in one kernel instead: markov_resident.hip.)
+#include <map>
+#include <mutex>
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
 #include "markov_dev.h"
@@ -282,103 +287,254 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Batched bf16 step kernel (B > 16).  A workgroup of 4 waves owns one tile of
-// 128 columns for 64*RGW requests.  Bm is read once per tile: in each round
-// of 128 rows, wave w loads rows [32w, 32w+32) of the round for the 128 columns
-// (the same 16-byte loads as above), transposes them in registers and writes
-// the eight B operands to LDS; after a barrier every wave applies all 32 B
-// operands of the round to its RGW groups of 16 requests (A operands gathered
-// from A[x_{j-1}]).  Rounds are double-buffered in LDS with a register
-// prefetch of the next round's rows.  The epilogue is the same as above.
-template <int RGW, bool SAMPLE>
-__global__ __launch_bounds__(256) void markov_step_batched(StepArgs a) {
-  __shared__ u32x4 bop_s[2][4][8][kWave];   // [buffer][chunk][column c][lane]: 64 KB
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Wide bf16 step kernel (B > 16, r <= 256).  A workgroup owns a contiguous
+// range of 64-column tiles for up to 8 waves x 16 requests.
+//  - Each wave keeps its requests' A[x_{j-1}] rows (the MFMA A operands, one
+//    per 32-row chunk) in registers for the whole range.
+//  - A tile's Bm (r x 64) sits in LDS in MFMA B-operand form (the 4-column
+//    byte permute of load_chunk: operand c of lane (g, n) is column 4n + c,
+//    rows 8g .. 8g+7 of a 32-row chunk), double-buffered: the waves fetch
+//    later tiles' rows into registers while the current tile is computed,
+//    and one barrier per tile separates the buffers.
+//  - U_j of the next tile is fetched a tile ahead as well.  Every load is
+//    unconditional (addresses clamped into the arrays, values masked), the
+//    loop is unrolled by two so that no loaded register is copied while in
+//    flight, and the barrier waits for LDS writes only, so the loads stay in
+//    flight across it.
+//  - Each lane keeps, per request, lane-local online states over its columns
+//    of all tiles: (max, sum-exp) with one rescale per tile, and the best
+//    score with its column (columns arrive in increasing order, so a strict
+//    comparison keeps the lowest index) and U~ there.  The 16-lane reductions
+//    (DPP) run once per request per workgroup; the argmax travels as a 64-bit
+//    order key (best_key).  One partial per (request, workgroup range).
+constexpr int kWideCols = 64;
+
+// LDS of the wide kernel: two B-operand buffers of nch chunks, then (when
+// sampling) the seeds of up to 8 x 16 requests
+__host__ __device__ constexpr size_t wide_ops_bytes(int nch) { return static_cast<size_t>(nch) * 2 * 4 * kWave * 16; }
+constexpr size_t kWideSeedBytes = 8 * 16 * 8;
+
+// 16-lane maximum of 64-bit keys
+__device__ __forceinline__ unsigned long long row16_max_u64(unsigned long long k) {
+  auto step = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const unsigned lo = static_cast<unsigned>(dpp_i<C>(static_cast<int>(static_cast<uint32_t>(k))));
+    const unsigned hi = static_cast<unsigned>(dpp_i<C>(static_cast<int>(static_cast<uint32_t>(k >> 32))));
+    const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
+    k = o > k ? o : k;
+  };
+  step(std::integral_constant<int, kDppXor1>{});
+  step(std::integral_constant<int, kDppXor2>{});
+  step(std::integral_constant<int, kDppHalfMirror>{});
+  step(std::integral_constant<int, kDppMirror>{});
+  return k;
+}
+
+// this wave's LDS writes are complete, then a plain s_barrier: unlike
+// __syncthreads it leaves outstanding global loads in flight
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int NCH, int CPW, bool SAMPLE>
+__global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
+  extern __shared__ __align__(16) unsigned char wide_lds[];
+  u32x4* const ops = reinterpret_cast<u32x4*>(wide_lds);   // [2][NCH * 4][64] B operands
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int g = lane >> 4, n = lane & 15;
-  const int tile = blockIdx.x;
-  const int vcol = tile * kMarkovTile + 8 * n;
-  const bool vok = vcol < a.V;
-  const int req0 = blockIdx.y * (64 * RGW) + w * (16 * RGW);
+  const int req0 = (blockIdx.y * nw + w) * 16;
+  const size_t V = static_cast<size_t>(a.V);
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm);
-  const size_t V = static_cast<size_t>(a.V);
+  const int tb = blockIdx.x * tpw;                                   // first tile
+  const int nt = min(tpw, (a.V + kWideCols - 1) / kWideCols - tb);
+  if (nt <= 0) return;                     // padding of the grid (whole workgroup)
+  const int last = nt - 1;
 
-  const uint16_t* arow[RGW];
-  bool bok[RGW];
+  // the lane's first column in tile t; loads use it clamped to V - 4 (V % 8 == 0)
+  auto col_of = [&](int t) { return (tb + t) * kWideCols + 4 * n; };
+  auto lcol = [&](int t) { return static_cast<size_t>(min(col_of(t), a.V - 4)); };
+  // U_j rows of the lane's requests 4g + ii (clamped to a valid request)
+  const float* urow[4];
 #pragma unroll
-  for (int rg = 0; rg < RGW; ++rg) {
-    const int b = req0 + 16 * rg + n;
-    bok[rg] = b < a.B;
-    const int prev = bok[rg] ? prev_token(a, b, a.j) : 0;
-    arow[rg] = A + static_cast<size_t>(prev) * a.r;
+  for (int ii = 0; ii < 4; ++ii) {
+    const int b = min(req0 + 4 * g + ii, a.B - 1);
+    urow[ii] = a.U + (static_cast<size_t>(b) * a.gamma + a.j) * V;
   }
-  f32x4 acc[RGW][8];
+  auto load_u = [&](int t, f32x4 (&u)[4]) {
+    const size_t c = lcol(t);
 #pragma unroll
-  for (int rg = 0; rg < RGW; ++rg)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[rg][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // rows of round `rd` that this wave loads: k = 128 rd + 32 w + 8 g + i
-  const uint16_t* bcol = Bm + vcol;
-  const int nrounds = (a.r + 127) / 128;
-  auto load_round = [&](int rd, u32x4* rows) {
-    const int kc = 128 * rd + 32 * w;
-    const bool on = vok && kc < a.r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rows[i] = on ? *reinterpret_cast<const u32x4*>(bcol + static_cast<size_t>(kc + 8 * g + i) * V)
-                   : u32x4{0u, 0u, 0u, 0u};
+    for (int ii = 0; ii < 4; ++ii) u[ii] = *reinterpret_cast<const f32x4*>(urow[ii] + c);
   };
-  auto store_round = [&](int buf, const u32x4* rows) {
+  // Bm rows of this wave's chunks of tile t (chunks w, w + nw, ...; NCH <= CPW * nw)
+  auto load_bm = [&](int t, u32x2 (&raw)[CPW][8]) {
+    const size_t c = lcol(t);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 op;
+    for (int s = 0; s < CPW; ++s) {
+      const int q = min(w + s * nw, NCH - 1);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) op[p] = __builtin_amdgcn_perm(rows[2 * p + 1][c >> 1], rows[2 * p][c >> 1], sel);
-      bop_s[buf][w][c][lane] = op;
+      for (int i = 0; i < 8; ++i)
+        raw[s][i] = *reinterpret_cast<const u32x2*>(Bm + static_cast<size_t>(32 * q + 8 * g + i) * V + c);
     }
   };
-  // A operands of chunk q (32 rows of r) for this wave's request groups;
-  // fetched one chunk ahead of their use
-  const int nchunks = a.r / 32;
-  auto load_a = [&](int q, u32x4* av) {
+  auto store_bm = [&](int buf, const u32x2 (&raw)[CPW][8]) {
+    u32x4* const o = ops + buf * NCH * 4 * kWave;
 #pragma unroll
-    for (int rg = 0; rg < RGW; ++rg)
-      av[rg] = (bok[rg] && q < nchunks) ? *reinterpret_cast<const u32x4*>(arow[rg] + 32 * q + 8 * g)
-                                        : u32x4{0u, 0u, 0u, 0u};
-  };
-  u32x4 rows[8];
-  u32x4 av_next[RGW];
-  load_round(0, rows);
-  load_a(0, av_next);
-  f32x4 up[RGW][4][2];
-  prefetch_u<RGW>(a, req0, vcol, vok, g, up);
-  store_round(0, rows);
-  __syncthreads();
-  for (int rd = 0; rd < nrounds; ++rd) {
-    const int buf = rd & 1;
-    if (rd + 1 < nrounds) load_round(rd + 1, rows);
+    for (int s = 0; s < CPW; ++s) {
+      const int q = w + s * nw;
+      if (q < NCH) {
+        u32x4 op[4];
+        transpose_rows4(raw[s], op);
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const int q = 4 * rd + ch;
-      if (q >= nchunks) break;                         // uniform: r % 32 == 0
-      u32x4 av[RGW];
-#pragma unroll
-      for (int rg = 0; rg < RGW; ++rg) av[rg] = av_next[rg];
-      load_a(q + 1, av_next);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const u32x4 bo = bop_s[buf][ch][c][lane];
-#pragma unroll
-        for (int rg = 0; rg < RGW; ++rg)
-          acc[rg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[rg]), as_bf16x8(bo), acc[rg][c], 0, 0, 0);
+        for (int c = 0; c < 4; ++c) o[(q * 4 + c) * kWave + lane] = op[c];
       }
     }
-    if (rd + 1 < nrounds) store_round(buf ^ 1, rows);
-    __syncthreads();
+  };
+
+  // A operands: lane (g, n) holds request req0 + n, rows 32q + 8g .. of chunk q
+  u32x4 av[NCH];
+  {
+    const int b = min(req0 + n, a.B - 1);
+    const uint16_t* arow = A + static_cast<size_t>(prev_token(a, b, a.j)) * a.r + 8 * g;
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) av[q] = *reinterpret_cast<const u32x4*>(arow + 32 * q);
   }
-  epilogue_store<RGW, SAMPLE>(a, acc, up, req0, tile, vcol, vok, g, n);
+
+  // sampling seeds of the workgroup's requests, staged in LDS before the first
+  // barrier (a global load inside the tile loop would wait for every
+  // look-ahead load issued before it)
+  uint64_t* const seeds_s = reinterpret_cast<uint64_t*>(wide_lds + wide_ops_bytes(NCH));
+  if constexpr (SAMPLE) {
+    if (lane < 16) seeds_s[w * 16 + lane] = a.seeds[min(req0 + lane, a.B - 1)];
+  }
+
+  // lane-local states per request 4g + ii
+  float ml[4], sl[4], bs[4], bx[4];
+  int bc[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) { ml[ii] = kNegInf; sl[ii] = 0.f; bs[ii] = kNegInf; bx[ii] = 0.f; bc[ii] = 0x7fffffff; }
+
+  auto tile = [&](int t, int buf, const f32x4 (&u)[4]) {
+    const u32x4* const o = ops + buf * NCH * 4 * kWave;
+    f32x4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < NCH; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[q]), as_bf16x8(o[(q * 4 + c) * kWave + lane]),
+                                                         acc[c], 0, 0, 0);
+    const int col = col_of(t);
+    const bool cok = col < a.V;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int b = req0 + 4 * g + ii;
+      const bool live = b < a.B && cok;
+      const size_t row = static_cast<size_t>(b) * a.gamma + a.j;
+      float x[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = live ? acc[c][ii] + u[ii][c] : kNegInf;
+      if (live && a.logits_out) *reinterpret_cast<f32x4*>(a.logits_out + row * V + col) = f32x4{x[0], x[1], x[2], x[3]};
+      const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (a.segmax) {
+        const float m8 = fmaxf(m4, dpp_f<kDppXor1>(m4));   // lanes 2s, 2s+1: one 8-column segment
+        if (live && (n & 1) == 0) a.segmax[row * a.S + col / kSeg] = m8;
+      }
+      if (live) {
+        const float mn = fmaxf(ml[ii], m4);
+        sl[ii] = sl[ii] * __expf(ml[ii] - mn) +
+                 ((__expf(x[0] - mn) + __expf(x[1] - mn)) + (__expf(x[2] - mn) + __expf(x[3] - mn)));
+        ml[ii] = mn;
+        float score[4];
+        if constexpr (SAMPLE) {
+          const uint64_t sd = seeds_s[w * 16 + 4 * g + ii];
+          const Philox4 r = philox4x32_10(col >> 2, a.j, a.off_lo, a.off_hi, static_cast<uint32_t>(sd),
+                                          static_cast<uint32_t>(sd >> 32));
+          const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) score[c] = x[c] * a.inv_temp + gumbel_from_word(wd[c]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) score[c] = x[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (score[c] > bs[ii]) { bs[ii] = score[c]; bc[ii] = col + c; bx[ii] = x[c]; }
+      }
+    }
+  };
+
+  // tile t computes from buffer t & 1 and U registers u0 (t even) or u1 (t
+  // odd); look-aheads past the range reload the last tile (an L2 hit).  With
+  // one chunk per wave the Bm rows have two register sets (ra for even
+  // tiles, rb for odd ones) and are fetched two tiles ahead; with two chunks
+  // one set, a tile ahead.
+  f32x4 u0[4], u1[4];
+  u32x2 ra[CPW][8];
+  int t = 0;
+  if constexpr (CPW == 1) {
+    u32x2 rb[CPW][8];
+    load_bm(0, ra);
+    load_u(0, u0);
+    load_bm(min(1, last), rb);
+    load_u(min(1, last), u1);
+    store_bm(0, ra);
+    load_bm(min(2, last), ra);
+    lds_barrier();
+    do {
+      tile(t, 0, u0);
+      store_bm(1, rb);                                  // tile t + 1
+      load_bm(min(t + 3, last), rb);
+      load_u(min(t + 2, last), u0);
+      lds_barrier();
+      if (t + 1 < nt) tile(t + 1, 1, u1);
+      store_bm(0, ra);                                  // tile t + 2
+      load_bm(min(t + 4, last), ra);
+      load_u(min(t + 3, last), u1);
+      lds_barrier();
+      t += 2;
+    } while (t < nt);
+  } else {
+    load_bm(0, ra);
+    load_u(0, u0);
+    store_bm(0, ra);
+    load_bm(min(1, last), ra);
+    load_u(min(1, last), u1);
+    lds_barrier();
+    do {
+      tile(t, 0, u0);
+      store_bm(1, ra);                                  // tile t + 1
+      load_bm(min(t + 2, last), ra);
+      load_u(min(t + 2, last), u0);
+      lds_barrier();
+      if (t + 1 < nt) tile(t + 1, 1, u1);
+      store_bm(0, ra);                                  // tile t + 2
+      load_bm(min(t + 3, last), ra);
+      load_u(min(t + 3, last), u1);
+      lds_barrier();
+      t += 2;
+    } while (t < nt);
+  }
+
+  // one partial per request: 16-lane reductions of the lane states
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int b = req0 + 4 * g + ii;
+    const float M = row16_max(ml[ii]);
+    const float ssum = row16_sum(ml[ii] == kNegInf ? 0.f : sl[ii] * __expf(ml[ii] - M));
+    const unsigned long long key = row16_max_u64(bs[ii] == kNegInf ? 0ull : best_key(bs[ii], bc[ii]));
+    const float xw = row16_max((bs[ii] != kNegInf && best_key(bs[ii], bc[ii]) == key) ? bx[ii] : kNegInf);
+    if (n == 0 && b < a.B) {
+      const size_t pq = (static_cast<size_t>(b) * a.gamma + a.j) * a.P + blockIdx.x;
+      a.p_m[pq] = M;
+      a.p_s[pq] = ssum;
+      a.p_score[pq] = best_value(key);
+      a.p_idx[pq] = best_index(key);
+      a.p_x[pq] = xw;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -831,33 +987,97 @@ static void launch_bf16(const StepArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL((markov_step_bf16<RG, KS, false>), grid, dim3(kWave * KS), 0, s, a);
 }
 
-template <int RGW>
-static void launch_batched(const StepArgs& a, hipStream_t s) {
-  const dim3 grid((a.V + kMarkovTile - 1) / kMarkovTile, (a.B + 64 * RGW - 1) / (64 * RGW));
-  if (a.sample) hipLaunchKernelGGL((markov_step_batched<RGW, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((markov_step_batched<RGW, false>), grid, dim3(256), 0, s, a);
+// wide kernel plan: one request group of 16 per wave (up to 8 waves), each
+// wave loading at most 2 of a tile's 32-row Bm chunks, and as many
+// workgroups as the device holds at once, each over a contiguous tile range.
+// The grid's x extent is padded to a multiple of 8 (the padding returns at
+// once): workgroups are dealt to the 8 XCDs by linear index, so the ny
+// workgroups of one tile range then share an XCD and its L2.
+struct WidePlan {
+  const void* fn;
+  void (*launch)(const StepArgs&, int, dim3, int, hipStream_t);
+  int nw, ny, tpw, nx, gx;
+  size_t lds;
+};
+
+template <int NCH, int CPW, bool SAMPLE>
+static void launch_wide_kernel(const StepArgs& a, int tpw, dim3 grid, int nw, hipStream_t s) {
+  hipLaunchKernelGGL((markov_step_wide<NCH, CPW, SAMPLE>), grid, dim3(kWave * nw),
+                     wide_ops_bytes(NCH) + (SAMPLE ? kWideSeedBytes : 0), s, a, tpw);
+}
+
+template <int NCH, int CPW>
+static void pick_wide(bool sample, WidePlan* p) {
+  p->fn = sample ? reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, true>)
+                 : reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, false>);
+  p->launch = sample ? &launch_wide_kernel<NCH, CPW, true> : &launch_wide_kernel<NCH, CPW, false>;
+  p->lds = wide_ops_bytes(NCH) + (sample ? kWideSeedBytes : 0);
+}
+
+// workgroups of fn (with nw waves) resident per compute unit, cached
+static int wide_occupancy(const void* fn, int nw, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(fn, nw);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kWave * nw, lds) != hipSuccess || nb < 1) nb = 1;
+  cache[key] = nb;
+  return nb;
+}
+
+// false: the shape takes the narrow kernel (B <= 16, or a rank other than
+// 32, 64, 128 or 256)
+static bool wide_plan(bool bf16, bool sample, int B, int r, int V, WidePlan* p) {
+  const int nch = r / 32;
+  if (!bf16 || B <= 16 || r % 32 || (nch != 1 && nch != 2 && nch != 4 && nch != 8)) return false;
+  const int groups = (B + 15) / 16;
+  // at least nch / 2 waves, so that a wave loads at most 2 chunks (waves
+  // past the last request only load and store operands)
+  p->nw = min(8, max(groups, nch / 2));
+  p->ny = (groups + p->nw - 1) / p->nw;
+  const bool two = nch > p->nw;                        // chunks per wave: 1 or 2
+  switch (nch * 2 + (two ? 1 : 0)) {
+    case 2: pick_wide<1, 1>(sample, p); break;
+    case 4: pick_wide<2, 1>(sample, p); break;
+    case 8: pick_wide<4, 1>(sample, p); break;
+    case 9: pick_wide<4, 2>(sample, p); break;
+    case 16: pick_wide<8, 1>(sample, p); break;
+    default: pick_wide<8, 2>(sample, p); break;
+  }
+  const int ntiles = (V + kWideCols - 1) / kWideCols;
+  const int slots = max(1, wide_occupancy(p->fn, p->nw, p->lds) * max(1, device_info().cus));
+  const int nx = max(1, slots / p->ny);
+  p->tpw = (ntiles + nx - 1) / nx;
+  p->nx = (ntiles + p->tpw - 1) / p->tpw;
+  p->gx = (p->nx + 7) / 8 * 8;
+  return true;
 }
 
 static int partial_count(const StepArgs& a) { return (a.V + a.tile_cols - 1) / a.tile_cols; }
 
-int markov_tile_cols(bool bf16) { return bf16 ? kMarkovTile : kMarkovTileF32; }
+int markov_tile_cols(bool bf16, bool sample, int B, int r, int V) {
+  if (!bf16) return kMarkovTileF32;
+  WidePlan p{};
+  return wide_plan(bf16, sample, B, r, V, &p) ? p.tpw * kWideCols : kMarkovTile;
+}
 
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
   a.Pn = partial_count(a);
   if (bf16) {
-    // request blocking and r-split: small batches split r over 4 waves so a
-    // step has enough waves in flight; large batches reuse each transposed Bm
-    // block for 4 request groups.
-    if (a.B <= 16) {
-      if (a.r % 128 == 0) launch_bf16<1, 4>(a, s);
-      else if (a.r % 64 == 0) launch_bf16<1, 2>(a, s);
-      else launch_bf16<1, 1>(a, s);
-    } else if (a.B <= 64) {
-      launch_batched<1>(a, s);
-    } else if (a.B <= 128) {
-      launch_batched<2>(a, s);
+    WidePlan p{};
+    if (wide_plan(bf16, a.sample, a.B, a.r, a.V, &p)) {
+      if (p.tpw * kWideCols != a.tile_cols) return hipErrorInvalidValue;   // plan changed since tile_cols was set
+      p.launch(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
+    } else if (a.r % 128 == 0) {
+      // small batches split r over waves so that a step has enough waves in flight
+      launch_bf16<1, 4>(a, s);
+    } else if (a.r % 64 == 0) {
+      launch_bf16<1, 2>(a, s);
     } else {
-      launch_batched<4>(a, s);
+      launch_bf16<1, 1>(a, s);
     }
   } else {
     const dim3 grid(a.Pn, a.B);

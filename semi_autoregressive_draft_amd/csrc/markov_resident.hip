@@ -55,8 +55,6 @@
 
 namespace dspark {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / kWave;
 constexpr int kResCols = 64;                  // vocabulary columns per group
@@ -72,29 +70,6 @@ struct ResidentArgs {
   unsigned* sync;      // wait tree, kSyncWords words (zero at launch)
   unsigned long long wait_ticks;   // bound of one grid-wide wait, wall-clock ticks
 };
-
-// Four B operands (columns c = 0..3) from eight rows of four bf16 columns:
-// operand c, dword p = (row 2p+1, column c) << 16 | (row 2p, column c).
-__device__ __forceinline__ void transpose_rows4(const u32x2 (&rows)[8], u32x4 (&op)[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) op[c][p] = __builtin_amdgcn_perm(rows[2 * p + 1][c >> 1], rows[2 * p][c >> 1], sel);
-  }
-}
-
-// Operands of chunk q of group column base `col` (= 64G + 4n), zero past V.
-template <int KCH>
-__device__ __forceinline__ void load_chunk(const uint16_t* Bm, size_t V, int col, bool cok, int q, int g,
-                                           u32x4 (&op)[4]) {
-  u32x2 rows[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    rows[i] = cok ? *reinterpret_cast<const u32x2*>(Bm + static_cast<size_t>(32 * q + 8 * g + i) * V + col)
-                  : u32x2{0u, 0u};
-  transpose_rows4(rows, op);
-}
 
 // Wait-tree layout in the sync block (32-bit words; counters and flags each on
 // their own 256-byte line): time-out flag, group counters, top counter, group

@@ -83,9 +83,14 @@ def chain_path(request, monkeypatch):
     (1, 5000, 256, "bf16", 0.0, 0),     # one request (per position: r split over 4 waves)
     (3, 5000, 64, "bf16", 0.0, 0),      # r split over 2 waves
     (5, 4096, 32, "bf16", 0.7, 0),      # sampled, no r split
-    (17, 5000, 128, "bf16", 0.0, 0),    # 2 request groups per wave, ragged request block
-    (40, 3000, 256, "bf16", 1.0, 0),    # 4 request groups per wave, sampled
-    (70, 2000, 64, "bf16", 0.0, 16),    # two request blocks, top-16
+    (17, 5000, 128, "bf16", 0.0, 0),    # 64-column tiles, 2 request groups, ragged
+    (40, 3000, 256, "bf16", 1.0, 0),    # 3 request groups, sampled
+    (70, 2000, 64, "bf16", 0.0, 16),    # 5 request groups, top-16
+    (150, 3000, 128, "bf16", 0.0, 16),  # two groups of 16 per wave, ragged request block
+    (300, 2000, 64, "bf16", 1.0, 0),    # two request blocks, sampled
+    (64, 3000, 256, "bf16", 1.0, 0),    # 4 waves of one group, 2 Bm chunks per wave, sampled
+    (129, 2008, 256, "bf16", 0.0, 16),  # 8 waves x 2 request blocks, ragged requests and last tile
+    (20, 1000, 32, "bf16", 0.0, 0),     # one chunk, 2 waves
     (2, 5000, 256, "bf16", 0.0, 32),    # top-32
     (1, 1000, 64, "bf16", 1.0, 16),     # sampled with top-16
     (1, 4096, 32, "f32", 0.0, 0),       # tiny reference config
