@@ -19,6 +19,10 @@ Sources (the pages), cited by title and section:
        first previous token, predict_confidence_step).
   Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
        Easy as 1, 2, 3", SC'11 (the pages name no sampler).
+  [P4] §3.2 (hardware-aware prefix scheduler: B(l), tau(l), Theta = tau *
+       SPS(B), the greedy scan over candidates sorted by survival) and §7.2
+       (SPS(B) as an offline-measured monotone lookup table; the sort is
+       O(R gamma log(R gamma))).
 
 Readings where the pages are silent or disagree (each is listed in the design
 notes as well):
@@ -31,11 +35,13 @@ notes as well):
   * the confidence head is w_c.h + b_c, plus w_m.A[prev] when w_m is given
     ([P1] s_i = w_c^T [h_i; m_i] + b_c); no calibration is applied;
   * alpha is clamped to [0, 1] and set to 0 at invalid slots; a block with no
-    valid slot reports tau = 0 and is left out of the mean ([P1] 离线指标).
+    valid slot reports tau = 0 and is left out of the mean ([P1] 离线指标);
+  * the prefix scheduler: see ``prefix_schedule`` for its four readings.
 """
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 from typing import Optional
 
 import numpy as np
@@ -267,3 +273,63 @@ def tau_metrics(alpha: np.ndarray, valid: Optional[np.ndarray] = None):
     acc = np.where(cnt > 0, (a * v).sum(axis=0) / np.maximum(cnt, 1), 0.0)
     tau_mean = float(tau[has].mean()) if has.any() else 0.0
     return a, tau, acc, tau_mean
+
+
+# --------------------------------------------------------------------------
+# K5: hardware-aware prefix scheduler.  [P4] §3.2: a request r that sends its
+# first l_r draft tokens to verification costs 1 + l_r batch slots, so the
+# verification batch is B(l) = sum_r (1 + l_r); it is expected to emit
+# 1 + sum_{j<=l_r} a_{r,j} tokens, so tau(l) = sum_r (1 + sum_{j<=l_r} a_{r,j});
+# the objective is Theta(l) = tau(l) * SPS(B(l)).  Every extra candidate adds
+# one slot to B whatever it is, so for each B the best choice is the B - R
+# largest survival values, and since a_{r,j} falls with j, taking candidates in
+# descending order of a keeps every request's choice a prefix.  The algorithm:
+# start from l = 0, B = R, tau = R, Theta_max = R * SPS(R); visit all (r, j)
+# in descending order of a, each time B += 1, tau += a_{r,j}, Theta = tau *
+# SPS(B); return the lengths at the cut where Theta was largest.
+
+
+def prefix_schedule(survival: np.ndarray, sps: np.ndarray):
+    """survival a [R, gamma] (column j holds the pages' position j + 1),
+    sps [n] with sps[B - 1] = SPS(B) for B = 1..n (n >= R)
+    -> (lengths [R] int64, theta, tau, batch).
+
+    Readings where [P4] §3.2 leaves a step open:
+      * a is a probability: values are clamped to [0, 1], NaN read as 0;
+      * equal survival values are taken in order of the flat index r*gamma + j
+        (within a request the earlier position first, so lengths stay prefixes);
+      * tau is the exact sum, rounded once to float64, and Theta one float64
+        product tau * SPS(B); the first cut (smallest B) attaining the largest
+        Theta is returned;
+      * the table ends at the largest batch the engine accepts: cuts with
+        B > n are not considered.
+    """
+    a = np.asarray(survival, dtype=np.float32)
+    sps = np.asarray(sps, dtype=np.float64)
+    R, gamma = a.shape
+    n = sps.shape[0]
+    if n < R:
+        raise ValueError("the SPS table must cover B = R")
+    cands = []
+    for r in range(R):
+        for j in range(gamma):
+            v = float(a[r, j])
+            v = min(v, 1.0) if v > 0.0 else 0.0          # NaN > 0 is false
+            cands.append((v, r * gamma + j))
+    cands.sort(key=lambda c: (-c[0], c[1]))
+    B = R
+    tau = Fraction(R)
+    theta_max, k_best, tau_best = float(R) * float(sps[R - 1]), 0, float(R)
+    for k, (v, _) in enumerate(cands, start=1):
+        if B + 1 > n:
+            break
+        B += 1
+        tau += Fraction(v)
+        t = float(tau)                                   # correctly rounded
+        theta = t * float(sps[B - 1])
+        if theta > theta_max:
+            theta_max, k_best, tau_best = theta, k, t
+    lengths = np.zeros(R, dtype=np.int64)
+    for _, m in cands[:k_best]:
+        lengths[m // gamma] += 1
+    return lengths, theta_max, tau_best, R + k_best

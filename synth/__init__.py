@@ -21,7 +21,7 @@ import numpy as np
 
 # tensor ids of the per-tensor generators
 TID_H, TID_WLM, TID_A, TID_BM, TID_ANCHOR, TID_TEACHER, TID_WC, TID_VALID, \
-    TID_DRAFT, TID_U, TID_WM, TID_CAND = range(12)
+    TID_DRAFT, TID_U, TID_WM, TID_CAND, TID_SURV = range(13)
 
 GAMMA = 7
 QWEN_H = 2560
@@ -170,3 +170,21 @@ CONFIGS = {
     "c5_flash_next_b256": dict(B=256, H=QWEN_H, V=QWEN_V, r=QWEN_R, wdtype="bf16",
                                temperature=0.0, topk=16),
 }
+
+
+def survival_rows(R: int, gamma: int = GAMMA, *, seed: int = 0) -> np.ndarray:
+    """[R, gamma] float32 prefix-survival stand-ins: uniform draws in [0, 1)
+    sorted in descending order along each row (the scheduler's inputs are
+    non-increasing along the block)."""
+    u = rng(seed, TID_SURV).random((R, gamma), dtype=np.float32)
+    return -np.sort(-u, axis=1)
+
+
+def sps_table(n: int, *, knee: int = 64, base_ms: float = 10.0, per_token_ms: float = 0.05) -> np.ndarray:
+    """Synthetic steps-per-second table [n] float64, entry B - 1 for a
+    verification batch of B tokens: flat while the target model's step is
+    memory-bound (B <= knee), then falling as the step time grows linearly
+    with B.  A roofline-shaped stand-in for a table measured offline on the
+    serving GPU ("DSpark 论文精读", §7.2 checklist item 3)."""
+    B = np.arange(1, n + 1, dtype=np.float64)
+    return 1000.0 / (base_ms + per_token_ms * np.maximum(0.0, B - knee))
