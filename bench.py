@@ -124,6 +124,40 @@ def cpu_baseline(inp, overlap, budget_s=10.0, max_reps=100000):
                       f"full path in float64, {el:.1f} s"}
 
 
+def bench_prefix_schedule(dev, stream, R=256, gamma=7, calls=200, with_oracle=True):
+    """The hardware-aware prefix scheduler at a serving batch of R requests
+    (not part of the step): mean time per call over back-to-back launches
+    between two events, and the oracle's time for one call beside it."""
+    import numpy as np
+    import torch
+    import synth
+    from semi_autoregressive_draft_amd import binding as bd
+    a = synth.survival_rows(R, gamma, seed=0)
+    sps = synth.sps_table(R * (gamma + 1), knee=R + R * gamma // 3, per_token_ms=20.0 / R)
+    d_a = torch.from_numpy(a).to(dev)
+    d_sps = torch.from_numpy(sps).to(dev)
+    lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+    stats = torch.empty((3,), dtype=torch.float64, device=dev)
+    for _ in range(5):
+        bd.dspark_prefix_schedule(d_a, d_sps, lengths, stats)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        bd.dspark_prefix_schedule(d_a, d_sps, lengths, stats)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out = {"R": R, "gamma": gamma, "candidates": R * gamma, "us_per_call": round(e0.elapsed_time(e1) * 1e3 / calls, 2),
+           "bound": "latency (one workgroup: sort, exact scan, argmax)",
+           "batch_chosen": int(stats[2].item()), "calls": calls}
+    if with_oracle:
+        from oracle import dspark_oracle as o
+        t = time.perf_counter()
+        o.prefix_schedule(a, sps)
+        out["oracle_ms_per_call"] = round((time.perf_counter() - t) * 1e3, 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +277,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, overlap)
+    sched = bench_prefix_schedule(dev, stream, with_oracle=not args.no_cpu_baseline)
 
     out = {
         "metric": METRIC, "value": round(blocks_per_s, 2), "unit": "blocks/s", "n_gpus": 1,
@@ -259,6 +294,7 @@ def main():
         "stages_note": "lm_head from the timed region; the others from a separate pass with an event around every stage",
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
+        "next_rows": {"prefix_schedule": sched},
     }
     print(json.dumps(out), flush=True)
 

@@ -223,6 +223,35 @@ dspark_status_t dspark_overlap_tau(const float* teacher, const float* draft,
                                    double* tau_mean, void* ws, size_t ws_bytes,
                                    hipStream_t stream);
 
+/*
+ * K5 -- hardware-aware prefix scheduler.  [P4] §3.2: request r verifying its
+ * first l_r draft tokens costs 1 + l_r slots of the verification batch
+ * B = sum_r (1 + l_r) and is expected to emit 1 + sum_{j<=l_r} a_{r,j}
+ * tokens; the lengths maximise Theta = tau * SPS(B), found by one scan over
+ * all (r, j) in descending order of a_{r,j}.  [P4] §7.2: SPS(B) is a table
+ * measured offline.
+ *
+ *   survival  [R, gamma] float32       a_{r,j}; column j is position j + 1 of
+ *                                      the block (the layout
+ *                                      dspark_confidence_survival writes);
+ *                                      non-increasing along each row for the
+ *                                      lengths to be the optimum
+ *   sps       [n_sps] float64          sps[B - 1] = verification steps per
+ *                                      second at a batch of B tokens,
+ *                                      B = 1..n_sps; finite and >= 0
+ *   lengths   [R] int32 (out)          l_r in 0..gamma
+ *   stats     [3] float64 (out)        {Theta*, tau*, B*} at the chosen cut
+ * Semantics: values are clamped to [0, 1] (NaN read as 0); equal values are
+ * taken in order of the flat index r * gamma + j; tau is the exact sum
+ * rounded once to float64 and Theta one float64 product, so results are
+ * bit-identical to any exact evaluation of the same definition; the first
+ * (smallest-B) maximum wins; batches beyond n_sps are not admissible.
+ * Requirements: R, gamma > 0; n_sps >= R; gamma <= 16; R * gamma <= 16384.
+ */
+dspark_status_t dspark_prefix_schedule(const float* survival, int64_t R, int64_t gamma,
+                                       const double* sps, int64_t n_sps, int32_t* lengths,
+                                       double* stats, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

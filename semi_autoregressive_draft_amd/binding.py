@@ -35,6 +35,7 @@ _SIGNATURES = {
     "dspark_overlap_tau_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
     "dspark_overlap_tau": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp,
                                      _vp, _vp, _vp, _sz, _vp]),
+    "dspark_prefix_schedule": (C.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
 }
 
 
@@ -173,3 +174,11 @@ def dspark_overlap_tau(teacher, alpha, tau, *, draft=None, cand_idx=None, cand_p
         _ptr(teacher), _ptr(draft), _ptr(cand_idx), _ptr(cand_prob), k, _ptr(valid), N, gamma, V,
         _ptr(alpha), _ptr(tau), _ptr(accept_rate_at), _ptr(tau_mean), _ptr(ws), ws.numel(),
         _stream(stream)))
+
+
+def dspark_prefix_schedule(survival, sps, lengths, stats, stream=None) -> None:
+    """lengths [R] int32 and stats [3] float64 {Theta, tau, B} from survival
+    [R, gamma] float32 and the SPS table sps [n] float64."""
+    R, gamma = survival.shape
+    _check(lib().dspark_prefix_schedule(_ptr(survival), R, gamma, _ptr(sps), sps.shape[0],
+                                        _ptr(lengths), _ptr(stats), _stream(stream)))

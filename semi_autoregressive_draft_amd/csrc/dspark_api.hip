@@ -1,5 +1,6 @@
 // C ABI of the DSpark draft-proposal hot path: argument checks, workspace
 // carving and kernel dispatch.  Every check runs before anything is enqueued.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -315,4 +316,23 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
     a.ws_fused = reinterpret_cast<unsigned long long*>(p);
   }
   return hip_status(launch_overlap_tau(a, stream), fn);
+}
+
+// ---------------------------------------------------------------------------
+extern "C" dspark_status_t dspark_prefix_schedule(const float* survival, int64_t R, int64_t gamma,
+                                                  const double* sps, int64_t n_sps, int32_t* lengths,
+                                                  double* stats, hipStream_t stream) {
+  const char* fn = "dspark_prefix_schedule";
+  if (!survival || !sps || !lengths || !stats)
+    return fail(DSPARK_EINVAL, "%s: survival, sps, lengths and stats must be non-NULL", fn);
+  if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "%s: R and gamma must be positive", fn);
+  if (n_sps < R) return fail(DSPARK_EINVAL, "%s: the SPS table (%lld entries) must reach B = R = %lld", fn,
+                             static_cast<long long>(n_sps), static_cast<long long>(R));
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
+  if (R > kSchedMaxCand || R * gamma > kSchedMaxCand)
+    return fail(DSPARK_EUNSUPPORTED, "%s: R * gamma > %d", fn, kSchedMaxCand);
+  const int64_t kmax = std::min<int64_t>(R * gamma, n_sps - R);
+  return hip_status(launch_prefix_schedule(survival, static_cast<int>(R), static_cast<int>(gamma), sps,
+                                           static_cast<int>(kmax), lengths, stats, stream),
+                    fn);
 }

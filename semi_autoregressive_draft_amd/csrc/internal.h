@@ -78,6 +78,9 @@ bool lm_head_skinny_fits(int64_t M, int64_t H);
 hipError_t launch_lm_head_skinny(const uint16_t* h, const uint16_t* w, int64_t M, int64_t H, int64_t V,
                                  float* U, hipStream_t s);
 
+constexpr int kSchedMaxCand = 16384;   // R * gamma of the prefix scheduler (keys in LDS)
+hipError_t launch_prefix_schedule(const float* survival, int R, int gamma, const double* sps, int kmax,
+                                  int32_t* lengths, double* stats, hipStream_t s);
 hipError_t launch_confidence(const void* h, bool bf16, int B, int gamma, int H,
                              const void* w_c, float b_c, const void* w_m, const void* A, int r,
                              const int32_t* anchor, const int32_t* tokens, float* conf,

@@ -135,3 +135,18 @@ def test_overlap_validation(L):
     assert f(*args(draft=MISALIGNED)) == bd.EUNSUPPORTED
     assert f(*args()) == bd.EWORKSPACE
     assert f(*args(draft=None, idx=FAKE, prob=FAKE, k=16)) == bd.EWORKSPACE
+
+
+def test_prefix_schedule_validation(L):
+    f = L.dspark_prefix_schedule
+    args = lambda **k: [k.get(n, d) for n, d in (
+        ("surv", FAKE), ("R", 256), ("gamma", 7), ("sps", FAKE), ("n", 2048), ("len", FAKE),
+        ("stats", FAKE), ("s", None))]
+    assert f(*args(surv=None)) == bd.EINVAL
+    assert f(*args(stats=None)) == bd.EINVAL
+    assert f(*args(R=0)) == bd.EINVAL
+    assert f(*args(gamma=0)) == bd.EINVAL
+    assert f(*args(n=255)) == bd.EINVAL                      # the table must reach B = R
+    assert f(*args(gamma=17)) == bd.EUNSUPPORTED
+    assert f(*args(R=2341, n=20000)) == bd.EUNSUPPORTED      # R * gamma > 16384
+    assert "16384" in bd.last_error()

@@ -346,3 +346,89 @@ def test_overlap_candidates_parity(k, N):
     a_raw = o.overlap_sparse(t64, idx, prob.astype(np.float64))
     assert a_raw.max() > 0.05
     _check_tau(got, a_raw, None)
+
+
+# ----------------------------------------------------------------------------- K5
+def _schedule(a, sps):
+    dev = require_gpu()
+    R = a.shape[0]
+    lengths = torch.full((R,), -7, dtype=torch.int32, device=dev)
+    stats = torch.full((3,), -1.0, dtype=torch.float64, device=dev)
+    bd.dspark_prefix_schedule(to_dev(a), to_dev(np.ascontiguousarray(sps, dtype=np.float64)), lengths, stats)
+    torch.cuda.synchronize()
+    return lengths.cpu().numpy(), stats.cpu().numpy()
+
+
+def _check_schedule(a, sps):
+    lengths, stats = _schedule(a, sps)
+    want_l, theta, tau, batch = o.prefix_schedule(a, sps)
+    assert np.array_equal(lengths, want_l), (lengths[:16], want_l[:16])
+    assert stats[0] == theta and stats[1] == tau and stats[2] == batch, (stats, theta, tau, batch)
+    return want_l, batch
+
+
+@pytest.mark.parametrize("R,gamma,seed", [
+    (1, 1, 0),          # one candidate
+    (3, 7, 1),
+    (146, 7, 2),        # 1022 candidates: one per thread
+    (147, 7, 3),        # 1029: two sorted positions per thread, padding
+    (256, 7, 4),        # a serving batch of 256 requests
+    (100, 16, 5),       # longest block
+    (2048, 8, 6),       # 16384 candidates: the largest sort
+    (2340, 7, 7),       # 16380: ragged against the padding
+])
+def test_prefix_schedule_parity(R, gamma, seed):
+    a = synth.survival_rows(R, gamma, seed=seed)
+    # knee and slope chosen so that the best cut falls inside the candidates
+    sps = synth.sps_table(R * (gamma + 1), knee=R + R * gamma // 3, per_token_ms=20.0 / R)
+    _check_schedule(a, sps)
+
+
+@pytest.mark.parametrize("kind", ["flat", "inverse", "step", "capped", "ties", "clamp", "no_room"])
+def test_prefix_schedule_edge_cases(kind):
+    R, gamma = 40, 7
+    a = synth.survival_rows(R, gamma, seed=11)
+    n = R * (gamma + 1)
+    B = np.arange(1, n + 1, dtype=np.float64)
+    if kind == "flat":                       # every positive candidate admitted
+        a[5, 3:] = 0.0
+        sps = np.full(n, 2.5)
+    elif kind == "inverse":                  # SPS = 1/B: no drafts pay off
+        a = np.minimum(a, np.float32(0.99))
+        sps = 1.0 / B
+    elif kind == "step":
+        sps = np.where(B <= 90, 2.0, 1.0)
+    elif kind == "capped":                   # the table ends before every candidate fits
+        sps = np.full(R + 17, 1.0)
+    elif kind == "ties":                     # equal values: flat index order
+        a = np.full((R, gamma), 0.5, dtype=np.float32)
+        a[::3, 4:] = 0.25
+        sps = np.full(R + 100, 1.0)
+    elif kind == "clamp":
+        a[0, 0], a[7, 2], a[9, 6], a[20, 1] = np.nan, -3.0, 4.0, np.inf
+        sps = synth.sps_table(n, knee=60, per_token_ms=0.3)
+    else:                                    # the table stops at B = R
+        sps = np.full(R, 3.0)
+    lengths, batch = _check_schedule(a, sps)
+    if kind == "no_room":
+        assert batch == R and not lengths.any()
+
+
+def test_prefix_schedule_on_survival_from_the_confidence_kernel():
+    # the scheduler consumes what dspark_confidence_survival writes
+    dev = require_gpu()
+    B, gamma, H = 256, 7, 2560
+    h = synth.normal((B, gamma, H), 1.0, 3, synth.TID_H, "bf16")
+    w_c = synth.normal((H,), 0.02, 3, synth.TID_WC, "bf16")
+    conf = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    surv = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    bd.dspark_confidence_survival(to_dev(h, "bf16"), to_dev(w_c, "bf16"), 0.5, conf, surv)
+    sps = synth.sps_table(B * (gamma + 1), knee=B + 300, per_token_ms=0.02)
+    lengths = torch.empty((B,), dtype=torch.int32, device=dev)
+    stats = torch.empty((3,), dtype=torch.float64, device=dev)
+    bd.dspark_prefix_schedule(surv, to_dev(sps), lengths, stats)
+    torch.cuda.synchronize()
+    a = surv.cpu().numpy()
+    want_l, theta, tau, batch = o.prefix_schedule(a, sps)
+    assert np.array_equal(lengths.cpu().numpy(), want_l)
+    assert tuple(stats.cpu().numpy()) == (theta, tau, float(batch))
