@@ -19,6 +19,10 @@ Sources (the pages), cited by title and section:
        first previous token, predict_confidence_step).
   Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
        Easy as 1, 2, 3", SC'11 (the pages name no sampler).
+  [P4] §4.1 (training loss: per-position CE and full-vocabulary L1, the
+       accept-rate soft label, position weights exp(-j / gamma_decay)).
+  [P5] §3.4 (the same loss aggregated over masked positions divided by the
+       total weight; prev_token_ids = [anchor, t_1, ...] for the block bias).
   [P4] §3.2 (hardware-aware prefix scheduler: B(l), tau(l), Theta = tau *
        SPS(B), the greedy scan over candidates sorted by survival) and §7.2
        (SPS(B) as an offline-measured monotone lookup table; the sort is
@@ -36,7 +40,8 @@ notes as well):
     ([P1] s_i = w_c^T [h_i; m_i] + b_c); no calibration is applied;
   * alpha is clamped to [0, 1] and set to 0 at invalid slots; a block with no
     valid slot reports tau = 0 and is left out of the mean ([P1] 离线指标);
-  * the prefix scheduler: see ``prefix_schedule`` for its four readings.
+  * the prefix scheduler: see ``prefix_schedule`` for its four readings;
+  * the training loss: see ``compute_loss`` for how its terms are aggregated.
 """
 from __future__ import annotations
 
@@ -333,3 +338,65 @@ def prefix_schedule(survival: np.ndarray, sps: np.ndarray):
     for _, m in cands[:k_best]:
         lengths[m // gamma] += 1
     return lengths, theta_max, tau_best, R + k_best
+
+
+# --------------------------------------------------------------------------
+# Teacher-forced block logits and the training loss (forward).  [P4] §2.3 and
+# [P5] §3.3: with the reference tokens known, every position's bias comes from
+# its known previous token in one batched step (``teacher_forced_logits``
+# above).  [P4] §4.1: per position j, CE_j = -log q_j(x*_j) and
+# L1_j = sum_v |p_j(v) - q_j(v)| with p = softmax(teacher), q = softmax(draft);
+# the soft label alpha_j = clamp(1 - L1_j / 2, 0, 1) supervises the confidence
+# logit through BCE-with-logits; weights w_j = exp(-j / gamma_decay);
+# total = l_ce * CE + l_l1 * L1 + l_conf * conf.  [P1] Baseline loss: the same
+# three terms with weights exp(-i/4).
+
+
+def compute_loss(draft: np.ndarray, teacher: np.ndarray, target: np.ndarray,
+                 conf_logit: Optional[np.ndarray] = None, valid: Optional[np.ndarray] = None, *,
+                 lambda_ce: float = 0.1, lambda_l1: float = 0.9, lambda_conf: float = 1.0,
+                 decay_gamma: float = 4.0, conf_decay: bool = False):
+    """draft, teacher [B, gamma, V]; target [B, gamma] int; conf_logit
+    [B, gamma] or None (no confidence term); valid [B, gamma] or None (all)
+    -> (per_pos [B, gamma, 4] = (CE, L1, alpha, BCE), (total, ce, l1, conf)).
+
+    Aggregation (the pages give it three ways that agree when every position
+    is valid: [P4] §4.1 normalises the weights and averages over the batch,
+    [P5] §3.4 divides the masked weighted sum by the total weight, [P1] weights
+    valid response positions):
+      * CE and L1: sum over valid (b, j) of w_j * term / sum of w_j over the
+        same positions;
+      * conf: the plain mean of BCE over valid positions, as both code excerpts
+        ([P4] §4.1, [P5] §3.4) compute it; ``conf_decay`` weights it like CE
+        and L1 instead, as [P1]'s prose says all three terms are;
+      * invalid positions report zeros and carry no weight; with no valid
+        position every aggregate is 0.
+    """
+    B, gamma, V = draft.shape
+    v = np.ones((B, gamma), dtype=bool) if valid is None else valid.astype(bool)
+    p = softmax(np.asarray(teacher, dtype=np.float64))
+    q = softmax(np.asarray(draft, dtype=np.float64))
+    l1 = np.abs(p - q).sum(axis=-1)
+    alpha = np.clip(1.0 - 0.5 * l1, 0.0, 1.0)
+    d = np.asarray(draft, dtype=np.float64)
+    m = d.max(axis=-1)
+    lse = m + np.log(np.exp(d - m[..., None]).sum(axis=-1))
+    ce = lse - np.take_along_axis(d, np.asarray(target, dtype=np.int64)[..., None], axis=-1)[..., 0]
+    if conf_logit is not None:
+        s = np.asarray(conf_logit, dtype=np.float64)
+        bce = np.maximum(s, 0.0) - s * alpha + np.log1p(np.exp(-np.abs(s)))
+    else:
+        bce = np.zeros((B, gamma))
+    w = np.exp(-np.arange(gamma, dtype=np.float64) / decay_gamma)[None, :] * v
+    per_pos = np.stack([ce, l1, alpha, bce], axis=-1) * v[..., None]
+    W = w.sum()
+    ce_a = float((w * ce).sum() / W) if W > 0 else 0.0
+    l1_a = float((w * l1).sum() / W) if W > 0 else 0.0
+    if conf_logit is None or not v.any():
+        cf_a = 0.0
+    elif conf_decay:
+        cf_a = float((w * bce).sum() / W)
+    else:
+        cf_a = float(bce[v].mean())
+    total = lambda_ce * ce_a + lambda_l1 * l1_a + lambda_conf * cf_a
+    return per_pos, (total, ce_a, l1_a, cf_a)
