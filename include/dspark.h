@@ -252,6 +252,68 @@ dspark_status_t dspark_prefix_schedule(const float* survival, int64_t R, int64_t
                                        const double* sps, int64_t n_sps, int32_t* lengths,
                                        double* stats, hipStream_t stream);
 
+/*
+ * Teacher-forced block logits.  [P4] §2.3 (apply_block_logits: with the
+ * reference tokens known, every position's Markov bias comes from its known
+ * previous token in one batched step); [P5] §3.3 (prev_token_ids = [anchor,
+ * t_1, ..., t_{gamma-1}]).  The bias is linear as in dspark_markov_propose:
+ *   logits_out[b, j, v] = U[b, j, v] + sum_k A[prev_tokens[b, j], k] * Bm[k, v].
+ *
+ *   U            [B, gamma, V] float32   base logits (the LM head's output)
+ *   prev_tokens  [B, gamma] int32        previous token of each position, in [0, V)
+ *   A [V, r], Bm [r, V]  dtype wdt       Markov tables, as for dspark_markov_propose
+ *   logits_out   [B, gamma, V] float32   (out) corrected logits U~
+ * bf16 tables with r in {32, 64, 128, 256}, V % 8 == 0 and 16-byte aligned
+ * arrays run on MFMA (Bm streamed once per tile range for up to 128 rows);
+ * other shapes take a plain per-row kernel.
+ * Requirements: B, gamma, V, r > 0; r <= 1024.
+ */
+dspark_status_t dspark_apply_block_logits(const float* U, int64_t B, int64_t gamma, int64_t V,
+                                          const int32_t* prev_tokens, const void* A, const void* Bm,
+                                          dspark_dtype_t wdt, int64_t r, float* logits_out,
+                                          hipStream_t stream);
+
+/*
+ * Workspace size (bytes) needed by dspark_compute_loss for these sizes.
+ */
+dspark_status_t dspark_compute_loss_workspace(int64_t B, int64_t gamma, int64_t V, size_t* bytes);
+
+/*
+ * Training-loss forward.  [P4] §4.1: per position j, with p = softmax(teacher)
+ * and q = softmax(draft),
+ *   CE_j = -log q_j(target_j),  L1_j = sum_v |p_j(v) - q_j(v)|,
+ *   alpha_j = clamp(1 - L1_j / 2, 0, 1),
+ *   BCE_j = BCE-with-logits(conf_logit_j, alpha_j)
+ *         = max(s, 0) - s * alpha + log(1 + exp(-|s|)),
+ *   w_j = exp(-j / decay_gamma),
+ *   total = lambda_ce * CE + lambda_l1 * L1 + lambda_conf * conf.
+ * [P5] §3.4: aggregates are masked weighted sums over the total weight:
+ *   CE = sum_{valid (b,j)} w_j CE_bj / sum_{valid} w_j, L1 likewise;
+ *   conf = mean of BCE over valid positions (conf_decay == 0, as both code
+ *   excerpts compute it) or weighted like CE (conf_decay != 0, [P1]'s prose).
+ * The pages' defaults: lambda_ce 0.1, lambda_l1 0.9, lambda_conf 1.0,
+ * decay_gamma 4.
+ *
+ *   draft, teacher  [B, gamma, V] float32, 16-byte aligned
+ *   target          [B, gamma] int32 in [0, V)
+ *   conf_logit      [B, gamma] float32 or NULL (no confidence term: BCE = 0)
+ *   valid           [B, gamma] uint8 or NULL (all valid)
+ *   per_pos         [B, gamma, 4] float32 (out, optional): CE, L1, alpha, BCE;
+ *                   zeros at invalid positions
+ *   losses          [4] float64 (out): total, CE, L1, conf; 0 when no position
+ *                   is valid; NaN when a bounded wait of the overlap pass ran
+ *                   out (only possible when other work occupies the device)
+ *   ws, ws_bytes    workspace of at least dspark_compute_loss_workspace bytes,
+ *                   zero-filled before its first use (a call leaves it ready)
+ * Requirements: B, gamma, V > 0; gamma <= 16; V % 4 == 0; decay_gamma > 0.
+ */
+dspark_status_t dspark_compute_loss(const float* draft, const float* teacher, const int32_t* target,
+                                    const float* conf_logit, const uint8_t* valid, int64_t B,
+                                    int64_t gamma, int64_t V, float lambda_ce, float lambda_l1,
+                                    float lambda_conf, float decay_gamma, int32_t conf_decay,
+                                    float* per_pos, double* losses, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,10 @@ _SIGNATURES = {
     "dspark_overlap_tau": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp,
                                      _vp, _vp, _vp, _sz, _vp]),
     "dspark_prefix_schedule": (C.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "dspark_apply_block_logits": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64, _vp, _vp]),
+    "dspark_compute_loss_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
+    "dspark_compute_loss": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _f32, _f32, _f32,
+                                      _i32, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -182,3 +186,30 @@ def dspark_prefix_schedule(survival, sps, lengths, stats, stream=None) -> None:
     R, gamma = survival.shape
     _check(lib().dspark_prefix_schedule(_ptr(survival), R, gamma, _ptr(sps), sps.shape[0],
                                         _ptr(lengths), _ptr(stats), _stream(stream)))
+
+
+def dspark_apply_block_logits(U, prev_tokens, A, Bm, logits_out, stream=None) -> None:
+    """logits_out [B, gamma, V] = U + A[prev_tokens] . Bm (teacher-forced)."""
+    B, gamma, V = U.shape
+    _check(lib().dspark_apply_block_logits(_ptr(U), B, gamma, V, _ptr(prev_tokens), _ptr(A), _ptr(Bm),
+                                           _dtype(A), A.shape[1], _ptr(logits_out), _stream(stream)))
+
+
+def dspark_compute_loss_workspace(B: int, gamma: int, V: int) -> int:
+    n = _sz(0)
+    _check(lib().dspark_compute_loss_workspace(B, gamma, V, C.byref(n)))
+    return n.value
+
+
+def dspark_compute_loss(draft, teacher, target, losses, *, conf_logit=None, valid=None, per_pos=None,
+                        lambda_ce: float = 0.1, lambda_l1: float = 0.9, lambda_conf: float = 1.0,
+                        decay_gamma: float = 4.0, conf_decay: bool = False, ws=None, stream=None) -> None:
+    """losses [4] float64 (total, CE, L1, conf) and optional per_pos [B, gamma, 4]."""
+    import torch
+    B, gamma, V = draft.shape
+    if ws is None:
+        ws = torch.zeros(dspark_compute_loss_workspace(B, gamma, V), dtype=torch.uint8, device=draft.device)
+    _check(lib().dspark_compute_loss(
+        _ptr(draft), _ptr(teacher), _ptr(target), _ptr(conf_logit), _ptr(valid), B, gamma, V,
+        float(lambda_ce), float(lambda_l1), float(lambda_conf), float(decay_gamma), int(bool(conf_decay)),
+        _ptr(per_pos), _ptr(losses), _ptr(ws), ws.numel(), _stream(stream)))

@@ -72,6 +72,8 @@ size_t overlap_ws_tau_bytes(int64_t N, int64_t gamma) {
 // zero head (the single-launch path's counters, fixed offset 0), tau
 // partials, chunk states of the split path, and for the single-launch path
 // the row normalisers and 64-bit chunk slots
+void carve_overlap_ws(OverlapArgs& a, void* ws, int64_t N, int64_t gamma, int64_t V);
+
 size_t overlap_ws_bytes(int64_t N, int64_t gamma, int64_t V) {
   const int64_t rows = N * gamma;
   const int nchunk = overlap_split_chunks(rows, V);
@@ -81,6 +83,33 @@ size_t overlap_ws_bytes(int64_t N, int64_t gamma, int64_t V) {
     s += align_up(static_cast<size_t>(rows) * 16) + align_up(static_cast<size_t>(rows) * nchunk * 3 * 8);
   }
   return s;
+}
+
+// the overlap workspace: the zero head (wait words) first, then the per-block
+// tau partials and, on the split path, the chunk states, tagged normalisers
+// and single-launch slots
+void carve_overlap_ws(OverlapArgs& a, void* ws, int64_t N, int64_t gamma, int64_t V) {
+  char* p = static_cast<char*>(ws);
+  a.sync = reinterpret_cast<unsigned*>(p);
+  p += kOvSyncWords * 4;
+  a.ws_acc = reinterpret_cast<double*>(p);
+  p += overlap_ws_tau_bytes(N, gamma);
+  a.nchunk = overlap_split_chunks(N * gamma, V);
+  if (a.nchunk > 1) {
+    const size_t rows = static_cast<size_t>(N * gamma);
+    a.ws_split = reinterpret_cast<float*>(p);
+    p += align_up(rows * a.nchunk * 5 * sizeof(float));
+    a.ws_norm = reinterpret_cast<unsigned long long*>(p);
+    p += align_up(rows * 16);
+    a.ws_fused = reinterpret_cast<unsigned long long*>(p);
+  }
+}
+
+// compute_loss: the overlap workspace, then alpha [rows], tau [N], the draft
+// log-normalisers [rows] and the overlap sums [rows]
+size_t loss_ws_bytes(int64_t B, int64_t gamma, int64_t V) {
+  const size_t rows = static_cast<size_t>(B * gamma);
+  return align_up(overlap_ws_bytes(B, gamma, V)) + 3 * align_up(rows * 4) + align_up(static_cast<size_t>(B) * 4);
 }
 
 }  // namespace
@@ -301,20 +330,7 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
   a.tau = tau;
   a.accept_rate_at = accept_rate_at;
   a.tau_mean = tau_mean;
-  char* p = static_cast<char*>(ws);
-  a.sync = reinterpret_cast<unsigned*>(p);
-  p += kOvSyncWords * 4;
-  a.ws_acc = reinterpret_cast<double*>(p);
-  p += overlap_ws_tau_bytes(N, gamma);
-  a.nchunk = overlap_split_chunks(N * gamma, V);
-  if (a.nchunk > 1) {
-    const size_t rows = static_cast<size_t>(N * gamma);
-    a.ws_split = reinterpret_cast<float*>(p);
-    p += align_up(rows * a.nchunk * 5 * sizeof(float));
-    a.ws_norm = reinterpret_cast<unsigned long long*>(p);
-    p += align_up(rows * 16);
-    a.ws_fused = reinterpret_cast<unsigned long long*>(p);
-  }
+  carve_overlap_ws(a, ws, N, gamma, V);
   return hip_status(launch_overlap_tau(a, stream), fn);
 }
 
@@ -335,4 +351,96 @@ extern "C" dspark_status_t dspark_prefix_schedule(const float* survival, int64_t
   return hip_status(launch_prefix_schedule(survival, static_cast<int>(R), static_cast<int>(gamma), sps,
                                            static_cast<int>(kmax), lengths, stats, stream),
                     fn);
+}
+
+// ---------------------------------------------------------------------------
+extern "C" dspark_status_t dspark_apply_block_logits(const float* U, int64_t B, int64_t gamma, int64_t V,
+                                                     const int32_t* prev_tokens, const void* A, const void* Bm,
+                                                     dspark_dtype_t wdt, int64_t r, float* logits_out,
+                                                     hipStream_t stream) {
+  const char* fn = "dspark_apply_block_logits";
+  if (!U || !prev_tokens || !A || !Bm || !logits_out)
+    return fail(DSPARK_EINVAL, "%s: U, prev_tokens, A, Bm and logits_out must be non-NULL", fn);
+  if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0) return fail(DSPARK_EINVAL, "%s: B, gamma, V, r must be positive", fn);
+  if (V > kI32Max || B * gamma > kI32Max / 2) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  if (wdt != DSPARK_F32 && wdt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)wdt);
+  if (r > kMaxRank) return fail(DSPARK_EUNSUPPORTED, "%s: r > %d", fn, kMaxRank);
+  const bool bf16 = wdt == DSPARK_BF16;
+  // the MFMA kernel needs 16-byte rows of U and aligned tables
+  const bool vec = bf16 && V % 8 == 0 && aligned16(U) && aligned16(A) && aligned16(Bm) && aligned16(logits_out);
+  return hip_status(launch_block_logits(U, prev_tokens, A, Bm, vec, static_cast<int>(B * gamma), static_cast<int>(V),
+                                        static_cast<int>(r), logits_out, stream, bf16),
+                    fn);
+}
+
+extern "C" dspark_status_t dspark_compute_loss_workspace(int64_t B, int64_t gamma, int64_t V, size_t* bytes) {
+  if (!bytes) return fail(DSPARK_EINVAL, "dspark_compute_loss_workspace: bytes is NULL");
+  if (B <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "dspark_compute_loss_workspace: sizes must be positive");
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "dspark_compute_loss_workspace: gamma > %d", kMaxGamma);
+  if (B * gamma > kI32Max) return fail(DSPARK_EINVAL, "dspark_compute_loss_workspace: sizes too large");
+  *bytes = loss_ws_bytes(B, gamma, V);
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status_t dspark_compute_loss(const float* draft, const float* teacher, const int32_t* target,
+                                               const float* conf_logit, const uint8_t* valid, int64_t B,
+                                               int64_t gamma, int64_t V, float lambda_ce, float lambda_l1,
+                                               float lambda_conf, float decay_gamma, int32_t conf_decay,
+                                               float* per_pos, double* losses, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
+  const char* fn = "dspark_compute_loss";
+  if (!draft || !teacher || !target || !losses)
+    return fail(DSPARK_EINVAL, "%s: draft, teacher, target and losses must be non-NULL", fn);
+  if (B <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "%s: B, gamma, V must be positive", fn);
+  if (V > kI32Max || B * gamma > kI32Max) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  if (!std::isfinite(decay_gamma) || decay_gamma <= 0.0f)
+    return fail(DSPARK_EINVAL, "%s: decay_gamma must be finite and positive", fn);
+  if (!std::isfinite(lambda_ce) || !std::isfinite(lambda_l1) || !std::isfinite(lambda_conf))
+    return fail(DSPARK_EINVAL, "%s: the loss weights must be finite", fn);
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
+  if (V % 4) return fail(DSPARK_EUNSUPPORTED, "%s: V %% 4 != 0", fn);
+  if (!aligned16(teacher) || !aligned16(draft))
+    return fail(DSPARK_EUNSUPPORTED, "%s: teacher/draft must be 16-byte aligned", fn);
+  const size_t need = loss_ws_bytes(B, gamma, V);
+  if (!ws || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+  const size_t rows = static_cast<size_t>(B * gamma);
+  char* tail = static_cast<char*>(ws) + align_up(overlap_ws_bytes(B, gamma, V));
+  float* alpha = reinterpret_cast<float*>(tail);
+  float* lse_d = reinterpret_cast<float*>(tail + align_up(rows * 4));
+  float* ov = reinterpret_cast<float*>(tail + 2 * align_up(rows * 4));
+  float* tau = reinterpret_cast<float*>(tail + 3 * align_up(rows * 4));
+  OverlapArgs o{};
+  o.teacher = teacher;
+  o.draft = draft;
+  o.valid = valid;
+  o.N = static_cast<int>(B);
+  o.gamma = static_cast<int>(gamma);
+  o.V = static_cast<int>(V);
+  o.alpha = alpha;
+  o.tau = tau;
+  o.lse_draft = lse_d;
+  o.ov_sum = ov;
+  carve_overlap_ws(o, ws, B, gamma, V);
+  hipError_t e = launch_overlap_tau(o, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  LossArgs l{};
+  l.draft = draft;
+  l.target = target;
+  l.conf = conf_logit;
+  l.valid = valid;
+  l.lse_draft = lse_d;
+  l.ov_sum = ov;
+  l.tau = tau;
+  l.N = static_cast<int>(B);
+  l.gamma = static_cast<int>(gamma);
+  l.V = static_cast<int>(V);
+  l.lambda_ce = lambda_ce;
+  l.lambda_l1 = lambda_l1;
+  l.lambda_conf = lambda_conf;
+  l.decay = decay_gamma;
+  l.conf_decay = conf_decay != 0;
+  l.per_pos = per_pos;
+  l.losses = losses;
+  return hip_status(launch_loss_finish(l, stream), fn);
 }

@@ -111,7 +111,30 @@ struct OverlapArgs {
   unsigned long long wait_ticks;
   int nchunk;            // workgroups per row (1: one workgroup per row)
   int chunk4;            // float4 elements per chunk (set by the launcher)
+  // optional per-row outputs of the dense mode (valid rows only): the draft's
+  // log-normaliser and the unclamped sum of min(p, q)
+  float* lse_draft;
+  float* ov_sum;
 };
+
+// training-loss finish: per-row CE, L1, alpha, BCE and the weighted aggregates
+struct LossArgs {
+  const float* draft;
+  const int32_t* target;
+  const float* conf;       // NULL: no confidence term
+  const uint8_t* valid;    // NULL: every position valid
+  const float* lse_draft;  // per row, from the overlap pass
+  const float* ov_sum;     // per row, from the overlap pass
+  const float* tau;        // per block, from the overlap pass (NaN: a wait ran out)
+  int N, gamma, V;
+  float lambda_ce, lambda_l1, lambda_conf, decay;
+  int conf_decay;
+  float* per_pos;          // [rows][4] or NULL
+  double* losses;          // [4]
+};
+hipError_t launch_loss_finish(const LossArgs& a, hipStream_t s);
+hipError_t launch_block_logits(const float* U, const int32_t* prev, const void* A, const void* Bm, bool vec,
+                               int M, int V, int r, float* out, hipStream_t s, bool bf16);
 
 int overlap_tau_blocks(int64_t N);
 int overlap_split_chunks(int64_t rows, int64_t V);

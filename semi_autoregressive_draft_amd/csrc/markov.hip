@@ -337,7 +337,9 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int NCH, int CPW, bool SAMPLE>
+// STATS = false: teacher-forced block logits only (every row's previous token
+// given; each tile's U~ is stored to logits_out and nothing else is kept).
+template <int NCH, int CPW, bool SAMPLE, bool STATS = true>
 __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
   extern __shared__ __align__(16) unsigned char wide_lds[];
   u32x4* const ops = reinterpret_cast<u32x4*>(wide_lds);   // [2][NCH * 4][64] B operands
@@ -428,6 +430,16 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
                                                          acc[c], 0, 0, 0);
     const int col = col_of(t);
     const bool cok = col < a.V;
+    if constexpr (!STATS) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int b = req0 + 4 * g + ii;
+        if (b < a.B && cok)
+          *reinterpret_cast<f32x4*>(a.logits_out + (static_cast<size_t>(b) * a.gamma + a.j) * V + col) =
+              f32x4{acc[0][ii] + u[ii][0], acc[1][ii] + u[ii][1], acc[2][ii] + u[ii][2], acc[3][ii] + u[ii][3]};
+      }
+      return;
+    }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int b = req0 + 4 * g + ii;
@@ -519,6 +531,7 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
   }
 
   // one partial per request: 16-lane reductions of the lane states
+  if constexpr (!STATS) return;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int b = req0 + 4 * g + ii;
@@ -1000,17 +1013,24 @@ struct WidePlan {
   size_t lds;
 };
 
-template <int NCH, int CPW, bool SAMPLE>
+template <int NCH, int CPW, bool SAMPLE, bool STATS>
 static void launch_wide_kernel(const StepArgs& a, int tpw, dim3 grid, int nw, hipStream_t s) {
-  hipLaunchKernelGGL((markov_step_wide<NCH, CPW, SAMPLE>), grid, dim3(kWave * nw),
+  hipLaunchKernelGGL((markov_step_wide<NCH, CPW, SAMPLE, STATS>), grid, dim3(kWave * nw),
                      wide_ops_bytes(NCH) + (SAMPLE ? kWideSeedBytes : 0), s, a, tpw);
 }
 
+// stats = false: the block-logits variant (never sampled)
 template <int NCH, int CPW>
-static void pick_wide(bool sample, WidePlan* p) {
-  p->fn = sample ? reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, true>)
-                 : reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, false>);
-  p->launch = sample ? &launch_wide_kernel<NCH, CPW, true> : &launch_wide_kernel<NCH, CPW, false>;
+static void pick_wide(bool sample, bool stats, WidePlan* p) {
+  if (!stats) {
+    p->fn = reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, false, false>);
+    p->launch = &launch_wide_kernel<NCH, CPW, false, false>;
+    p->lds = wide_ops_bytes(NCH);
+    return;
+  }
+  p->fn = sample ? reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, true, true>)
+                 : reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, false, true>);
+  p->launch = sample ? &launch_wide_kernel<NCH, CPW, true, true> : &launch_wide_kernel<NCH, CPW, false, true>;
   p->lds = wide_ops_bytes(NCH) + (sample ? kWideSeedBytes : 0);
 }
 
@@ -1028,11 +1048,11 @@ static int wide_occupancy(const void* fn, int nw, size_t lds) {
   return nb;
 }
 
-// false: the shape takes the narrow kernel (B <= 16, or a rank other than
-// 32, 64, 128 or 256)
-static bool wide_plan(bool bf16, bool sample, int B, int r, int V, WidePlan* p) {
+// false: the shape takes another kernel (fp32 tables, a rank other than 32,
+// 64, 128 or 256, or, for the chain, B <= 16)
+static bool wide_plan(bool bf16, bool sample, int B, int r, int V, WidePlan* p, bool stats = true) {
   const int nch = r / 32;
-  if (!bf16 || B <= 16 || r % 32 || (nch != 1 && nch != 2 && nch != 4 && nch != 8)) return false;
+  if (!bf16 || (stats && B <= 16) || r % 32 || (nch != 1 && nch != 2 && nch != 4 && nch != 8)) return false;
   const int groups = (B + 15) / 16;
   // at least nch / 2 waves, so that a wave loads at most 2 chunks (waves
   // past the last request only load and store operands)
@@ -1040,12 +1060,12 @@ static bool wide_plan(bool bf16, bool sample, int B, int r, int V, WidePlan* p) 
   p->ny = (groups + p->nw - 1) / p->nw;
   const bool two = nch > p->nw;                        // chunks per wave: 1 or 2
   switch (nch * 2 + (two ? 1 : 0)) {
-    case 2: pick_wide<1, 1>(sample, p); break;
-    case 4: pick_wide<2, 1>(sample, p); break;
-    case 8: pick_wide<4, 1>(sample, p); break;
-    case 9: pick_wide<4, 2>(sample, p); break;
-    case 16: pick_wide<8, 1>(sample, p); break;
-    default: pick_wide<8, 2>(sample, p); break;
+    case 2: pick_wide<1, 1>(sample, stats, p); break;
+    case 4: pick_wide<2, 1>(sample, stats, p); break;
+    case 8: pick_wide<4, 1>(sample, stats, p); break;
+    case 9: pick_wide<4, 2>(sample, stats, p); break;
+    case 16: pick_wide<8, 1>(sample, stats, p); break;
+    default: pick_wide<8, 2>(sample, stats, p); break;
   }
   const int ntiles = (V + kWideCols - 1) / kWideCols;
   const int slots = max(1, wide_occupancy(p->fn, p->nw, p->lds) * max(1, device_info().cus));
@@ -1103,6 +1123,60 @@ hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s) {
     hipLaunchKernelGGL(markov_topk<uint16_t>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
   else
     hipLaunchKernelGGL(markov_topk<float>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Teacher-forced block logits ("DSpark 论文精读", §2.3 apply_block_logits;
+// "DeepSpec 训练全流程详解", §3.3 prev_token_ids = [anchor, t_1, ...]):
+// U~[m, v] = U[m, v] + sum_k A[prev[m], k] Bm[k, v] for every row m at once.
+// bf16 tables with r in {32, 64, 128, 256} take the wide step kernel in its
+// store-only form (rows as requests, the previous token of row m given);
+// other shapes take this kernel: one thread per (row, column), the A row in
+// LDS, a plain dot product over r (Bm is re-read per row: a fallback for
+// fp32 tables and uncommon ranks).
+template <typename WT>
+__global__ __launch_bounds__(256) void block_logits_generic(const float* __restrict__ U, const int32_t* __restrict__ prev,
+                                                            const WT* __restrict__ A, const WT* __restrict__ Bm, int V,
+                                                            int r, float* __restrict__ out) {
+  __shared__ float arow[kMaxRank];
+  const int m = blockIdx.y, tid = threadIdx.x;
+  const int pv = prev[m];
+  for (int k = tid; k < r; k += 256) arow[k] = to_f32(A[static_cast<size_t>(pv) * r + k]);
+  __syncthreads();
+  const int v = blockIdx.x * 256 + tid;
+  if (v >= V) return;
+  float bias = 0.f;
+  for (int k = 0; k < r; ++k) bias = fmaf(arow[k], to_f32(Bm[static_cast<size_t>(k) * V + v]), bias);
+  out[static_cast<size_t>(m) * V + v] = U[static_cast<size_t>(m) * V + v] + bias;
+}
+
+// vec: bf16 tables, V % 8 == 0 and 16-byte aligned operands (the MFMA kernel)
+hipError_t launch_block_logits(const float* U, const int32_t* prev, const void* A, const void* Bm, bool vec,
+                               int M, int V, int r, float* out, hipStream_t s, bool bf16) {
+  StepArgs a{};
+  a.U = U;
+  a.anchor = prev;
+  a.A = A;
+  a.Bm = Bm;
+  a.B = M;
+  a.gamma = 1;
+  a.j = 0;
+  a.V = V;
+  a.r = r;
+  a.logits_out = out;
+  WidePlan p{};
+  if (vec && wide_plan(true, false, M, r, V, &p, false)) {
+    p.launch(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
+  } else {
+    const dim3 grid((V + 255) / 256, M);
+    if (bf16)
+      hipLaunchKernelGGL(block_logits_generic<uint16_t>, grid, dim3(256), 0, s, U, prev,
+                         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), V, r, out);
+    else
+      hipLaunchKernelGGL(block_logits_generic<float>, grid, dim3(256), 0, s, U, prev, static_cast<const float*>(A),
+                         static_cast<const float*>(Bm), V, r, out);
+  }
   return hipGetLastError();
 }
 

@@ -106,6 +106,10 @@ __global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
     const int last = (n4 - 1 - tid) >= 0 ? tid + ((n4 - 1 - tid) / kOvThreads) * kOvThreads : -1;
     for (int e = last; e >= 0; e -= kOvThreads) s += sum_exp_min4(tp[e], dp[e], Lt, Ld);
     total = block_sum<NW>(s, red_f);
+    if (tid == 0) {
+      if (a.lse_draft) a.lse_draft[row] = Ld;
+      if (a.ov_sum) a.ov_sum[row] = total;
+    }
   } else {
     LseState lt{kNegInf, 0.f};
     for (int e = tid; e < n4; e += kOvThreads) online_add4(lt, tp[e]);
@@ -195,13 +199,21 @@ __global__ __launch_bounds__(kWave) void overlap_split_finish(OverlapArgs a) {
   if (a.draft) {
     const float* st = a.ws_split + static_cast<size_t>(row) * a.nchunk * 5;
     for (int c = lane; c < a.nchunk; c += kWave) s += st[c * 5 + 4];
+    if (a.lse_draft) {
+      float lt, ld;
+      row_normalisers(a, row, lt, ld);
+      if (lane == 0) a.lse_draft[row] = ld;
+    }
   } else {
     float lt, ld;
     row_normalisers(a, row, lt, ld);
     s = candidate_overlap(a, row, lt, lane, kWave);
   }
   s = wave_sum(s);
-  if (lane == 0) a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
+  if (lane == 0) {
+    a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
+    if (a.draft && a.ov_sum) a.ov_sum[row] = s;
+  }
 }
 
 // tau per block and per-workgroup partial sums for the aggregates (a full
@@ -271,10 +283,16 @@ __global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapA
   const int rows = a.N * a.gamma;
   for (int row = w; row < rows; row += kTauThreads / kWave) {
     float s = 0.f;
-    if (!a.valid || a.valid[row]) {
+    const bool vr = !a.valid || a.valid[row];
+    if (vr) {
       if (a.draft) {
         const float* st = a.ws_split + static_cast<size_t>(row) * a.nchunk * 5;
         for (int c = lane; c < a.nchunk; c += kWave) s += st[c * 5 + 4];
+        if (a.lse_draft) {
+          float lt, ld;
+          row_normalisers(a, row, lt, ld);
+          if (lane == 0) a.lse_draft[row] = ld;
+        }
       } else {
         float lt, ld;
         row_normalisers(a, row, lt, ld);
@@ -282,7 +300,10 @@ __global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapA
       }
       s = wave_sum(s);
     }
-    if (lane == 0) a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
+    if (lane == 0) {
+      a.alpha[row] = fminf(fmaxf(s, 0.f), 1.f);
+      if (vr && a.draft && a.ov_sum) a.ov_sum[row] = s;
+    }
   }
   __syncthreads();   // alpha of every row written by this workgroup
   tau_range<false>(a, 0);
@@ -393,6 +414,7 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
     }
     const float Lt = t.m + logf(t.s), Ld = d.m + logf(d.s);
     if constexpr (DENSE) {
+      if (lane == 0 && valid && a.lse_draft) a.lse_draft[row] = Ld;
       // each normaliser travels with this call's number in one 64-bit word,
       // so the word is its own release flag
       if (lane < 2) {
@@ -450,6 +472,7 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
       float s2 = __uint_as_float(static_cast<uint32_t>(sv[0])) + __uint_as_float(static_cast<uint32_t>(sv[1]));
       s2 = wave_sum(s2);
       if (lane == 0) {
+        if (valid && a.ov_sum) a.ov_sum[row] = s2;
         const float al = valid ? fminf(fmaxf(s2, 0.f), 1.f) : 0.f;
         wait_for(__hip_atomic_exchange(reinterpret_cast<unsigned*>(a.alpha) + row, __float_as_uint(al),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));

@@ -150,3 +150,31 @@ def test_prefix_schedule_validation(L):
     assert f(*args(gamma=17)) == bd.EUNSUPPORTED
     assert f(*args(R=2341, n=20000)) == bd.EUNSUPPORTED      # R * gamma > 16384
     assert "16384" in bd.last_error()
+
+
+def test_block_logits_and_loss_validation(L):
+    f = L.dspark_apply_block_logits
+    args = lambda **k: [k.get(n, d) for n, d in (
+        ("U", FAKE), ("B", 4), ("gamma", 7), ("V", 151936), ("prev", FAKE), ("A", FAKE), ("Bm", FAKE),
+        ("dt", bd.BF16), ("r", 256), ("out", FAKE), ("s", None))]
+    assert f(*args(U=None)) == bd.EINVAL
+    assert f(*args(out=None)) == bd.EINVAL
+    assert f(*args(r=0)) == bd.EINVAL
+    assert f(*args(r=1025)) == bd.EUNSUPPORTED
+    assert f(*args(dt=7)) == bd.EUNSUPPORTED
+    st, n = _ws(L.dspark_compute_loss_workspace, 4, 7, 151936)
+    assert st == bd.OK and n > 4 * 7 * 16
+    assert _ws(L.dspark_compute_loss_workspace, 4, 17, 151936)[0] == bd.EUNSUPPORTED
+    g = L.dspark_compute_loss
+    largs = lambda **k: [k.get(n, d) for n, d in (
+        ("draft", FAKE), ("teacher", FAKE), ("target", FAKE), ("conf", None), ("valid", None), ("B", 4),
+        ("gamma", 7), ("V", 151936), ("lce", 0.1), ("ll1", 0.9), ("lcf", 1.0), ("decay", 4.0), ("cd", 0),
+        ("per", None), ("losses", FAKE), ("ws", None), ("wsb", 0), ("s", None))]
+    assert g(*largs(target=None)) == bd.EINVAL
+    assert g(*largs(losses=None)) == bd.EINVAL
+    assert g(*largs(decay=0.0)) == bd.EINVAL
+    assert g(*largs(decay=float("nan"))) == bd.EINVAL
+    assert g(*largs(gamma=17)) == bd.EUNSUPPORTED
+    assert g(*largs(V=151934)) == bd.EUNSUPPORTED
+    assert g(*largs(draft=MISALIGNED)) == bd.EUNSUPPORTED
+    assert g(*largs()) == bd.EWORKSPACE

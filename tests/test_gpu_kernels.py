@@ -432,3 +432,103 @@ def test_prefix_schedule_on_survival_from_the_confidence_kernel():
     want_l, theta, tau, batch = o.prefix_schedule(a, sps)
     assert np.array_equal(lengths.cpu().numpy(), want_l)
     assert tuple(stats.cpu().numpy()) == (theta, tau, float(batch))
+
+
+# ----------------------------------------------------------------------------- K7
+@pytest.mark.parametrize("B,V,r,wdtype", [
+    (1, 5000, 256, "bf16"),      # 7 rows: one partly filled wave
+    (40, 3000, 256, "bf16"),     # 280 rows, ragged against 8 waves x 16 rows
+    (19, 2008, 64, "bf16"),      # ragged last tile
+    (5, 1000, 96, "bf16"),       # rank off the MFMA variants: plain kernel
+    (2, 1004, 64, "bf16"),       # V % 8 != 0: plain kernel
+    (3, 1000, 48, "f32"),        # float32 tables
+])
+def test_apply_block_logits_parity(B, V, r, wdtype):
+    dev = require_gpu()
+    gamma = 7
+    U, anchor, A, Bm = _markov_case(B, V, r, wdtype, seed=21)
+    prev = np.random.default_rng([21, 1]).integers(0, V, (B, gamma)).astype(np.int32)
+    out = torch.full((B, gamma, V), float("nan"), dtype=torch.float32, device=dev)
+    bd.dspark_apply_block_logits(to_dev(U), to_dev(prev), to_dev(A, wdtype), to_dev(Bm, wdtype), out)
+    torch.cuda.synchronize()
+    want = o.teacher_forced_logits(U.astype(np.float64), prev, o.to_f64(A, wdtype), o.to_f64(Bm, wdtype))
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    tight_check(got, want, np.abs(want).max(axis=-1, keepdims=True), what="block logits")
+
+
+def _run_loss(draft, teacher, target, conf, valid, conf_decay=False):
+    dev = require_gpu()
+    B, gamma, V = draft.shape
+    per = torch.full((B, gamma, 4), float("nan"), dtype=torch.float32, device=dev)
+    losses = torch.full((4,), float("nan"), dtype=torch.float64, device=dev)
+    bd.dspark_compute_loss(to_dev(draft), to_dev(teacher), to_dev(target), losses,
+                           conf_logit=None if conf is None else to_dev(conf),
+                           valid=None if valid is None else to_dev(valid), per_pos=per, conf_decay=conf_decay)
+    torch.cuda.synchronize()
+    return per.cpu().numpy(), losses.cpu().numpy()
+
+
+def _check_loss(per, losses, want_per, want_losses):
+    rel_check(per[..., 0], want_per[..., 0], np.abs(want_per[..., 0]), what="CE")
+    assert np.abs(per[..., 1] - want_per[..., 1]).max() <= 2 * ALPHA_ABS, "L1"
+    assert np.abs(per[..., 2] - want_per[..., 2]).max() <= ALPHA_ABS, "alpha"
+    assert np.abs(per[..., 3] - want_per[..., 3]).max() <= ALPHA_ABS, "BCE"
+    assert abs(losses[1] - want_losses[1]) <= 2e-2 * abs(want_losses[1]) + 1e-6, ("CE", losses, want_losses)
+    assert abs(losses[2] - want_losses[2]) <= 2 * ALPHA_ABS, ("L1", losses, want_losses)
+    assert abs(losses[3] - want_losses[3]) <= ALPHA_ABS, ("conf", losses, want_losses)
+    # the weights cross the ABI as float32
+    lam = [float(np.float32(x)) for x in (0.1, 0.9, 1.0)]
+    tot = lam[0] * losses[1] + lam[1] * losses[2] + lam[2] * losses[3]
+    assert abs(losses[0] - tot) <= 1e-12 * max(1.0, abs(tot))
+
+
+@pytest.mark.parametrize("N,sigma,conf_decay", [
+    (1, 0.5, False),     # 7 rows: the one-launch overlap path
+    (9, 1.0, True),      # 63 rows, decay-weighted confidence term
+    (20, 2.0, False),    # 140 rows: chunked rows over several launches
+    (200, 1.0, False),   # 1400 rows: one workgroup per row
+])
+def test_compute_loss_parity(N, sigma, conf_decay):
+    V, gamma = 5000, 7
+    teacher, draft = synth.overlap_inputs(N, V, sigma, seed=3)
+    g = np.random.default_rng([3, 9])
+    target = g.integers(0, V, (N, gamma)).astype(np.int32)
+    conf = g.standard_normal((N, gamma)).astype(np.float32)
+    valid = synth.validity(N, seed=3, trunc_frac=0.4, n_dummy=1 if N > 1 else 0)
+    per, losses = _run_loss(draft, teacher, target, conf, valid, conf_decay)
+    want_per, want_losses = o.compute_loss(draft.astype(np.float64), teacher.astype(np.float64), target,
+                                           conf.astype(np.float64), valid, conf_decay=conf_decay)
+    _check_loss(per, losses, want_per, want_losses)
+
+
+def test_compute_loss_without_confidence_or_mask():
+    V, gamma, N = 4096, 7, 3
+    teacher, draft = synth.overlap_inputs(N, V, 1.0, seed=5)
+    target = np.random.default_rng([5, 9]).integers(0, V, (N, gamma)).astype(np.int32)
+    per, losses = _run_loss(draft, teacher, target, None, None)
+    want_per, want_losses = o.compute_loss(draft.astype(np.float64), teacher.astype(np.float64), target)
+    _check_loss(per, losses, want_per, want_losses)
+    assert losses[3] == 0.0 and not per[..., 3].any()
+
+
+def test_teacher_forced_block_logits_then_loss():
+    # the training forward of [P5] §3.3-3.4: corrected logits from the reference
+    # tokens, then the loss against the teacher at those tokens
+    dev = require_gpu()
+    B, gamma, V, r = 6, 7, 3000, 256
+    U, anchor, A, Bm = _markov_case(B, V, r, "bf16", seed=23)
+    g = np.random.default_rng([23, 2])
+    ref = g.integers(0, V, (B, gamma)).astype(np.int32)               # reference tokens t_1..t_gamma
+    prev = np.concatenate([anchor[:, None], ref[:, :-1]], axis=1).astype(np.int32)
+    teacher = (U + g.standard_normal(U.shape).astype(np.float32)).astype(np.float32)
+    conf = g.standard_normal((B, gamma)).astype(np.float32)
+    draft = torch.empty((B, gamma, V), dtype=torch.float32, device=dev)
+    bd.dspark_apply_block_logits(to_dev(U), to_dev(prev), to_dev(A, "bf16"), to_dev(Bm, "bf16"), draft)
+    per = torch.empty((B, gamma, 4), dtype=torch.float32, device=dev)
+    losses = torch.empty((4,), dtype=torch.float64, device=dev)
+    bd.dspark_compute_loss(draft, to_dev(teacher), to_dev(ref), losses, conf_logit=to_dev(conf), per_pos=per)
+    torch.cuda.synchronize()
+    d64 = o.teacher_forced_logits(U.astype(np.float64), prev, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"))
+    want_per, want_losses = o.compute_loss(d64, teacher.astype(np.float64), ref, conf.astype(np.float64))
+    _check_loss(per.cpu().numpy(), losses.cpu().numpy(), want_per, want_losses)
