@@ -23,6 +23,11 @@ Sources (the pages), cited by title and section:
        accept-rate soft label, position weights exp(-j / gamma_decay)).
   [P5] §3.4 (the same loss aggregated over masked positions divided by the
        total weight; prev_token_ids = [anchor, t_1, ...] for the block bias).
+  [P5] §4.4 (verify_draft_tokens: accept probability min(1, p/q) at the
+       drafted token, the prefix cumprod of accept flags, a residual draw
+       from max(p - q, 0) after a rejection, a draw from the last target
+       distribution when every token is accepted); [P4] §2.1 (the rejection
+       step keeps the output distribution exactly the target's).
   [P4] §3.2 (hardware-aware prefix scheduler: B(l), tau(l), Theta = tau *
        SPS(B), the greedy scan over candidates sorted by survival) and §7.2
        (SPS(B) as an offline-measured monotone lookup table; the sort is
@@ -41,7 +46,9 @@ notes as well):
   * alpha is clamped to [0, 1] and set to 0 at invalid slots; a block with no
     valid slot reports tau = 0 and is left out of the mean ([P1] 离线指标);
   * the prefix scheduler: see ``prefix_schedule`` for its four readings;
-  * the training loss: see ``compute_loss`` for how its terms are aggregated.
+  * the training loss: see ``compute_loss`` for how its terms are aggregated;
+  * verification draws its uniforms and Gumbel noise from Philox4x32-10 with
+    counters kept apart from the draft sampler's: see ``verify_draft``.
 """
 from __future__ import annotations
 
@@ -400,3 +407,88 @@ def compute_loss(draft: np.ndarray, teacher: np.ndarray, target: np.ndarray,
         cf_a = float(bce[v].mean())
     total = lambda_ce * ce_a + lambda_l1 * l1_a + lambda_conf * cf_a
     return per_pos, (total, ce_a, l1_a, cf_a)
+
+
+# --------------------------------------------------------------------------
+# Rejection-sampling verification.  [P5] §4.4: for the proposal x_0..x_{L-1}
+# with draft distributions q_j and target distributions p_0..p_L (p_j is the
+# target's distribution for position j given the prefix up to x_{j-1}), token
+# j is accepted when u_j < min(1, p_j(x_j) / q_j(x_j)); only the leading run of
+# accepts counts (the cumprod of the accept flags); after a rejection at n the
+# next token is drawn from the residual max(p_n - q_n, 0) normalised, and when
+# all L are accepted it is drawn from p_L.  [P4] §2.1: this keeps the emitted
+# tokens distributed exactly as the target's.
+
+VERIFY_UNIFORM = 0x40000000   # counter word 1 of an acceptance uniform: this | j
+VERIFY_GUMBEL = 0x80000000    # counter word 1 of the final draw's noise: this | n
+
+
+def verify_uniform(seed: int, offset: int, j: int) -> float:
+    """u_j = (floor(w / 2^9) + 1/2) 2^-23 with w word 0 of Philox4x32-10 under key
+    (lo32 seed, hi32 seed) and counter (0, VERIFY_UNIFORM | j, lo32 offset,
+    hi32 offset): the draft sampler's u mapping on its own counter stream."""
+    w = philox_words(seed, offset, VERIFY_UNIFORM | j, 1)[0]
+    return (float(w >> np.uint64(9)) + 0.5) * 2.0 ** -23
+
+
+def verify_draft(target_logits: np.ndarray, draft_logits: np.ndarray, draft_tokens: np.ndarray,
+                 lengths: np.ndarray, seeds: np.ndarray, offset: int = 0, forced=None):
+    """target_logits [B, G+1, V], draft_logits [B, G, V], draft_tokens [B, G],
+    lengths [B] in 0..G, seeds [B] -> dict(accepted [B], next_token [B],
+    margin [B, G] = log-domain decision margins, gap [B] = top-2 gap of the
+    final draw's score, residual_empty [B]).
+
+    Readings: p = softmax(target row), q = softmax(draft row) at temperature 1;
+    token j is accepted iff log u_j < min(0, log p_j(x_j) - log q_j(x_j))
+    (the same event as u_j < min(1, p/q)); the final draw is Gumbel-max,
+    argmax_v log r(v) + G_v with G_v from ``gumbel`` on counter word 1
+    VERIFY_GUMBEL | n, over r = max(p_n - q_n, 0) after a rejection at n and
+    over r = p_L otherwise; a rejection whose residual has no mass (p_n = q_n
+    up to rounding) draws from p_n instead.  ``forced`` [B] (optional)
+    overrides the accepted count, to continue along another valid decision."""
+    t = np.asarray(target_logits, dtype=np.float64)
+    d = np.asarray(draft_logits, dtype=np.float64)
+    B, G1, V = t.shape
+    G = G1 - 1
+
+    def lse(x):
+        m = x.max()
+        return m + math.log(np.exp(x - m).sum())
+
+    accepted = np.zeros(B, dtype=np.int64)
+    nxt = np.zeros(B, dtype=np.int64)
+    margin = np.full((B, G), np.inf)
+    gap = np.zeros(B)
+    empty = np.zeros(B, dtype=bool)
+    for b in range(B):
+        L = int(lengths[b])
+        seed = int(seeds[b])
+        n = L
+        for j in range(L):
+            x = int(draft_tokens[b, j])
+            delta = (t[b, j, x] - lse(t[b, j])) - (d[b, j, x] - lse(d[b, j]))
+            lu = math.log(verify_uniform(seed, offset, j))
+            margin[b, j] = min(0.0, delta) - lu
+            if not lu < min(0.0, delta):
+                n = j
+                break
+        if forced is not None:
+            n = int(forced[b])
+        accepted[b] = n
+        g = gumbel(seed, offset, VERIFY_GUMBEL | n, V)
+        logp = t[b, n] - lse(t[b, n])
+        if n < L:
+            r = np.exp(logp) - np.exp(d[b, n] - lse(d[b, n]))
+            pos = r > 0.0
+            if pos.any():
+                score = np.where(pos, np.log(np.where(pos, r, 1.0)) + g, -np.inf)
+            else:
+                empty[b] = True
+                score = logp + g
+        else:
+            score = logp + g
+        k = int(np.argmax(score))                   # first index of the maximum
+        nxt[b] = k
+        srt = np.sort(score)
+        gap[b] = srt[-1] - srt[-2] if V > 1 else np.inf
+    return dict(accepted=accepted, next_token=nxt, margin=margin, gap=gap, residual_empty=empty)
