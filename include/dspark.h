@@ -314,6 +314,55 @@ dspark_status_t dspark_compute_loss(const float* draft, const float* teacher, co
                                     float* per_pos, double* losses, void* ws, size_t ws_bytes,
                                     hipStream_t stream);
 
+/*
+ * Workspace size (bytes) needed by dspark_verify for these sizes.
+ */
+dspark_status_t dspark_verify_workspace(int64_t B, int64_t gamma, int64_t V, size_t* bytes);
+
+/*
+ * Rejection-sampling verification of drafted blocks.  [P5] §4.4
+ * (verify_draft_tokens): with p_j = softmax(target row j) and q_j =
+ * softmax(draft row j), drafted token x_j is accepted with probability
+ * min(1, p_j(x_j) / q_j(x_j)); only the leading run of accepts counts; after
+ * a rejection at n the next token is drawn from max(p_n - q_n, 0)
+ * normalised, and when all L tokens are accepted from p_L.  [P4] §2.1: the
+ * emitted tokens then follow the target's distribution exactly.
+ *
+ *   target_logits [B, gamma + 1, V] float32   row j: the target's logits for
+ *                                             position j given the prefix up to
+ *                                             x_{j-1} (row 0: after the anchor)
+ *   draft_logits  [B, gamma, V] float32       the draft's logits at each position
+ *   draft_tokens  [B, gamma] int32            drafted tokens x_j in [0, V)
+ *   lengths       [B] int32 or NULL           proposal length L_b in 0..gamma
+ *                                             (e.g. dspark_prefix_schedule's
+ *                                             lengths; NULL: gamma)
+ *   seeds [B] uint64, offset                  randomness: Philox4x32-10 under key
+ *                                             (lo32 seed, hi32 seed); the
+ *                                             acceptance uniform of position j
+ *                                             from word 0 of counter (0, 2^30 | j,
+ *                                             lo32 offset, hi32 offset),
+ *                                             u = (floor(w / 2^9) + 1/2) 2^-23;
+ *                                             the final draw is Gumbel-max with
+ *                                             the noise of token v from word v mod 4
+ *                                             of counter (floor(v / 4), 2^31 | n,
+ *                                             lo32 offset, hi32 offset)
+ *   accepted      [B] int32 (out)             number of accepted drafted tokens
+ *   next_token    [B] int32 (out)             the token drawn after them
+ *   accept_prob   [B, gamma] float32 (out, optional)  min(1, p/q) at the
+ *                                             decided positions, 0 past them
+ *   ws, ws_bytes  workspace of at least dspark_verify_workspace bytes
+ * Decisions are taken as log u_j < min(0, log p_j(x_j) - log q_j(x_j)).  A
+ * rejection whose residual has no mass (p_n equal to q_n after rounding) draws
+ * from p_n.  Token ids outside [0, V) and lengths outside [0, gamma] are
+ * clamped.
+ * Requirements: B, gamma, V > 0; gamma <= 16; V % 4 == 0; logits 16-byte aligned.
+ */
+dspark_status_t dspark_verify(const float* target_logits, const float* draft_logits,
+                              const int32_t* draft_tokens, const int32_t* lengths,
+                              const uint64_t* seeds, uint64_t offset, int64_t B, int64_t gamma,
+                              int64_t V, int32_t* accepted, int32_t* next_token, float* accept_prob,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

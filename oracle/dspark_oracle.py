@@ -435,6 +435,7 @@ def verify_draft(target_logits: np.ndarray, draft_logits: np.ndarray, draft_toke
                  lengths: np.ndarray, seeds: np.ndarray, offset: int = 0, forced=None):
     """target_logits [B, G+1, V], draft_logits [B, G, V], draft_tokens [B, G],
     lengths [B] in 0..G, seeds [B] -> dict(accepted [B], next_token [B],
+    accept_prob [B, G] = min(1, p/q) at the decided positions (0 past them),
     margin [B, G] = log-domain decision margins, gap [B] = top-2 gap of the
     final draw's score, residual_empty [B]).
 
@@ -457,6 +458,7 @@ def verify_draft(target_logits: np.ndarray, draft_logits: np.ndarray, draft_toke
 
     accepted = np.zeros(B, dtype=np.int64)
     nxt = np.zeros(B, dtype=np.int64)
+    acc = np.zeros((B, G))
     margin = np.full((B, G), np.inf)
     gap = np.zeros(B)
     empty = np.zeros(B, dtype=bool)
@@ -469,6 +471,7 @@ def verify_draft(target_logits: np.ndarray, draft_logits: np.ndarray, draft_toke
             delta = (t[b, j, x] - lse(t[b, j])) - (d[b, j, x] - lse(d[b, j]))
             lu = math.log(verify_uniform(seed, offset, j))
             margin[b, j] = min(0.0, delta) - lu
+            acc[b, j] = min(1.0, math.exp(delta))
             if not lu < min(0.0, delta):
                 n = j
                 break
@@ -491,4 +494,5 @@ def verify_draft(target_logits: np.ndarray, draft_logits: np.ndarray, draft_toke
         nxt[b] = k
         srt = np.sort(score)
         gap[b] = srt[-1] - srt[-2] if V > 1 else np.inf
-    return dict(accepted=accepted, next_token=nxt, margin=margin, gap=gap, residual_empty=empty)
+    return dict(accepted=accepted, next_token=nxt, accept_prob=acc, margin=margin, gap=gap,
+                residual_empty=empty)

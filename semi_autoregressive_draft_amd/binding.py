@@ -40,6 +40,8 @@ _SIGNATURES = {
     "dspark_compute_loss_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
     "dspark_compute_loss": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _f32, _f32, _f32,
                                       _i32, _vp, _vp, _vp, _sz, _vp]),
+    "dspark_verify_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
+    "dspark_verify": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _u64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -213,3 +215,23 @@ def dspark_compute_loss(draft, teacher, target, losses, *, conf_logit=None, vali
         _ptr(draft), _ptr(teacher), _ptr(target), _ptr(conf_logit), _ptr(valid), B, gamma, V,
         float(lambda_ce), float(lambda_l1), float(lambda_conf), float(decay_gamma), int(bool(conf_decay)),
         _ptr(per_pos), _ptr(losses), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dspark_verify_workspace(B: int, gamma: int, V: int) -> int:
+    n = _sz(0)
+    _check(lib().dspark_verify_workspace(B, gamma, V, C.byref(n)))
+    return n.value
+
+
+def dspark_verify(target_logits, draft_logits, draft_tokens, seeds, accepted, next_token, *, lengths=None,
+                  offset: int = 0, accept_prob=None, ws=None, stream=None) -> None:
+    """accepted [B] and next_token [B] from target_logits [B, gamma+1, V],
+    draft_logits [B, gamma, V] and draft_tokens [B, gamma]."""
+    import torch
+    B, gamma, V = draft_logits.shape
+    if ws is None:
+        ws = torch.empty(dspark_verify_workspace(B, gamma, V), dtype=torch.uint8, device=draft_logits.device)
+    _check(lib().dspark_verify(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(lengths), _ptr(seeds), int(offset),
+        B, gamma, V, _ptr(accepted), _ptr(next_token), _ptr(accept_prob), _ptr(ws), ws.numel(),
+        _stream(stream)))

@@ -444,3 +444,36 @@ extern "C" dspark_status_t dspark_compute_loss(const float* draft, const float* 
   l.losses = losses;
   return hip_status(launch_loss_finish(l, stream), fn);
 }
+
+// ---------------------------------------------------------------------------
+extern "C" dspark_status_t dspark_verify_workspace(int64_t B, int64_t gamma, int64_t V, size_t* bytes) {
+  if (!bytes) return fail(DSPARK_EINVAL, "dspark_verify_workspace: bytes is NULL");
+  if (B <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "dspark_verify_workspace: sizes must be positive");
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "dspark_verify_workspace: gamma > %d", kMaxGamma);
+  if (B * (2 * gamma + 1) > kI32Max / 2) return fail(DSPARK_EINVAL, "dspark_verify_workspace: sizes too large");
+  *bytes = verify_ws_bytes(B, gamma, V);
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status_t dspark_verify(const float* target_logits, const float* draft_logits,
+                                         const int32_t* draft_tokens, const int32_t* lengths,
+                                         const uint64_t* seeds, uint64_t offset, int64_t B, int64_t gamma,
+                                         int64_t V, int32_t* accepted, int32_t* next_token, float* accept_prob,
+                                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "dspark_verify";
+  if (!target_logits || !draft_logits || !draft_tokens || !seeds || !accepted || !next_token)
+    return fail(DSPARK_EINVAL, "%s: target_logits, draft_logits, draft_tokens, seeds, accepted and next_token must be non-NULL", fn);
+  if (B <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "%s: B, gamma, V must be positive", fn);
+  if (V > kI32Max / 2 || B * (2 * gamma + 1) > kI32Max / 2) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
+  if (V % 4) return fail(DSPARK_EUNSUPPORTED, "%s: V %% 4 != 0", fn);
+  if (!aligned16(target_logits) || !aligned16(draft_logits))
+    return fail(DSPARK_EUNSUPPORTED, "%s: target_logits/draft_logits must be 16-byte aligned", fn);
+  const size_t need = verify_ws_bytes(B, gamma, V);
+  if (!ws || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+  return hip_status(launch_verify(target_logits, draft_logits, draft_tokens, lengths, seeds, offset,
+                                  static_cast<int>(B), static_cast<int>(gamma), static_cast<int>(V), accepted,
+                                  next_token, accept_prob, ws, stream),
+                    fn);
+}

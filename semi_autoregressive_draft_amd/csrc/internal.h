@@ -136,6 +136,13 @@ hipError_t launch_loss_finish(const LossArgs& a, hipStream_t s);
 hipError_t launch_block_logits(const float* U, const int32_t* prev, const void* A, const void* Bm, bool vec,
                                int M, int V, int r, float* out, hipStream_t s, bool bf16);
 
+// rejection-sampling verification
+int verify_chunks(int64_t rows, int64_t V);
+size_t verify_ws_bytes(int64_t B, int64_t G, int64_t V);
+hipError_t launch_verify(const float* target, const float* draft, const int32_t* tokens, const int32_t* lengths,
+                         const uint64_t* seeds, uint64_t offset, int B, int G, int V, int32_t* accepted,
+                         int32_t* next_token, float* accept_prob, void* ws, hipStream_t s);
+
 int overlap_tau_blocks(int64_t N);
 int overlap_split_chunks(int64_t rows, int64_t V);
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s);

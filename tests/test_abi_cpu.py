@@ -178,3 +178,21 @@ def test_block_logits_and_loss_validation(L):
     assert g(*largs(V=151934)) == bd.EUNSUPPORTED
     assert g(*largs(draft=MISALIGNED)) == bd.EUNSUPPORTED
     assert g(*largs()) == bd.EWORKSPACE
+
+
+def test_verify_validation(L):
+    st, n = _ws(L.dspark_verify_workspace, 256, 7, 151936)
+    assert st == bd.OK and n > 256 * 15 * 8
+    assert _ws(L.dspark_verify_workspace, 256, 17, 151936)[0] == bd.EUNSUPPORTED
+    f = L.dspark_verify
+    args = lambda **k: [k.get(n, d) for n, d in (
+        ("t", FAKE), ("d", FAKE), ("tok", FAKE), ("len", None), ("seeds", FAKE), ("off", 0), ("B", 4),
+        ("gamma", 7), ("V", 151936), ("acc", FAKE), ("nxt", FAKE), ("ap", None), ("ws", None), ("wsb", 0),
+        ("s", None))]
+    assert f(*args(seeds=None)) == bd.EINVAL
+    assert f(*args(nxt=None)) == bd.EINVAL
+    assert f(*args(gamma=0)) == bd.EINVAL
+    assert f(*args(gamma=17)) == bd.EUNSUPPORTED
+    assert f(*args(V=151934)) == bd.EUNSUPPORTED
+    assert f(*args(t=MISALIGNED)) == bd.EUNSUPPORTED
+    assert f(*args()) == bd.EWORKSPACE

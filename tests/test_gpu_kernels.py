@@ -532,3 +532,81 @@ def test_teacher_forced_block_logits_then_loss():
     d64 = o.teacher_forced_logits(U.astype(np.float64), prev, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"))
     want_per, want_losses = o.compute_loss(d64, teacher.astype(np.float64), ref, conf.astype(np.float64))
     _check_loss(per.cpu().numpy(), losses.cpu().numpy(), want_per, want_losses)
+
+
+# ----------------------------------------------------------------------------- K6
+DECISION_MARGIN = 1e-4      # log-domain margin below which fp32 and fp64 may decide differently
+
+
+def _verify_case(B, G, V, seed, sigma):
+    g = np.random.default_rng([seed, 41])
+    draft = g.standard_normal((B, G, V)).astype(np.float32)
+    target = np.concatenate([draft, g.standard_normal((B, 1, V)).astype(np.float32)], axis=1)
+    target += np.float32(sigma) * g.standard_normal((B, G + 1, V)).astype(np.float32)
+    # drafted tokens drawn from the draft distribution (numpy's generator)
+    toks = np.empty((B, G), dtype=np.int32)
+    for b in range(B):
+        for j in range(G):
+            p = np.exp(draft[b, j].astype(np.float64) - draft[b, j].max())
+            toks[b, j] = g.choice(V, p=p / p.sum())
+    return target, draft, toks
+
+
+def _run_verify(target, draft, toks, lengths, seeds, offset):
+    dev = require_gpu()
+    B, G, V = draft.shape
+    acc = torch.full((B,), -9, dtype=torch.int32, device=dev)
+    nxt = torch.full((B,), -9, dtype=torch.int32, device=dev)
+    ap = torch.full((B, G), float("nan"), dtype=torch.float32, device=dev)
+    bd.dspark_verify(to_dev(target), to_dev(draft), to_dev(toks), to_dev(seeds), acc, nxt,
+                     lengths=None if lengths is None else to_dev(lengths), offset=offset, accept_prob=ap)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), nxt.cpu().numpy(), ap.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,G,V,sigma,with_len", [
+    (1, 7, 5000, 0.3, False),      # one request: rows chunked over many workgroups
+    (6, 7, 4096, 1.0, True),       # scheduler-style lengths, including 0 and gamma
+    (40, 7, 3000, 0.5, True),
+    (300, 4, 2000, 2.0, False),    # many requests: few chunks per row
+    (3, 16, 1000, 0.1, True),      # longest block
+])
+def test_verify_parity(B, G, V, sigma, with_len):
+    target, draft, toks = _verify_case(B, G, V, seed=B + G, sigma=sigma)
+    g = np.random.default_rng([B, 43])
+    lengths = g.integers(0, G + 1, B).astype(np.int32) if with_len else None
+    if lengths is not None:
+        lengths[0], lengths[-1] = 0, G
+    seeds = (np.arange(B, dtype=np.uint64) * np.uint64(2654435761)) + np.uint64(17)
+    offset = 5
+    acc, nxt, ap = _run_verify(target, draft, toks, lengths, seeds, offset)
+    L = lengths if lengths is not None else np.full(B, G)
+    want = o.verify_draft(target, draft, toks, L, seeds, offset)
+    forced = want["accepted"].copy()
+    for b in range(B):
+        if acc[b] != want["accepted"][b]:
+            # only where the oracle's decision at the first differing position was a near-tie
+            k = min(acc[b], want["accepted"][b])
+            assert abs(want["margin"][b, k]) < DECISION_MARGIN, (b, acc[b], want["accepted"][b], want["margin"][b])
+            forced[b] = acc[b]
+    if (forced != want["accepted"]).any():
+        want = o.verify_draft(target, draft, toks, L, seeds, offset, forced=forced)
+    assert np.array_equal(acc, want["accepted"])
+    bad = (nxt != want["next_token"]) & (want["gap"] >= 1e-3)
+    assert not bad.any(), (np.nonzero(bad), nxt[bad], want["next_token"][bad], want["gap"][bad])
+    ok = want["accept_prob"] > 0
+    assert np.abs(ap[ok] - want["accept_prob"][ok]).max(initial=0.0) <= 1e-4
+    assert (ap[~ok] == 0).all()
+
+
+def test_verify_accepts_everything_when_draft_equals_target():
+    V, G, B = 2048, 7, 8
+    g = np.random.default_rng(47)
+    target = g.standard_normal((B, G + 1, V)).astype(np.float32)
+    draft = np.ascontiguousarray(target[:, :G])
+    toks = g.integers(0, V, (B, G)).astype(np.int32)
+    seeds = np.arange(B, dtype=np.uint64)
+    acc, nxt, ap = _run_verify(target, draft, toks, None, seeds, 0)
+    assert (acc == G).all()
+    want = o.verify_draft(target, draft, toks, np.full(B, G), seeds, 0)
+    assert np.array_equal(nxt, want["next_token"]) or (want["gap"] < 1e-3).all()
