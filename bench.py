@@ -158,6 +158,98 @@ def bench_prefix_schedule(dev, stream, R=256, gamma=7, calls=200, with_oracle=Tr
     return out
 
 
+def bench_teacher_forced_loss(dev, stream, N=512, gamma=7, V=151936, r=256, reps=10):
+    """Teacher-forced block logits plus the loss forward at one sequence's
+    offline-eval blocks (N anchors, block 7): mean time per call of each entry
+    point over back-to-back launches, and the HBM fraction of the pair against
+    its algorithmic bytes (U read and U~ written once, Bm and A rows once;
+    U~ and the teacher read once by the loss)."""
+    import numpy as np
+    import torch
+    import synth
+    from semi_autoregressive_draft_amd import binding as bd
+    M = N * gamma
+    g = torch.Generator(device=dev)
+    g.manual_seed(29)
+    U = torch.randn((N, gamma, V), generator=g, device=dev, dtype=torch.float32)
+    teacher = torch.randn((N, gamma, V), generator=g, device=dev, dtype=torch.float32).add_(U)
+    A = torch.from_numpy(synth.normal((V, r), 0.02, 0, synth.TID_A, "bf16").view("int16")).view(torch.bfloat16).to(dev)
+    Bm = torch.from_numpy(synth.normal((r, V), 0.02, 0, synth.TID_BM, "bf16").view("int16")).view(torch.bfloat16).to(dev)
+    prev = torch.randint(0, V, (N, gamma), generator=g, device=dev, dtype=torch.int32)
+    target = torch.randint(0, V, (N, gamma), generator=g, device=dev, dtype=torch.int32)
+    conf = torch.randn((N, gamma), generator=g, device=dev, dtype=torch.float32)
+    draft = torch.empty_like(U)
+    per = torch.empty((N, gamma, 4), dtype=torch.float32, device=dev)
+    losses = torch.empty((4,), dtype=torch.float64, device=dev)
+    ws = torch.zeros(bd.dspark_compute_loss_workspace(N, gamma, V), dtype=torch.uint8, device=dev)
+
+    def blk():
+        bd.dspark_apply_block_logits(U, prev, A, Bm, draft)
+
+    def loss():
+        bd.dspark_compute_loss(draft, teacher, target, losses, conf_logit=conf, per_pos=per, ws=ws)
+
+    out = {"blocks": N, "rows": M, "V": V, "r": r}
+    for name, fn in (("apply_block_logits", blk), ("compute_loss", loss)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+    blk_bytes = 8.0 * M * V + 2.0 * r * V + 2.0 * M * r
+    loss_bytes = 8.0 * M * V
+    out["apply_block_logits_GBps"] = round(blk_bytes / (out["apply_block_logits_ms"] * 1e-3) / 1e9, 1)
+    out["compute_loss_GBps"] = round(loss_bytes / (out["compute_loss_ms"] * 1e-3) / 1e9, 1)
+    tot_ms = out["apply_block_logits_ms"] + out["compute_loss_ms"]
+    out["hbm_frac"] = round((blk_bytes + loss_bytes) / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    out["bound"] = "hbm"
+    out["loss_total"] = round(float(losses[0].item()), 6)
+    del U, teacher, draft, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_verify(dev, stream, B=256, gamma=7, V=151936, reps=20):
+    """Rejection-sampling verification of B drafted blocks (serving shape):
+    mean time per call over back-to-back launches and the HBM fraction
+    against its algorithmic bytes (every needed target and draft row once)."""
+    import numpy as np
+    import torch
+    from semi_autoregressive_draft_amd import binding as bd
+    g = torch.Generator(device=dev)
+    g.manual_seed(31)
+    draft = torch.randn((B, gamma, V), generator=g, device=dev, dtype=torch.float32)
+    target = torch.randn((B, gamma + 1, V), generator=g, device=dev, dtype=torch.float32)
+    target[:, :gamma].mul_(0.5).add_(draft)
+    toks = torch.randint(0, V, (B, gamma), generator=g, device=dev, dtype=torch.int32)
+    seeds = torch.arange(B, dtype=torch.int64, device=dev).to(torch.uint64)
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = torch.empty(bd.dspark_verify_workspace(B, gamma, V), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        bd.dspark_verify(target, draft, toks, seeds, acc, nxt, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        bd.dspark_verify(target, draft, toks, seeds, acc, nxt, offset=i, ws=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    byt = 4.0 * B * (2 * gamma + 1) * V
+    out = {"B": B, "gamma": gamma, "V": V, "ms_per_call": round(ms, 4),
+           "GBps": round(byt / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "bound": "hbm", "mean_accepted": round(float(acc.float().mean().item()), 3)}
+    del draft, target, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +370,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, overlap)
     sched = bench_prefix_schedule(dev, stream, with_oracle=not args.no_cpu_baseline)
+    tfl = bench_teacher_forced_loss(dev, stream)
+    ver = bench_verify(dev, stream)
 
     out = {
         "metric": METRIC, "value": round(blocks_per_s, 2), "unit": "blocks/s", "n_gpus": 1,
@@ -294,7 +388,7 @@ def main():
         "stages_note": "lm_head from the timed region; the others from a separate pass with an event around every stage",
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
-        "next_rows": {"prefix_schedule": sched},
+        "next_rows": {"prefix_schedule": sched, "teacher_forced_loss": tfl, "verify": ver},
     }
     print(json.dumps(out), flush=True)
 

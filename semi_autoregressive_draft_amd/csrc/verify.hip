@@ -12,7 +12,8 @@
 // 1 is the position j < 16): acceptance uniform u_j from word 0 of counter
 // (0, 2^30 | j, offset), mapped as u = (floor(w / 2^9) + 1/2) 2^-23; Gumbel
 // noise for the final draw from word v mod 4 of counter (floor(v / 4),
-// 2^31 | n, offset).  Token j is accepted iff log u_j < min(0, log p_j(x_j) -
+// 2^31 | n, offset); the kernel takes the equivalent argmax of r(v) / E_v with
+// E_v = -log u_v the exponential variate behind G_v = -log E_v.  Token j is accepted iff log u_j < min(0, log p_j(x_j) -
 // log q_j(x_j)) (the same event as u_j < min(1, p/q)).  The final draw is
 // Gumbel-max over log r(v) + G_v with r = max(p_n - q_n, 0) after a rejection
 // (or r = p_n if that residual has no mass) and r = p_L otherwise.
@@ -23,8 +24,9 @@
 //  2. verify_decide: one wave per request folds the chunk states in a fixed
 //     order into the normalisers, takes the decisions in position order and
 //     stops at the first rejection;
-//  3. verify_sample: (chunk, request) workgroups compute the best Gumbel-max
-//     order key of the residual and of p_n over their chunk of row n;
+//  3. verify_sample: (chunk, request) workgroups, with finer chunks than pass 1
+//     (the pass is heavy in Philox and logarithm arithmetic), compute the best
+//     Gumbel-max order key of the residual and of p_n over their chunk of row n;
 //  4. verify_finish: one wave per request folds the keys into the next token.
 // All HBM traffic is in pass 1 (every needed row once) and pass 3 (one target
 // row and at most one draft row per request).
@@ -47,13 +49,14 @@ struct VerifyArgs {
   const uint64_t* seeds;     // [B]
   uint32_t off_lo, off_hi;
   int B, G, V;
-  int nchunk, chunk4;
+  int nchunk, chunk4;        // pass 1: chunks per row and float4 per chunk
+  int nchunk_s, chunk4_s;    // pass 3 (one row per request: finer chunks)
   int32_t* accepted;         // [B]
   int32_t* next_token;       // [B]
   float* accept_prob;        // [B][G] or NULL
   float* ws_state;           // [rows][nchunk][2]: target rows first, then draft rows
   float* ws_req;             // [B][4]: n, L_t(n), L_d(n), proposal length
-  unsigned long long* ws_key;  // [B][nchunk][2]: residual key, target key
+  unsigned long long* ws_key;  // [B][nchunk_s][2]: residual key, target key
 };
 
 __device__ __forceinline__ int proposal_len(const VerifyArgs& a, int b) {
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_sample(VerifyArgs a) {
   const f32x4* trow = reinterpret_cast<const f32x4*>(a.target + (static_cast<size_t>(b) * (a.G + 1) + n) * V);
   const f32x4* drow = reinterpret_cast<const f32x4*>(a.draft + (static_cast<size_t>(b) * a.G + (residual ? n : 0)) * V);
   const uint64_t sd = a.seeds[b];
-  const int e0 = c * a.chunk4, e1 = min(e0 + a.chunk4, a.V / 4);
+  const int e0 = c * a.chunk4_s, e1 = min(e0 + a.chunk4_s, a.V / 4);
   unsigned long long kr = 0ull, kt = 0ull;
   for (int e = e0 + tid; e < e1; e += kVerThreads) {
     const f32x4 t = trow[e];
@@ -172,18 +175,21 @@ __global__ __launch_bounds__(kVerThreads) void verify_sample(VerifyArgs a) {
     const uint32_t wd[4] = {ph.x, ph.y, ph.z, ph.w};
     f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
     if (residual) d = drow[e];
+    // argmax_v log r(v) + G_v with G = -log E, E = -log u, is argmax_v r(v) / E_v:
+    // one logarithm per element instead of three (a probability that
+    // underflows float32 cannot win: G stays below 16.7 for this u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float g = gumbel_from_word(wd[i]);
-      const float lp = t[i] - Lt;
-      const unsigned long long k2 = best_key(lp + g, 4 * e + i);
+      const float u = (static_cast<float>(wd[i] >> 9) + 0.5f) * 0x1p-23f;
+      const float E = (u >= 0.5f) ? -log1pf(u - 1.0f) : -logf(u);
+      const float inv = 1.0f / E;
+      const float p = __expf(t[i] - Lt);
+      const unsigned long long k2 = best_key(p * inv, 4 * e + i);
       kt = k2 > kt ? k2 : kt;
       if (residual) {
-        const float r = __expf(lp) - __expf(d[i] - Ld);
-        if (r > 0.f) {
-          const unsigned long long k1 = best_key(logf(r) + g, 4 * e + i);
-          kr = k1 > kr ? k1 : kr;
-        }
+        const float r = p - __expf(d[i] - Ld);
+        const unsigned long long k1 = r > 0.f ? best_key(r * inv, 4 * e + i) : 0ull;
+        kr = k1 > kr ? k1 : kr;
       }
     }
   }
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_sample(VerifyArgs a) {
       kr = red[i][0] > kr ? red[i][0] : kr;
       kt = red[i][1] > kt ? red[i][1] : kt;
     }
-    unsigned long long* o = a.ws_key + (static_cast<size_t>(b) * a.nchunk + c) * 2;
+    unsigned long long* o = a.ws_key + (static_cast<size_t>(b) * a.nchunk_s + c) * 2;
     o[0] = kr;
     o[1] = kt;
   }
@@ -214,8 +220,8 @@ __global__ __launch_bounds__(kVerThreads) void verify_sample(VerifyArgs a) {
 __global__ __launch_bounds__(kWave) void verify_finish(VerifyArgs a) {
   const int b = blockIdx.x, lane = threadIdx.x;
   unsigned long long kr = 0ull, kt = 0ull;
-  const unsigned long long* k = a.ws_key + static_cast<size_t>(b) * a.nchunk * 2;
-  for (int c = lane; c < a.nchunk; c += kWave) {
+  const unsigned long long* k = a.ws_key + static_cast<size_t>(b) * a.nchunk_s * 2;
+  for (int c = lane; c < a.nchunk_s; c += kWave) {
     kr = k[2 * c] > kr ? k[2 * c] : kr;
     kt = k[2 * c + 1] > kt ? k[2 * c + 1] : kt;
   }
@@ -228,19 +234,26 @@ __global__ __launch_bounds__(kWave) void verify_finish(VerifyArgs a) {
   if (lane == 0) a.next_token[b] = best_index(kr != 0ull ? kr : kt);
 }
 
-size_t verify_ws_bytes(int64_t B, int64_t G, int64_t V) {
-  const int64_t rows = B * (2 * G + 1);
-  const int nchunk = verify_chunks(rows, V);
-  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  return al(static_cast<size_t>(rows) * nchunk * 2 * 4) + al(static_cast<size_t>(B) * 16) +
-         al(static_cast<size_t>(B) * nchunk * 16);
-}
-
-int verify_chunks(int64_t rows, int64_t V) {
+// chunks per row: at most one per kVerChunk elements, and no more than it
+// takes for `target` workgroups over all rows
+static int chunks_for(int64_t rows, int64_t V, int64_t target) {
   const int64_t by_size = (V + kVerChunk - 1) / kVerChunk;
-  const int64_t by_rows = (4096 + rows - 1) / rows;
+  const int64_t by_rows = (target + rows - 1) / rows;
   const int64_t n = by_size < by_rows ? by_size : by_rows;
   return static_cast<int>(n < 1 ? 1 : n);
+}
+
+// pass 1 streams every needed row; pass 3 one row per request, with the
+// Philox and Gumbel arithmetic per element, so it is split more finely
+int verify_chunks(int64_t rows, int64_t V) { return chunks_for(rows, V, 4096); }
+static int verify_chunks_sample(int64_t B, int64_t V) { return chunks_for(B, V, 8192); }
+
+size_t verify_ws_bytes(int64_t B, int64_t G, int64_t V) {
+  const int64_t rows = B * (2 * G + 1);
+  const int nchunk = verify_chunks(rows, V), nchunk_s = verify_chunks_sample(B, V);
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  return al(static_cast<size_t>(rows) * nchunk * 2 * 4) + al(static_cast<size_t>(B) * 16) +
+         al(static_cast<size_t>(B) * nchunk_s * 16);
 }
 
 hipError_t launch_verify(const float* target, const float* draft, const int32_t* tokens, const int32_t* lengths,
@@ -260,6 +273,8 @@ hipError_t launch_verify(const float* target, const float* draft, const int32_t*
   const int64_t rows = static_cast<int64_t>(B) * (2 * G + 1);
   a.nchunk = verify_chunks(rows, V);
   a.chunk4 = (V / 4 + a.nchunk - 1) / a.nchunk;
+  a.nchunk_s = verify_chunks_sample(B, V);
+  a.chunk4_s = (V / 4 + a.nchunk_s - 1) / a.nchunk_s;
   a.accepted = accepted;
   a.next_token = next_token;
   a.accept_prob = accept_prob;
@@ -272,7 +287,7 @@ hipError_t launch_verify(const float* target, const float* draft, const int32_t*
   a.ws_key = reinterpret_cast<unsigned long long*>(p);
   hipLaunchKernelGGL(verify_stats, dim3(a.nchunk, static_cast<unsigned>(rows)), dim3(kVerThreads), 0, s, a);
   hipLaunchKernelGGL(verify_decide, dim3(B), dim3(kWave), 0, s, a);
-  hipLaunchKernelGGL(verify_sample, dim3(a.nchunk, B), dim3(kVerThreads), 0, s, a);
+  hipLaunchKernelGGL(verify_sample, dim3(a.nchunk_s, B), dim3(kVerThreads), 0, s, a);
   hipLaunchKernelGGL(verify_finish, dim3(B), dim3(kWave), 0, s, a);
   return hipGetLastError();
 }
