@@ -314,11 +314,7 @@ def main():
     t_wall = time.perf_counter()
     for s in range(K):
         ev_step[s].record(stream)
-        path.lm_head()
-        ev_lm[s].record(stream)
-        path.propose()
-        path.confidence()
-        path.overlap_tau()
+        path.run(stream, lm_done=ev_lm[s])
     ev_step[K].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall

@@ -5,6 +5,8 @@ allocated once up front:
   dspark_lm_head -> dspark_markov_propose -> dspark_confidence_survival
   -> dspark_overlap_tau (against a teacher; dense over U~, or over the top-k
   candidate distribution when topk > 0)
+(Issuing the hidden-only confidence head on a second stream, beside the LM
+head, measured slower: the cross-stream events cost more than the kernel.)
 """
 from __future__ import annotations
 
@@ -79,9 +81,14 @@ class DraftPath:
                                   cand_prob=self.topk_prob, accept_rate_at=self.accept_rate,
                                   tau_mean=self.tau_mean, ws=self.ws_overlap, stream=stream)
 
-    def run(self, stream=None):
-        self.lm_head(stream)
-        self.propose(stream)
-        self.confidence(stream)
+    def run(self, stream=None, lm_done=None):
+        """One pass; lm_done (optional event) is recorded right after the
+        LM-head launch."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        self.lm_head(main)
+        if lm_done is not None:
+            lm_done.record(main)
+        self.propose(main)
+        self.confidence(main)
         if self.overlap:
-            self.overlap_tau(stream)
+            self.overlap_tau(main)
