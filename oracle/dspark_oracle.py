@@ -135,6 +135,41 @@ def gumbel(seed: int, offset: int, j: int, V: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Sequential-head variants.  [P4] §2.3 heads table: VanillaMarkov
+# b_j = W_up SiLU(W_down[x_{j-1}]); GatedMarkovHead g_j = sigma(W_g [h_j;
+# W_down[x_{j-1}]]), b_j = W_up (g_j * W_down[x_{j-1}]).  With A = W_down and
+# Bm = W_up^T, each variant changes only the r-vector m_j that the
+# up-projection receives; 'linear' is the reading used by the main chain
+# ([P1] b_i = W_2 m_i).  A module computing in the tables' dtype hands the
+# up-projection m_j rounded to that dtype, so the variants round it (bf16:
+# to nearest, ties to even, through float32).
+
+
+def round_to_dtype(x: np.ndarray, wdtype: str) -> np.ndarray:
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if wdtype != "bf16":
+        return x32.astype(np.float64)
+    u = x32.view(np.uint32).astype(np.uint64)
+    r = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def head_vector(head: str, a_row: np.ndarray, *, h_row: Optional[np.ndarray] = None,
+                W_g: Optional[np.ndarray] = None, wdtype: str = "bf16") -> np.ndarray:
+    """m_j for A[x_{j-1}] = a_row (and h_j, W_g [r, H + r] for the gated head)."""
+    if head == "linear":
+        return a_row
+    if head == "silu":
+        v = a_row / (1.0 + np.exp(-a_row))
+    elif head == "gated":
+        z = W_g @ np.concatenate([h_row, a_row])
+        v = a_row / (1.0 + np.exp(-z))
+    else:
+        raise ValueError(head)
+    return round_to_dtype(v, wdtype)
+
+
+# --------------------------------------------------------------------------
 # S2-S4: the sequential Vanilla-Markov stage.
 # [P1] Markov 顺序修正: m_i = W_1[t_{i-1}] (t_0 = anchor), b_i = W_2 m_i,
 # l_i = l_i^0 + b_i, q_i = softmax(l_i); inference selects t_i from l_i and
@@ -144,13 +179,16 @@ def gumbel(seed: int, offset: int, j: int, V: int) -> np.ndarray:
 def markov_chain(U: np.ndarray, anchor: np.ndarray, A: np.ndarray, Bm: np.ndarray, *,
                  temperature: float = 0.0, seeds: Optional[np.ndarray] = None,
                  offset: int = 0, topk: int = 0, forced: Optional[np.ndarray] = None,
-                 keep_logits: bool = False) -> dict:
+                 keep_logits: bool = False, head: str = "linear", h: Optional[np.ndarray] = None,
+                 W_g: Optional[np.ndarray] = None, wdtype: str = "bf16") -> dict:
     """Run the chain for every request.
 
     U [B, gamma, V] base logits; anchor [B]; A [V, r]; Bm [r, V] (all float64).
     temperature 0 selects greedily; otherwise token = argmax(U~/T + G).
     ``forced`` [B, gamma] (int, -1 = free) overrides the selected token at a
     position (used to continue a chain along another valid choice).
+    ``head`` selects the sequential head (see ``head_vector``; h [B, gamma, H]
+    and W_g for 'gated'; wdtype the tables' dtype for the rounding of m_j).
 
     Returns tokens [B,gamma], tok_logit (U~ at the token), lse (log-sum-exp of
     U~), gap (best minus second-best of the selection score), score_max and
@@ -171,7 +209,8 @@ def markov_chain(U: np.ndarray, anchor: np.ndarray, A: np.ndarray, Bm: np.ndarra
     for b in range(B):
         prev = int(anchor[b])
         for j in range(gamma):
-            ut = U[b, j] + A[prev] @ Bm                     # U~_j = U_j + W_2 W_1[prev]
+            m = head_vector(head, A[prev], h_row=None if h is None else h[b, j], W_g=W_g, wdtype=wdtype)
+            ut = U[b, j] + m @ Bm                           # U~_j = U_j + W_2 m_j
             mx = ut.max()
             out["lse"][b, j] = mx + math.log(np.exp(ut - mx).sum())
             if temperature == 0.0:
@@ -209,11 +248,17 @@ def topk_indices(x: np.ndarray, k: int) -> np.ndarray:
 
 
 def teacher_forced_logits(U: np.ndarray, prev_tokens: np.ndarray, A: np.ndarray,
-                          Bm: np.ndarray) -> np.ndarray:
+                          Bm: np.ndarray, head: str = "linear", h: Optional[np.ndarray] = None,
+                          W_g: Optional[np.ndarray] = None, wdtype: str = "bf16") -> np.ndarray:
     """All positions at once from known previous tokens ([P4] §2.3: training
     applies the Markov bias to the whole block in one batched step).
     prev_tokens [B, gamma] = [anchor, t_0, ..., t_{gamma-2}]."""
-    return U + np.einsum("bjr,rv->bjv", A[prev_tokens], Bm)
+    if head == "linear":
+        return U + np.einsum("bjr,rv->bjv", A[prev_tokens], Bm)
+    B, gamma = prev_tokens.shape
+    M = np.stack([np.stack([head_vector(head, A[prev_tokens[b, j]], h_row=None if h is None else h[b, j],
+                                        W_g=W_g, wdtype=wdtype) for j in range(gamma)]) for b in range(B)])
+    return U + np.einsum("bjr,rv->bjv", M, Bm)
 
 
 # --------------------------------------------------------------------------
