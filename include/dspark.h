@@ -155,6 +155,43 @@ dspark_status_t dspark_markov_propose(const float* U, int64_t B, int64_t gamma, 
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Sequential-head variants of dspark_markov_propose.  [P4] §2.3 heads table:
+ *   DSPARK_HEAD_SILU  (VanillaMarkov): b_j = W_up SiLU(W_down[x_{j-1}]),
+ *   DSPARK_HEAD_GATED (GatedMarkovHead): g_j = sigmoid(W_g [h_j; W_down[x_{j-1}]]),
+ *                     b_j = W_up (g_j * W_down[x_{j-1}]),
+ * with W_down = A [V, r] and W_up = Bm^T; DSPARK_HEAD_LINEAR is
+ * dspark_markov_propose itself.  The r-vector the up-projection receives is
+ * rounded to the tables' dtype (bf16: to nearest, ties to even), as a module
+ * computing in that dtype hands it on.  The variants run one step per position
+ * (no resident chain); every other argument, output and rule is that of
+ * dspark_markov_propose.
+ *
+ *   head   DSPARK_HEAD_LINEAR (0), DSPARK_HEAD_SILU (1) or DSPARK_HEAD_GATED (2)
+ *   h      [B, gamma, H] dtype wdt   hidden state h_j of each position (gated only)
+ *   W_g    [r, H + r] dtype wdt      gate weights over [h_j; A[x_{j-1}]] (gated only)
+ *   ws     at least dspark_markov_propose_head_workspace bytes, zero-filled
+ *          before its first use
+ * Requirements: those of dspark_markov_propose; gated: h, W_g non-NULL,
+ * 0 < H <= 16384.
+ */
+#define DSPARK_HEAD_LINEAR 0
+#define DSPARK_HEAD_SILU 1
+#define DSPARK_HEAD_GATED 2
+
+dspark_status_t dspark_markov_propose_head_workspace(int32_t head, int64_t B, int64_t gamma, int64_t V,
+                                                     int64_t r, dspark_dtype_t wdt, int32_t topk,
+                                                     size_t* bytes);
+
+dspark_status_t dspark_markov_propose_head(int32_t head, const void* h, int64_t H, const void* W_g,
+                                           const float* U, int64_t B, int64_t gamma, int64_t V,
+                                           const int32_t* anchor, const void* A, const void* Bm,
+                                           dspark_dtype_t wdt, int64_t r, float temperature,
+                                           const uint64_t* seeds, uint64_t offset, int32_t topk,
+                                           int32_t* tokens, float* tok_logit, float* lse,
+                                           int32_t* topk_idx, float* topk_prob, float* logits_out,
+                                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * S5 -- confidence head and prefix survival.  [P1] Confidence head:
  * s_i = w_c^T [h_i; m_i] + b_c, a^_i = sigmoid(s_i), m_i = W_1[t_{i-1}];
  * [P5] §4.3 predict_confidence_step(block_hidden) (hidden states only);

@@ -41,6 +41,11 @@ _SIGNATURES = {
     "dspark_compute_loss": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _f32, _f32, _f32,
                                       _i32, _vp, _vp, _vp, _sz, _vp]),
     "dspark_verify_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
+    "dspark_markov_propose_head_workspace": (C.c_int, [_i32, _i64, _i64, _i64, _i64, C.c_int, _i32,
+                                                       C.POINTER(_sz)]),
+    "dspark_markov_propose_head": (C.c_int, [_i32, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                             C.c_int, _i64, _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp,
+                                             _vp, _vp, _sz, _vp]),
     "dspark_verify": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _u64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
@@ -235,3 +240,30 @@ def dspark_verify(target_logits, draft_logits, draft_tokens, seeds, accepted, ne
         _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(lengths), _ptr(seeds), int(offset),
         B, gamma, V, _ptr(accepted), _ptr(next_token), _ptr(accept_prob), _ptr(ws), ws.numel(),
         _stream(stream)))
+
+
+HEAD_LINEAR, HEAD_SILU, HEAD_GATED = 0, 1, 2
+
+
+def dspark_markov_propose_head_workspace(head: int, B: int, gamma: int, V: int, r: int, wdtype: int = BF16,
+                                         topk: int = 0) -> int:
+    n = _sz(0)
+    _check(lib().dspark_markov_propose_head_workspace(head, B, gamma, V, r, wdtype, topk, C.byref(n)))
+    return n.value
+
+
+def dspark_markov_propose_head(head: int, U, anchor, A, Bm, tokens, *, h=None, W_g=None, temperature: float = 0.0,
+                               seeds=None, offset: int = 0, topk: int = 0, tok_logit=None, lse=None,
+                               topk_idx=None, topk_prob=None, logits_out=None, ws=None, stream=None) -> None:
+    """dspark_markov_propose with a sequential-head variant (HEAD_SILU, HEAD_GATED)."""
+    import torch
+    B, gamma, V = U.shape
+    r = A.shape[1]
+    H = h.shape[-1] if h is not None else 0
+    if ws is None:
+        ws = torch.zeros(dspark_markov_propose_head_workspace(head, B, gamma, V, r, _dtype(A), topk),
+                         dtype=torch.uint8, device=U.device)
+    _check(lib().dspark_markov_propose_head(
+        head, _ptr(h), H, _ptr(W_g), _ptr(U), B, gamma, V, _ptr(anchor), _ptr(A), _ptr(Bm), _dtype(A), r,
+        float(temperature), _ptr(seeds), int(offset), int(topk), _ptr(tokens), _ptr(tok_logit), _ptr(lse),
+        _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))

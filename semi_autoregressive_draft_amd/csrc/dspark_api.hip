@@ -164,13 +164,18 @@ extern "C" dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int6
   return DSPARK_OK;
 }
 
-extern "C" dspark_status_t dspark_markov_propose(
+// head vectors of the sequential-head variants, after the chain's workspace
+size_t head_table_bytes(int head, int64_t B, int64_t gamma, int64_t r, bool bf16) {
+  return head == kHeadLinear ? 0 : align_up(static_cast<size_t>(B) * gamma * r * (bf16 ? 2 : 4));
+}
+
+dspark_status_t propose_impl(
+    const char* fn, int head_kind, const void* h, int64_t H, const void* Wg,
     const float* U, int64_t B, int64_t gamma, int64_t V, const int32_t* anchor, const void* A,
     const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
     uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
     int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
     hipStream_t stream) {
-  const char* fn = "dspark_markov_propose";
   if (!U || !anchor || !A || !Bm || !tokens)
     return fail(DSPARK_EINVAL, "%s: U, anchor, A, Bm and tokens must be non-NULL", fn);
   if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0)
@@ -197,7 +202,7 @@ extern "C" dspark_status_t dspark_markov_propose(
     if (!aligned16(U) || !aligned16(A) || !aligned16(Bm) || (logits_out && !aligned16(logits_out)))
       return fail(DSPARK_EUNSUPPORTED, "%s: U, A, Bm, logits_out must be 16-byte aligned", fn);
   }
-  const size_t need = markov_ws_bytes(B, gamma, V, topk);
+  const size_t need = markov_ws_bytes(B, gamma, V, topk) + head_table_bytes(head_kind, B, gamma, r, bf16);
   if (!ws || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
 
@@ -238,7 +243,10 @@ extern "C" dspark_status_t dspark_markov_propose(
   a.topk_prob = topk_prob;
   int nwg = 0;
   size_t lds = 0;
-  const bool resident = resident_chain(bf16, a.B, a.V, a.r, &nwg, &lds);
+  // the head variants run per position: the prep kernel writes m_j between positions
+  const bool resident = head_kind == kHeadLinear && resident_chain(bf16, a.B, a.V, a.r, &nwg, &lds);
+  void* mtab = head_kind == kHeadLinear ? nullptr : static_cast<char*>(ws) + markov_ws_bytes(B, gamma, V, topk);
+  a.Mrow = mtab;
   a.tile_cols = resident ? 64 : markov_tile_cols(bf16, a.sample, a.B, a.r, a.V);
   a.resident = resident;
   a.nlist = nwg;
@@ -254,11 +262,55 @@ extern "C" dspark_status_t dspark_markov_propose(
   } else {
     for (int j = 0; j < gamma && e == hipSuccess; ++j) {
       a.j = j;
-      e = launch_markov_position(a, bf16, stream);
+      if (mtab) e = launch_head_prep(a, bf16, head_kind, h, static_cast<int>(H), Wg, mtab, stream);
+      if (e == hipSuccess) e = launch_markov_position(a, bf16, stream);
     }
   }
   if (e == hipSuccess) e = launch_markov_finish(a, bf16, stream);
   return hip_status(e, fn);
+}
+
+extern "C" dspark_status_t dspark_markov_propose(
+    const float* U, int64_t B, int64_t gamma, int64_t V, const int32_t* anchor, const void* A,
+    const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
+    uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
+    int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
+    hipStream_t stream) {
+  return propose_impl("dspark_markov_propose", kHeadLinear, nullptr, 0, nullptr, U, B, gamma, V, anchor, A, Bm,
+                      wdt, r, temperature, seeds, offset, topk, tokens, tok_logit, lse, topk_idx, topk_prob,
+                      logits_out, ws, ws_bytes, stream);
+}
+
+extern "C" dspark_status_t dspark_markov_propose_head_workspace(int32_t head, int64_t B, int64_t gamma, int64_t V,
+                                                                int64_t r, dspark_dtype_t wdt, int32_t topk,
+                                                                size_t* bytes) {
+  const char* fn = "dspark_markov_propose_head_workspace";
+  if (!bytes) return fail(DSPARK_EINVAL, "%s: bytes is NULL", fn);
+  if (head != kHeadLinear && head != kHeadSilu && head != kHeadGated)
+    return fail(DSPARK_EINVAL, "%s: unknown head %d", fn, head);
+  if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0 || topk < 0)
+    return fail(DSPARK_EINVAL, "%s: B, gamma, V, r must be positive, topk >= 0", fn);
+  if (V > kI32Max || B > kI32Max / 16 || r > kMaxRank) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  *bytes = markov_ws_bytes(B, gamma, V, topk) + head_table_bytes(head, B, gamma, r, wdt == DSPARK_BF16);
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status_t dspark_markov_propose_head(
+    int32_t head, const void* h, int64_t H, const void* W_g,
+    const float* U, int64_t B, int64_t gamma, int64_t V, const int32_t* anchor, const void* A,
+    const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
+    uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
+    int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
+    hipStream_t stream) {
+  const char* fn = "dspark_markov_propose_head";
+  if (head != kHeadLinear && head != kHeadSilu && head != kHeadGated)
+    return fail(DSPARK_EINVAL, "%s: unknown head %d", fn, head);
+  if (head == kHeadGated) {
+    if (!h || !W_g || H <= 0) return fail(DSPARK_EINVAL, "%s: the gated head needs h, W_g and H > 0", fn);
+    if (H > kMaxHeadHidden) return fail(DSPARK_EUNSUPPORTED, "%s: H > %d", fn, kMaxHeadHidden);
+  }
+  return propose_impl(fn, head, h, H, W_g, U, B, gamma, V, anchor, A, Bm, wdt, r, temperature, seeds, offset, topk,
+                      tokens, tok_logit, lse, topk_idx, topk_prob, logits_out, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

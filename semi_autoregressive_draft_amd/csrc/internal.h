@@ -33,6 +33,7 @@ struct StepArgs {
   unsigned long long* best;
   unsigned* sync;          // [kSyncWords] counters, flags and group keys of the resident chain
   unsigned epoch;          // number of this call (marks a timed-out resident chain)
+  const void* Mrow;        // head vectors [B][gamma][r] (dtype of A) or NULL: rows of A by previous token
   int tile_cols;           // vocabulary columns per partial (64 resident, 128 narrow bf16, a multiple of 64 wide bf16, 256 f32)
   int resident;            // 1: the chain ran as the resident kernel
   // resident chain with top-k: each workgroup's k largest order keys of U~_j
@@ -135,6 +136,12 @@ struct LossArgs {
 hipError_t launch_loss_finish(const LossArgs& a, hipStream_t s);
 hipError_t launch_block_logits(const float* U, const int32_t* prev, const void* A, const void* Bm, bool vec,
                                int M, int V, int r, float* out, hipStream_t s, bool bf16);
+
+// sequential-head variants (markov_head_prep writes m_j before each position)
+constexpr int kHeadLinear = 0, kHeadSilu = 1, kHeadGated = 2;
+constexpr int kMaxHeadHidden = 16384;   // H of the gated head (h_j and A[x] in LDS)
+hipError_t launch_head_prep(const StepArgs& a, bool bf16, int head, const void* h, int H, const void* Wg, void* M,
+                            hipStream_t s);
 
 // rejection-sampling verification
 int verify_chunks(int64_t rows, int64_t V);

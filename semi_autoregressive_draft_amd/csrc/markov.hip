@@ -222,8 +222,7 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
   for (int rg = 0; rg < RG; ++rg) {
     const int b = req0 + 16 * rg + n;
     bok[rg] = b < a.B;
-    const int prev = bok[rg] ? prev_token(a, b, a.j) : 0;
-    arow[rg] = A + static_cast<size_t>(prev) * a.r;
+    arow[rg] = bok[rg] ? a_operand_row<uint16_t>(a, b, a.j) : A;
   }
 
   f32x4 acc[RG][8];
@@ -398,7 +397,7 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
   u32x4 av[NCH];
   {
     const int b = min(req0 + n, a.B - 1);
-    const uint16_t* arow = A + static_cast<size_t>(prev_token(a, b, a.j)) * a.r + 8 * g;
+    const uint16_t* arow = a_operand_row<uint16_t>(a, b, a.j) + 8 * g;
 #pragma unroll
     for (int q = 0; q < NCH; ++q) av[q] = *reinterpret_cast<const u32x4*>(arow + 32 * q);
   }
@@ -559,10 +558,9 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
   __shared__ ArgState red_a[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int tile = blockIdx.x, b = blockIdx.y;
-  const float* A = static_cast<const float*>(a.A);
   const float* Bm = static_cast<const float*>(a.Bm);
-  const int prev = prev_token(a, b, a.j);
-  for (int k = tid; k < a.r; k += 256) arow[k] = A[static_cast<size_t>(prev) * a.r + k];
+  const float* ar = a_operand_row<float>(a, b, a.j);
+  for (int k = tid; k < a.r; k += 256) arow[k] = ar[k];
   __syncthreads();
 
   const int v = tile * kMarkovTileF32 + tid;
@@ -728,9 +726,8 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
   __shared__ float selv[kMaxTopk];
   __shared__ int seli[kMaxTopk];
 
-  const int prev = prev_token(a, b, j);
-  const WT* A = static_cast<const WT*>(a.A);
-  for (int i = tid; i < a.r; i += kTopkThreads) arow_s[i] = to_f32(A[static_cast<size_t>(prev) * a.r + i]);
+  const WT* ar = a_operand_row<WT>(a, b, j);
+  for (int i = tid; i < a.r; i += kTopkThreads) arow_s[i] = to_f32(ar[i]);
   const float* pm = a.p_m + row * a.P;
   const float* sm = a.segmax + row * a.S;
   const float* urow = a.U + row * static_cast<size_t>(a.V);

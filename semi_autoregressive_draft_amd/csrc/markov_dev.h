@@ -64,4 +64,13 @@ __device__ __forceinline__ int prev_token(const StepArgs& a, int b, int j) {
   return j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + j - 1];
 }
 
+// The A-operand row of (request b, position j): row x_{j-1} of A, or, with a
+// sequential-head variant, row b * gamma + j of the head vectors m_j that the
+// prep kernel wrote (a.Mrow, same dtype as A).
+template <typename T>
+__device__ __forceinline__ const T* a_operand_row(const StepArgs& a, int b, int j) {
+  if (a.Mrow) return static_cast<const T*>(a.Mrow) + (static_cast<size_t>(b) * a.gamma + j) * a.r;
+  return static_cast<const T*>(a.A) + static_cast<size_t>(prev_token(a, b, j)) * a.r;
+}
+
 }  // namespace dspark

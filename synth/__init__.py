@@ -21,7 +21,7 @@ import numpy as np
 
 # tensor ids of the per-tensor generators
 TID_H, TID_WLM, TID_A, TID_BM, TID_ANCHOR, TID_TEACHER, TID_WC, TID_VALID, \
-    TID_DRAFT, TID_U, TID_WM, TID_CAND, TID_SURV = range(13)
+    TID_DRAFT, TID_U, TID_WM, TID_CAND, TID_SURV, TID_WG = range(14)
 
 GAMMA = 7
 QWEN_H = 2560

@@ -52,7 +52,7 @@ def tight_check(got, want, scale, what=""):
 
 
 def check_chain(gpu: dict, U, anchor, A, Bm, *, temperature=0.0, seeds=None, offset=0, topk=0,
-                reqs=None, check_logits=True):
+                reqs=None, check_logits=True, oracle_kw=None):
     """Compare the GPU chain outputs (numpy dict: tokens, tok_logit, lse, and
     optionally topk_idx/topk_prob/logits) with the oracle for requests ``reqs``.
     U/A/Bm are float64.  Returns the number of near-tie divergences."""
@@ -63,6 +63,8 @@ def check_chain(gpu: dict, U, anchor, A, Bm, *, temperature=0.0, seeds=None, off
         forced = -np.ones((1, gamma), dtype=np.int64)
         kw = dict(temperature=temperature, seeds=None if seeds is None else seeds[b:b + 1],
                   offset=offset, topk=topk, keep_logits=True)
+        if oracle_kw:
+            kw.update({k: (v[b:b + 1] if k == "h" else v) for k, v in oracle_kw.items()})
         ref = o.markov_chain(U[b:b + 1], anchor[b:b + 1], A, Bm, **kw)
         for j in range(gamma):
             gt = int(gpu["tokens"][b, j])

@@ -196,3 +196,24 @@ def test_verify_validation(L):
     assert f(*args(V=151934)) == bd.EUNSUPPORTED
     assert f(*args(t=MISALIGNED)) == bd.EUNSUPPORTED
     assert f(*args()) == bd.EWORKSPACE
+
+
+
+def test_head_variant_validation(L):
+    st, n = _ws(L.dspark_markov_propose_head_workspace, 1, 4, 7, 151936, 256, bd.BF16, 16)
+    st0, n0 = _ws(L.dspark_markov_propose_workspace, 4, 7, 151936, 16)
+    assert st == bd.OK and st0 == bd.OK and n >= n0 + 4 * 7 * 256 * 2
+    assert _ws(L.dspark_markov_propose_head_workspace, 0, 4, 7, 151936, 256, bd.BF16, 16)[1] == n0
+    assert _ws(L.dspark_markov_propose_head_workspace, 3, 4, 7, 151936, 256, bd.BF16, 16)[0] == bd.EINVAL
+    f = L.dspark_markov_propose_head
+    args = lambda **k: [k.get(n, d) for n, d in (
+        ("head", 2), ("h", FAKE), ("H", 2560), ("Wg", FAKE), ("U", FAKE), ("B", 4), ("gamma", 7),
+        ("V", 151936), ("anchor", FAKE), ("A", FAKE), ("Bm", FAKE), ("dt", bd.BF16), ("r", 256),
+        ("T", 0.0), ("seeds", None), ("off", 0), ("topk", 0), ("tok", FAKE), ("tl", None), ("lse", None),
+        ("ti", None), ("tp", None), ("lo", None), ("ws", None), ("wsb", 0), ("s", None))]
+    assert f(*args(head=5)) == bd.EINVAL
+    assert f(*args(h=None)) == bd.EINVAL
+    assert f(*args(Wg=None)) == bd.EINVAL
+    assert f(*args(H=16385)) == bd.EUNSUPPORTED
+    assert f(*args()) == bd.EWORKSPACE
+    assert f(*args(head=1, h=None, Wg=None, H=0)) == bd.EWORKSPACE     # SiLU needs no h

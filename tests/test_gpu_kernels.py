@@ -610,3 +610,42 @@ def test_verify_accepts_everything_when_draft_equals_target():
     assert (acc == G).all()
     want = o.verify_draft(target, draft, toks, np.full(B, G), seeds, 0)
     assert np.array_equal(nxt, want["next_token"]) or (want["gap"] < 1e-3).all()
+
+
+# ----------------------------------------------------------------------------- sequential-head variants
+@pytest.mark.parametrize("head,B,V,r,wdtype,T,topk", [
+    ("silu", 1, 4000, 256, "bf16", 0.0, 16),     # narrow step (r split over waves), top-16
+    ("silu", 40, 3000, 256, "bf16", 1.0, 0),     # wide step, sampled
+    ("gated", 5, 3000, 128, "bf16", 0.0, 8),
+    ("gated", 33, 2008, 64, "bf16", 0.7, 16),    # wide step, sampled, top-16, ragged tile
+    ("gated", 3, 1000, 48, "f32", 0.0, 5),       # float32 tables
+    ("silu", 2, 1000, 32, "f32", 1.0, 0),
+])
+def test_markov_head_variants_parity(head, B, V, r, wdtype, T, topk):
+    dev = require_gpu()
+    gamma, H, seed = 7, 96, 29
+    U, anchor, A, Bm = _markov_case(B, V, r, wdtype, seed=seed)
+    h = synth.normal((B, gamma, H), 1.0, seed, synth.TID_H, wdtype)
+    W_g = synth.normal((r, H + r), 0.1, seed, synth.TID_WG, wdtype)
+    seeds = np.arange(B, dtype=np.uint64) + np.uint64(11) if T > 0 else None
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    tl = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    ls = torch.empty_like(tl)
+    ti = torch.empty((B, gamma, topk), dtype=torch.int32, device=dev) if topk else None
+    tp = torch.empty((B, gamma, topk), dtype=torch.float32, device=dev) if topk else None
+    lo = torch.empty((B, gamma, V), dtype=torch.float32, device=dev)
+    code = bd.HEAD_SILU if head == "silu" else bd.HEAD_GATED
+    bd.dspark_markov_propose_head(code, to_dev(U), to_dev(anchor), to_dev(A, wdtype), to_dev(Bm, wdtype), tokens,
+                                  h=to_dev(h, wdtype) if head == "gated" else None,
+                                  W_g=to_dev(W_g, wdtype) if head == "gated" else None, temperature=T,
+                                  seeds=None if seeds is None else to_dev(seeds), offset=3, topk=topk,
+                                  tok_logit=tl, lse=ls, topk_idx=ti, topk_prob=tp, logits_out=lo)
+    torch.cuda.synchronize()
+    gpu = dict(tokens=tokens.cpu().numpy(), tok_logit=tl.cpu().numpy(), lse=ls.cpu().numpy(), logits=lo.cpu().numpy())
+    if topk:
+        gpu["topk_idx"], gpu["topk_prob"] = ti.cpu().numpy(), tp.cpu().numpy()
+    kw = dict(head=head, wdtype=wdtype)
+    if head == "gated":
+        kw.update(h=o.to_f64(h, wdtype), W_g=o.to_f64(W_g, wdtype))
+    check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, wdtype), o.to_f64(Bm, wdtype), temperature=T,
+                seeds=seeds, offset=3, topk=topk, oracle_kw=kw)
