@@ -250,6 +250,55 @@ def bench_verify(dev, stream, B=256, gamma=7, V=151936, reps=20):
     return out
 
 
+def bench_heads(dev, stream, B=256, gamma=7, V=151936, r=256, H=2560, reps=5):
+    """The Markov chain with each sequential head at a serving batch (greedy,
+    no top-k): mean time per call over back-to-back calls; the HBM fraction is
+    against gamma * (2rV + 4BV) bytes (Bm and U_j once per position)."""
+    import numpy as np
+    import torch
+    import synth
+    from semi_autoregressive_draft_amd import binding as bd
+    g = torch.Generator(device=dev)
+    g.manual_seed(37)
+    U = torch.randn((B, gamma, V), generator=g, device=dev, dtype=torch.float32)
+
+    def bf(x):
+        return torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
+
+    A = bf(synth.normal((V, r), 0.02, 0, synth.TID_A, "bf16"))
+    Bm = bf(synth.normal((r, V), 0.02, 0, synth.TID_BM, "bf16"))
+    h = bf(synth.normal((B, gamma, H), 1.0, 0, synth.TID_H, "bf16"))
+    Wg = bf(synth.normal((r, H + r), 0.02, 0, synth.TID_WG, "bf16"))
+    anchor = torch.randint(0, V, (B,), generator=g, device=dev, dtype=torch.int32)
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    out = {"B": B, "gamma": gamma, "V": V, "r": r, "H": H}
+    byt = gamma * (2.0 * r * V + 4.0 * B * V)
+    for name, code in (("linear", bd.HEAD_LINEAR), ("silu", bd.HEAD_SILU), ("gated", bd.HEAD_GATED)):
+        ws = torch.zeros(bd.dspark_markov_propose_head_workspace(code, B, gamma, V, r), dtype=torch.uint8,
+                         device=dev)
+
+        def call():
+            bd.dspark_markov_propose_head(code, U, anchor, A, Bm, tokens, h=h if code == bd.HEAD_GATED else None,
+                                          W_g=Wg if code == bd.HEAD_GATED else None, ws=ws)
+
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name + "_ms"] = round(ms, 4)
+        out[name + "_hbm_frac"] = round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        del ws
+    del U
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +417,7 @@ def main():
     sched = bench_prefix_schedule(dev, stream, with_oracle=not args.no_cpu_baseline)
     tfl = bench_teacher_forced_loss(dev, stream)
     ver = bench_verify(dev, stream)
+    heads = bench_heads(dev, stream)
 
     out = {
         "metric": METRIC, "value": round(blocks_per_s, 2), "unit": "blocks/s", "n_gpus": 1,
@@ -384,7 +434,7 @@ def main():
         "stages_note": "lm_head from the timed region; the others from a separate pass with an event around every stage",
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
-        "next_rows": {"prefix_schedule": sched, "teacher_forced_loss": tfl, "verify": ver},
+        "next_rows": {"prefix_schedule": sched, "teacher_forced_loss": tfl, "verify": ver, "heads": heads},
     }
     print(json.dumps(out), flush=True)
 

@@ -8,11 +8,13 @@
 // that dtype hands it on) for every request, and the step and top-k kernels
 // read their A operand from those rows instead of A[x_{j-1}].
 //
-// One workgroup of 256 threads per request.  SiLU: elementwise over r.
-// Gated: the concatenation [h_j; A[x_{j-1}]] (H + r floats) sits in LDS and
-// each wave computes r / 4 of the gate's dot products with rows of W_g
-// [r, H + r] (lanes over the row, a fixed-order wave reduction), then
-// m_k = sigma(z_k) * a_k.
+// SiLU: one workgroup of 256 threads per request, elementwise over r.
+// Gated, bf16 with H % 8 == 0: the gate pre-activations are a small GEMM,
+// Z [B, r] = X [B, H + r] W_g^T with X = [h_j; A[x_{j-1}]], on MFMA: one wave
+// per 16 requests x 16 outputs, K in chunks of 32 (X rows as the A operand,
+// W_g rows as the B operand, both contiguous in k), then
+// m = sigma(z) * a.  Otherwise one workgroup per request with X in LDS and a
+// wave per output row of W_g.
 #include "common.h"
 #include "internal.h"
 #include "markov_dev.h"
@@ -57,8 +59,55 @@ __global__ __launch_bounds__(kHeadThreads) void markov_head_prep(StepArgs a, int
   }
 }
 
+// gated head on MFMA (bf16, H % 8 == 0): grid (ceil(r / 16), ceil(B / 16)),
+// one wave each.  Lane (g, n) loads 8 consecutive k of request row n (from h
+// for k < H, else from A[x_{j-1}]) and of gate row n; D[4g + i][n] is request
+// 4g + i, output n.
+__global__ __launch_bounds__(kWave) void markov_head_gate_bf16(StepArgs a, const uint16_t* __restrict__ h, int H,
+                                                               const uint16_t* __restrict__ Wg,
+                                                               uint16_t* __restrict__ M) {
+  const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+  const int o0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
+  const int D = H + a.r;
+  const int bx = min(b0 + n, a.B - 1);                 // this lane's request row (A operand)
+  const int ox = min(o0 + n, a.r - 1);                 // this lane's gate row (B operand)
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* hrow = h + (static_cast<size_t>(bx) * a.gamma + a.j) * H;
+  const uint16_t* arow = A + static_cast<size_t>(prev_token(a, bx, a.j)) * a.r;
+  const uint16_t* wrow = Wg + static_cast<size_t>(ox) * D;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nk = (D + 31) / 32;
+#pragma unroll 8
+  for (int c = 0; c < nk; ++c) {
+    const int k = 32 * c + 8 * g;                       // a multiple of 8: never straddles h and A (H % 8 == 0)
+    u32x4 xa = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
+    if (k < D) {
+      xa = k < H ? *reinterpret_cast<const u32x4*>(hrow + k) : *reinterpret_cast<const u32x4*>(arow + (k - H));
+      wb = *reinterpret_cast<const u32x4*>(wrow + k);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(wb), acc, 0, 0, 0);
+  }
+  const int o = o0 + n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = b0 + 4 * g + i;
+    if (b < a.B && o < a.r) {
+      const float av = bf16_to_f32(A[static_cast<size_t>(prev_token(a, b, a.j)) * a.r + o]);
+      M[(static_cast<size_t>(b) * a.gamma + a.j) * a.r + o] = bf16_round(av / (1.0f + expf(-acc[i])));
+    }
+  }
+}
+
 hipError_t launch_head_prep(const StepArgs& a, bool bf16, int head, const void* h, int H, const void* Wg, void* M,
                             hipStream_t s) {
+  if (head == kHeadGated && bf16 && H % 8 == 0 && (reinterpret_cast<uintptr_t>(h) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(Wg) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.A) & 15) == 0 &&
+      a.r % 8 == 0) {
+    const dim3 grid((a.r + 15) / 16, (a.B + 15) / 16);
+    hipLaunchKernelGGL(markov_head_gate_bf16, grid, dim3(kWave), 0, s, a, static_cast<const uint16_t*>(h), H,
+                       static_cast<const uint16_t*>(Wg), static_cast<uint16_t*>(M));
+    return hipGetLastError();
+  }
   const size_t lds = head == kHeadGated ? static_cast<size_t>(H + a.r) * 4 : 0;
   if (lds > 64 * 1024) {
     const void* fn = bf16 ? reinterpret_cast<const void*>(&markov_head_prep<uint16_t>)
