@@ -24,6 +24,8 @@ pytestmark = pytest.mark.gpu
     (130, 296, 5000, "bf16"),     # tiled, ragged M/K/V tiles
     (448, 320, 3000, "bf16"),
     (600, 136, 2104, "bf16"),     # several row tiles, K tail, vocabulary tail inside an XCD group
+    (257, 8, 264, "bf16"),        # tiled, one K stage that is all tail, one row past a tile
+    (270, 64, 1032, "bf16"),      # tiled, exactly one full K stage
 ])
 def test_lm_head_parity(M, H, V, wdtype):
     dev = require_gpu()
