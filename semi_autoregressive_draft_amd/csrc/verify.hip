@@ -180,9 +180,8 @@ __global__ __launch_bounds__(kVerThreads) void verify_sample(VerifyArgs a) {
     // underflows float32 cannot win: G stays below 16.7 for this u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float u = (static_cast<float>(wd[i] >> 9) + 0.5f) * 0x1p-23f;
-      const float E = (u >= 0.5f) ? -log1pf(u - 1.0f) : -logf(u);
-      const float inv = 1.0f / E;
+      const float E = neg_log_uniform(uniform_from_word(wd[i]));
+      const float inv = __builtin_amdgcn_rcpf(E);         // E is normal: at least 4e-8
       const float p = __expf(t[i] - Lt);
       const unsigned long long k2 = best_key(p * inv, 4 * e + i);
       kt = k2 > kt ? k2 : kt;
