@@ -60,7 +60,10 @@ __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
   const int g = lane >> 4, n = lane & 15;
   const bool lo = n < 8;
   const bool hcol = n < M;
-  const uint16_t* hrow = hs + n * ld;
+  // B-operand column m = n: lanes past the last row read row M - 1, so that
+  // every LDS read is unconditional; they only feed output columns m >= M,
+  // which are never stored
+  const uint16_t* hrow = hs + min(n, M - 1) * ld;
   const int v0 = (blockIdx.x * kSkinnyWaves + w) * 16;
 
   // h rows into LDS by DMA: instruction i moves bytes [1024 q, 1024 q + 1024)
@@ -88,18 +91,20 @@ __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
       m0[d] = lo ? a0[d] : a1[d];
       m1[d] = lo ? a1[d] : a0[d];
     }
-    const u32x4 hb0 = hcol ? *reinterpret_cast<const u32x4*>(hrow + k0 + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 hb1 = hcol ? *reinterpret_cast<const u32x4*>(hrow + k0 + 32 + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 hb0 = *reinterpret_cast<const u32x4*>(hrow + k0 + 8 * g);
+    const u32x4 hb1 = *reinterpret_cast<const u32x4*>(hrow + k0 + 32 + 8 * g);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(m0), as_bf16x8(hb0), acc, 0, 0, 0);
     acc8 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(m1), as_bf16x8(hb1), acc8, 0, 0, 0);
   };
 
   // Pairs of batches of kSkinnyUnroll chunks, software-pipelined over two
   // register sets: the loads of one batch are in flight while the other is
-  // computed.  Every load in the loop is unconditional (the compiler's wait
-  // counts stay exact): rows past V read row 0, whose outputs are never
-  // stored, and the last pair's look-ahead reloads its own second batch (an L2
-  // hit).  Chunks past the last pair take the plain loop below.
+  // computed.  Both batches of the first pair are issued before the wait for
+  // h, so that 16 KB per wave is in flight while h lands; the last pair is
+  // peeled, so no load reaches past the rows' end.  Every load is
+  // unconditional (the compiler's wait counts stay exact): rows past V read
+  // row 0, whose outputs are never stored.  Chunks past the last pair take the
+  // plain loop below.
   const int npairs = (H / 64) / (2 * kSkinnyUnroll);
   u32x4 x0[kSkinnyUnroll], x1[kSkinnyUnroll], y0[kSkinnyUnroll], y1[kSkinnyUnroll];
   auto issue = [&](u32x4 (&b0)[kSkinnyUnroll], u32x4 (&b1)[kSkinnyUnroll], int bt) {
@@ -115,21 +120,32 @@ __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
   };
   if constexpr (PIPE) {
     issue(x0, x1, 0);
-    wait_vmcnt_le<2 * kSkinnyUnroll>();           // this wave's h DMA (older) has landed
+    __builtin_amdgcn_sched_barrier(0);
+    issue(y0, y1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_le<4 * kSkinnyUnroll>();           // this wave's h DMA (older) has landed
   } else {
     wait_vmcnt_le<0>();
   }
   asm volatile("s_barrier" ::: "memory");          // every wave's h DMA has landed
   // (waves past V run to the end on row 0 and store nothing: an early exit
-  // would let the compiler sink the first batch below it)
-  if constexpr (PIPE) {                            // npairs >= 1: the batch above is used
-    int p = 0;
-    do {
-      issue(y0, y1, 2 * p + 1);
+  // would let the compiler sink the first batches below it)
+  if constexpr (PIPE) {                            // npairs >= 1: the batches above are used
+    // the scheduling barriers keep each batch's loads ahead of the other
+    // batch's arithmetic (the LDS reads of h are free to move, and would
+    // otherwise take the loads with them)
+    for (int p = 0; p + 1 < npairs; ++p) {
       compute(x0, x1, 2 * p);
-      issue(x0, x1, min(2 * p + 2, 2 * npairs - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      issue(x0, x1, 2 * p + 2);
+      __builtin_amdgcn_sched_barrier(0);
       compute(y0, y1, 2 * p + 1);
-    } while (++p < npairs);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(y0, y1, 2 * p + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    compute(x0, x1, 2 * npairs - 2);
+    compute(y0, y1, 2 * npairs - 1);
   }
   for (int kc = PIPE ? 2 * npairs * kSkinnyUnroll : 0; kc < H / 64; ++kc) {
     const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w0 + kc * 64));
@@ -145,7 +161,7 @@ __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
     const bool kok = k < H;
     const u32x4 wa = (vok && kok) ? *reinterpret_cast<const u32x4*>(W + static_cast<size_t>(vr) * H + k)
                                   : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 hb = (hcol && kok) ? *reinterpret_cast<const u32x4*>(hrow + k) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 hb = kok ? *reinterpret_cast<const u32x4*>(hrow + k) : u32x4{0u, 0u, 0u, 0u};
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa), as_bf16x8(hb), acc, 0, 0, 0);
   }
 #pragma unroll
