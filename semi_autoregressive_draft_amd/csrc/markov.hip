@@ -366,7 +366,7 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
   auto load_u = [&](int t, f32x4 (&u)[4]) {
     const size_t c = lcol(t);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) u[ii] = *reinterpret_cast<const f32x4*>(urow[ii] + c);
+    for (int ii = 0; ii < 4; ++ii) u[ii] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(urow[ii] + c));
   };
   // Bm rows of this wave's chunks of tile t (chunks w, w + nw, ...; NCH <= CPW * nw)
   auto load_bm = [&](int t, u32x2 (&raw)[CPW][8]) {
@@ -434,8 +434,9 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
       for (int ii = 0; ii < 4; ++ii) {
         const int b = req0 + 4 * g + ii;
         if (b < a.B && cok)
-          *reinterpret_cast<f32x4*>(a.logits_out + (static_cast<size_t>(b) * a.gamma + a.j) * V + col) =
-              f32x4{acc[0][ii] + u[ii][0], acc[1][ii] + u[ii][1], acc[2][ii] + u[ii][2], acc[3][ii] + u[ii][3]};
+          __builtin_nontemporal_store(
+              f32x4{acc[0][ii] + u[ii][0], acc[1][ii] + u[ii][1], acc[2][ii] + u[ii][2], acc[3][ii] + u[ii][3]},
+              reinterpret_cast<f32x4*>(a.logits_out + (static_cast<size_t>(b) * a.gamma + a.j) * V + col));
       }
       return;
     }
@@ -447,7 +448,8 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
       float x[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = live ? acc[c][ii] + u[ii][c] : kNegInf;
-      if (live && a.logits_out) *reinterpret_cast<f32x4*>(a.logits_out + row * V + col) = f32x4{x[0], x[1], x[2], x[3]};
+      if (live && a.logits_out)
+        __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(a.logits_out + row * V + col));
       const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       if (a.segmax) {
         const float m8 = fmaxf(m4, dpp_f<kDppXor1>(m4));   // lanes 2s, 2s+1: one 8-column segment
