@@ -55,6 +55,13 @@
 
 namespace dspark {
 
+// barrier for LDS traffic only: waits for this wave's LDS operations, not its
+// global loads and stores (__syncthreads waits for both)
+__device__ __forceinline__ void res_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
+
 constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / kWave;
 constexpr int kResCols = 64;                  // vocabulary columns per group
@@ -334,11 +341,12 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
 
   // U_j rows of this workgroup's groups, [t][b][64] floats, into buffer j % 2
   // by DMA: each wave instruction moves 4 rows of 256 bytes (lane i: row
-  // 4k + i/16, bytes 16 (i%16))
+  // 4k + i/16, bytes 16 (i%16)); wave wv of nwv takes instructions wv, wv +
+  // nwv, ...
   const int nrows = ra.T * a.B;
-  auto issue_u = [&](int j) {
+  auto issue_u = [&](int j, int wv, int nwv) {
     float* lds_u = lds_u0 + (j & 1) * ubuf;
-    for (int k = w; 4 * k < nrows; k += kResWaves) {
+    for (int k = wv; 4 * k < nrows; k += nwv) {
       const int rr = 4 * k + (lane >> 4);
       const int t = rr / a.B, b = rr - t * a.B;
       const int col = gid_of(t) * kResCols + 4 * (lane & 15);
@@ -348,7 +356,7 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
       }
     }
   };
-  issue_u(0);
+  issue_u(0, w, kResWaves);
 
   // Bm share: register groups t = w*RGW + s, LDS group t = nreg + w
   u32x4 dreg[RGW][KCH][4];
@@ -444,8 +452,11 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
           wlse[w][4 * g + ii] = run[ii];
         }
     }
-    __syncthreads();                                  // wave bests in LDS; U_j no longer read
-    if (j + 1 < a.gamma) issue_u(j + 1);
+    res_lds_barrier();                                // wave bests in LDS; U_j no longer read
+    // waves 1..7 fetch U_{j+1}; not wave 0: a wave's LDS reads after its own
+    // DMA into LDS wait for the DMA to land (the compiler cannot tell the
+    // buffers apart), and wave 0's reads of the wave bests lead the wait tree
+    if (j + 1 < a.gamma && w > 0) issue_u(j + 1, w - 1, kResWaves - 1);
     if (a.topk > 0 && w > 0) {                       // local candidate lists, beside the wait
       for (int b = w - 1; b < a.B; b += kResWaves - 1)
         local_topk(a, ra, lds_u, b, wg, lane, ltk_max[w - 1], ltk_key[w - 1]);
