@@ -36,6 +36,70 @@ __device__ __forceinline__ void online_add4(LseState& st, f32x4 x) {
   st.s += (__expf(x[0] - st.m) + __expf(x[1] - st.m)) + (__expf(x[2] - st.m) + __expf(x[3] - st.m));
 }
 
+__device__ __forceinline__ float sum_exp_min4(f32x4 t, f32x4 d, float Lt, float Ld) {
+  return (__expf(fminf(t[0] - Lt, d[0] - Ld)) + __expf(fminf(t[1] - Lt, d[1] - Ld))) +
+         (__expf(fminf(t[2] - Lt, d[2] - Ld)) + __expf(fminf(t[3] - Lt, d[3] - Ld)));
+}
+
+// Streaming passes keep kOvUnroll loads per thread in flight: kOvUnroll
+// independent online states (or partial sums), one per load slot, merged in a
+// fixed order at the end.  (One state per thread serialises the loop: each
+// load's value feeds the next update, and the wave waits for every load
+// before issuing the next.)  NT: non-temporal loads, for rows read once.
+constexpr int kOvUnroll = 4;
+
+template <bool NT>
+__device__ __forceinline__ f32x4 ld4(const f32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// online (max, sum exp) of elements e0 + tid, e0 + tid + stride, ... < e1
+template <bool NT>
+__device__ LseState range_lse(const f32x4* p, int e0, int e1, int stride) {
+  LseState st[kOvUnroll];
+#pragma unroll
+  for (int u = 0; u < kOvUnroll; ++u) st[u] = LseState{kNegInf, 0.f};
+  int e = e0;
+  for (; e + (kOvUnroll - 1) * stride < e1; e += kOvUnroll * stride) {
+    f32x4 v[kOvUnroll];
+#pragma unroll
+    for (int u = 0; u < kOvUnroll; ++u) v[u] = ld4<NT>(p + e + u * stride);
+#pragma unroll
+    for (int u = 0; u < kOvUnroll; ++u) online_add4(st[u], v[u]);
+  }
+  for (; e < e1; e += stride) online_add4(st[0], ld4<NT>(p + e));
+#pragma unroll
+  for (int u = 1; u < kOvUnroll; ++u) st[0] = lse_merge(st[0], st[u]);
+  return st[0];
+}
+
+// sum over the same elements of exp(min(t - Lt, d - Ld)), the elements taken
+// in the order `first, first - stride, ...` down to e0 (walk_down) or up from
+// first to e1
+template <bool WALK_DOWN>
+__device__ float range_min_sum(const f32x4* tp, const f32x4* dp, int first, int e0, int e1, int stride, float Lt,
+                               float Ld) {
+  float s[kOvUnroll];
+#pragma unroll
+  for (int u = 0; u < kOvUnroll; ++u) s[u] = 0.f;
+  const int step = WALK_DOWN ? -stride : stride;
+  int e = first;
+  auto more = [&](int x) { return WALK_DOWN ? x >= e0 : x < e1; };
+  for (; more(e + (kOvUnroll - 1) * step); e += kOvUnroll * step) {
+    f32x4 t[kOvUnroll], d[kOvUnroll];
+#pragma unroll
+    for (int u = 0; u < kOvUnroll; ++u) {
+      t[u] = tp[e + u * step];
+      d[u] = dp[e + u * step];
+    }
+#pragma unroll
+    for (int u = 0; u < kOvUnroll; ++u) s[u] += sum_exp_min4(t[u], d[u], Lt, Ld);
+  }
+  for (; more(e); e += step) s[0] += sum_exp_min4(tp[e], dp[e], Lt, Ld);
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
 template <int NW>
 __device__ LseState block_lse_state(LseState st, LseState* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -59,11 +123,6 @@ __device__ float block_sum(float v, float* red) {
   for (int i = 0; i < NW; ++i) r += red[i];
   __syncthreads();
   return r;
-}
-
-__device__ __forceinline__ float sum_exp_min4(f32x4 t, f32x4 d, float Lt, float Ld) {
-  return (__expf(fminf(t[0] - Lt, d[0] - Ld)) + __expf(fminf(t[1] - Lt, d[1] - Ld))) +
-         (__expf(fminf(t[2] - Lt, d[2] - Ld)) + __expf(fminf(t[3] - Lt, d[3] - Ld)));
 }
 
 // candidate-set overlap of one row: this thread's share (candidates first,
@@ -94,25 +153,21 @@ __global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
   float total;
   if (a.draft) {
     const f32x4* dp = reinterpret_cast<const f32x4*>(a.draft + row * V);
-    LseState lt{kNegInf, 0.f}, ld{kNegInf, 0.f};
-    for (int e = tid; e < n4; e += kOvThreads) {
-      online_add4(lt, tp[e]);
-      online_add4(ld, dp[e]);
-    }
+    const LseState lt = range_lse<false>(tp, tid, n4, kOvThreads);
+    const LseState ld = range_lse<false>(dp, tid, n4, kOvThreads);
     const LseState rt = block_lse_state<NW>(lt, red_l);
     const LseState rd = block_lse_state<NW>(ld, red_l);
     const float Lt = rt.m + logf(rt.s), Ld = rd.m + logf(rd.s);
-    float s = 0.f;
+    // second pass walks down, to reuse what the first touched last
     const int last = (n4 - 1 - tid) >= 0 ? tid + ((n4 - 1 - tid) / kOvThreads) * kOvThreads : -1;
-    for (int e = last; e >= 0; e -= kOvThreads) s += sum_exp_min4(tp[e], dp[e], Lt, Ld);
+    const float s = range_min_sum<true>(tp, dp, last, 0, n4, kOvThreads, Lt, Ld);
     total = block_sum<NW>(s, red_f);
     if (tid == 0) {
       if (a.lse_draft) a.lse_draft[row] = Ld;
       if (a.ov_sum) a.ov_sum[row] = total;
     }
   } else {
-    LseState lt{kNegInf, 0.f};
-    for (int e = tid; e < n4; e += kOvThreads) online_add4(lt, tp[e]);
+    const LseState lt = range_lse<true>(tp, tid, n4, kOvThreads);   // the row is read once
     const LseState rt = block_lse_state<NW>(lt, red_l);
     total = block_sum<NW>(candidate_overlap(a, row, rt.m + logf(rt.s), tid, kOvThreads), red_f);
   }
@@ -129,11 +184,14 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_split_stats(OverlapArgs
   const size_t V = static_cast<size_t>(a.V);
   const int e0 = c * a.chunk4, e1 = min(e0 + a.chunk4, a.V / 4);
   const f32x4* tp = reinterpret_cast<const f32x4*>(a.teacher + row * V);
-  LseState lt{kNegInf, 0.f}, ld{kNegInf, 0.f};
-  for (int e = e0 + tid; e < e1; e += kSplitThreads) online_add4(lt, tp[e]);
+  // candidate mode reads the teacher once; the dense pass 2 reads both again
+  LseState lt, ld{kNegInf, 0.f};
   if (a.draft) {
     const f32x4* dp = reinterpret_cast<const f32x4*>(a.draft + row * V);
-    for (int e = e0 + tid; e < e1; e += kSplitThreads) online_add4(ld, dp[e]);
+    lt = range_lse<false>(tp, e0 + tid, e1, kSplitThreads);
+    ld = range_lse<false>(dp, e0 + tid, e1, kSplitThreads);
+  } else {
+    lt = range_lse<true>(tp, e0 + tid, e1, kSplitThreads);
   }
   const LseState rt = block_lse_state<NW>(lt, red_l);
   const LseState rd = block_lse_state<NW>(ld, red_l);
@@ -181,8 +239,7 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_split_sum(OverlapArgs a
   const int e0 = c * a.chunk4, e1 = min(e0 + a.chunk4, a.V / 4);
   const f32x4* tp = reinterpret_cast<const f32x4*>(a.teacher + row * V);
   const f32x4* dp = reinterpret_cast<const f32x4*>(a.draft + row * V);
-  float s = 0.f;
-  for (int e = e0 + tid; e < e1; e += kSplitThreads) s += sum_exp_min4(tp[e], dp[e], Lt, Ld);
+  const float s = range_min_sum<false>(tp, dp, e0 + tid, e0, e1, kSplitThreads, Lt, Ld);
   const float tot = block_sum<NW>(s, red_f);
   if (tid == 0) a.ws_split[(static_cast<size_t>(row) * a.nchunk + c) * 5 + 4] = tot;
 }
