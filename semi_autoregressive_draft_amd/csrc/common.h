@@ -84,6 +84,50 @@ __device__ __forceinline__ LseState lse_merge(LseState a, LseState b) {
   return {m, sa + sb};
 }
 
+// online (max, sum exp) update with four elements
+__device__ __forceinline__ void online_add4(LseState& st, f32x4 x) {
+  const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (m4 > st.m) {
+    st.s = (st.m == kNegInf) ? 0.f : st.s * __expf(st.m - m4);
+    st.m = m4;
+  }
+  st.s += (__expf(x[0] - st.m) + __expf(x[1] - st.m)) + (__expf(x[2] - st.m) + __expf(x[3] - st.m));
+}
+
+// Streaming passes keep kStreamUnroll loads per thread in flight: as many
+// independent online states (or partial sums), one per load slot, merged in a
+// fixed order at the end.  (One state per thread serialises the loop: each
+// load's value feeds the next update, and the wave waits for every load
+// before issuing the next.)  NT: non-temporal loads, for rows read once.
+constexpr int kStreamUnroll = 4;
+
+template <bool NT>
+__device__ __forceinline__ f32x4 ld4(const f32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// online (max, sum exp) of elements e0 + tid, e0 + tid + stride, ... < e1
+template <bool NT>
+__device__ LseState range_lse(const f32x4* p, int e0, int e1, int stride) {
+  LseState st[kStreamUnroll];
+#pragma unroll
+  for (int u = 0; u < kStreamUnroll; ++u) st[u] = LseState{kNegInf, 0.f};
+  int e = e0;
+  for (; e + (kStreamUnroll - 1) * stride < e1; e += kStreamUnroll * stride) {
+    f32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = ld4<NT>(p + e + u * stride);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) online_add4(st[u], v[u]);
+  }
+  for (; e < e1; e += stride) online_add4(st[0], ld4<NT>(p + e));
+#pragma unroll
+  for (int u = 1; u < kStreamUnroll; ++u) st[0] = lse_merge(st[0], st[u]);
+  return st[0];
+}
+
+
 struct ArgState { float score; int idx; float x; };  // best score, its index, U~ there
 
 __device__ __forceinline__ ArgState arg_merge(ArgState a, ArgState b) {

@@ -27,74 +27,33 @@ constexpr int kSplitChunk = 2048;      // elements per workgroup on the split pa
 constexpr int kSplitRowsMax = 1024;    // at and above this many rows, one workgroup per row
 constexpr int kFusedFinishRows = 64;   // up to this many rows, one workgroup finishes rows and tau
 
-__device__ __forceinline__ void online_add4(LseState& st, f32x4 x) {
-  const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  if (m4 > st.m) {
-    st.s = (st.m == kNegInf) ? 0.f : st.s * __expf(st.m - m4);
-    st.m = m4;
-  }
-  st.s += (__expf(x[0] - st.m) + __expf(x[1] - st.m)) + (__expf(x[2] - st.m) + __expf(x[3] - st.m));
-}
-
 __device__ __forceinline__ float sum_exp_min4(f32x4 t, f32x4 d, float Lt, float Ld) {
   return (__expf(fminf(t[0] - Lt, d[0] - Ld)) + __expf(fminf(t[1] - Lt, d[1] - Ld))) +
          (__expf(fminf(t[2] - Lt, d[2] - Ld)) + __expf(fminf(t[3] - Lt, d[3] - Ld)));
 }
 
-// Streaming passes keep kOvUnroll loads per thread in flight: kOvUnroll
-// independent online states (or partial sums), one per load slot, merged in a
-// fixed order at the end.  (One state per thread serialises the loop: each
-// load's value feeds the next update, and the wave waits for every load
-// before issuing the next.)  NT: non-temporal loads, for rows read once.
-constexpr int kOvUnroll = 4;
-
-template <bool NT>
-__device__ __forceinline__ f32x4 ld4(const f32x4* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(p);
-  else return *p;
-}
-
-// online (max, sum exp) of elements e0 + tid, e0 + tid + stride, ... < e1
-template <bool NT>
-__device__ LseState range_lse(const f32x4* p, int e0, int e1, int stride) {
-  LseState st[kOvUnroll];
-#pragma unroll
-  for (int u = 0; u < kOvUnroll; ++u) st[u] = LseState{kNegInf, 0.f};
-  int e = e0;
-  for (; e + (kOvUnroll - 1) * stride < e1; e += kOvUnroll * stride) {
-    f32x4 v[kOvUnroll];
-#pragma unroll
-    for (int u = 0; u < kOvUnroll; ++u) v[u] = ld4<NT>(p + e + u * stride);
-#pragma unroll
-    for (int u = 0; u < kOvUnroll; ++u) online_add4(st[u], v[u]);
-  }
-  for (; e < e1; e += stride) online_add4(st[0], ld4<NT>(p + e));
-#pragma unroll
-  for (int u = 1; u < kOvUnroll; ++u) st[0] = lse_merge(st[0], st[u]);
-  return st[0];
-}
-
 // sum over the same elements of exp(min(t - Lt, d - Ld)), the elements taken
 // in the order `first, first - stride, ...` down to e0 (walk_down) or up from
 // first to e1
+static_assert(kStreamUnroll == 4, "range_min_sum folds four partial sums");
 template <bool WALK_DOWN>
 __device__ float range_min_sum(const f32x4* tp, const f32x4* dp, int first, int e0, int e1, int stride, float Lt,
                                float Ld) {
-  float s[kOvUnroll];
+  float s[kStreamUnroll];
 #pragma unroll
-  for (int u = 0; u < kOvUnroll; ++u) s[u] = 0.f;
+  for (int u = 0; u < kStreamUnroll; ++u) s[u] = 0.f;
   const int step = WALK_DOWN ? -stride : stride;
   int e = first;
   auto more = [&](int x) { return WALK_DOWN ? x >= e0 : x < e1; };
-  for (; more(e + (kOvUnroll - 1) * step); e += kOvUnroll * step) {
-    f32x4 t[kOvUnroll], d[kOvUnroll];
+  for (; more(e + (kStreamUnroll - 1) * step); e += kStreamUnroll * step) {
+    f32x4 t[kStreamUnroll], d[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kOvUnroll; ++u) {
+    for (int u = 0; u < kStreamUnroll; ++u) {
       t[u] = tp[e + u * step];
       d[u] = dp[e + u * step];
     }
 #pragma unroll
-    for (int u = 0; u < kOvUnroll; ++u) s[u] += sum_exp_min4(t[u], d[u], Lt, Ld);
+    for (int u = 0; u < kStreamUnroll; ++u) s[u] += sum_exp_min4(t[u], d[u], Lt, Ld);
   }
   for (; more(e); e += step) s[0] += sum_exp_min4(tp[e], dp[e], Lt, Ld);
   return (s[0] + s[1]) + (s[2] + s[3]);

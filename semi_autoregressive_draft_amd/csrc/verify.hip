@@ -63,15 +63,6 @@ __device__ __forceinline__ int proposal_len(const VerifyArgs& a, int b) {
   return a.lengths ? min(max(a.lengths[b], 0), a.G) : a.G;
 }
 
-__device__ __forceinline__ void online_add4v(LseState& st, f32x4 x) {
-  const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  if (m4 > st.m) {
-    st.s = (st.m == kNegInf) ? 0.f : st.s * __expf(st.m - m4);
-    st.m = m4;
-  }
-  st.s += (__expf(x[0] - st.m) + __expf(x[1] - st.m)) + (__expf(x[2] - st.m) + __expf(x[3] - st.m));
-}
-
 // 1. chunk states of the needed rows
 __global__ __launch_bounds__(kVerThreads) void verify_stats(VerifyArgs a) {
   __shared__ LseState red[kVerThreads / kWave];
@@ -86,8 +77,7 @@ __global__ __launch_bounds__(kVerThreads) void verify_stats(VerifyArgs a) {
   const f32x4* row = reinterpret_cast<const f32x4*>(is_t ? a.target + static_cast<size_t>(r) * V
                                                          : a.draft + static_cast<size_t>(r - nt) * V);
   const int e0 = c * a.chunk4, e1 = min(e0 + a.chunk4, a.V / 4);
-  LseState st{kNegInf, 0.f};
-  for (int e = e0 + tid; e < e1; e += kVerThreads) online_add4v(st, row[e]);
+  LseState st = range_lse<true>(row, e0 + tid, e1, kVerThreads);
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) st = lse_merge(st, shfl_xor(st, o));
   if (lane == 0) red[w] = st;
