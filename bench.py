@@ -311,8 +311,8 @@ def main():
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE per dispatch calibrate the counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU; the multi-GPU path is a design only "
-              "(requests shard across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: measures one GPU only; running on several GPUs is not supported "
+              "(requests would shard across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
