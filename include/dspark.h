@@ -182,6 +182,28 @@ dspark_status_t dspark_markov_propose_head_workspace(int32_t head, int64_t B, in
                                                      int64_t r, dspark_dtype_t wdt, int32_t topk,
                                                      size_t* bytes);
 
+/*
+ * Workspace that also holds a transposed copy of Bm ([V, r], bf16) for the
+ * exact top-k of S4 (an implementation choice: the pages fix what the top-k
+ * is, not how its candidates are recomputed).  On the per-position path the
+ * top-k recomputes the U~ of its candidate 8-column segments from Bm; read
+ * from Bm [r, V], each segment takes 16 bytes of each of r rows, i.e. r whole
+ * cache lines for 16 useful bytes per line.  With this larger workspace,
+ * dspark_markov_propose and dspark_markov_propose_head first transpose Bm
+ * into the workspace's tail and the recompute reads whole row pieces, when
+ * that moves fewer bytes (large B; bf16, topk > 0, not the resident chain).
+ * The results are the same top-k (up to float32 summation order in the
+ * recomputed values).
+ *
+ *   bytes  out: dspark_markov_propose_head_workspace(head, ...) plus, for bf16
+ *          and topk > 0, r * V * 2 bytes rounded up to 256
+ * Errors: those of dspark_markov_propose_head_workspace; an unknown wdt is
+ * DSPARK_EUNSUPPORTED.
+ */
+dspark_status_t dspark_markov_propose_workspace_bmt(int32_t head, int64_t B, int64_t gamma, int64_t V,
+                                                    int64_t r, dspark_dtype_t wdt, int32_t topk,
+                                                    size_t* bytes);
+
 dspark_status_t dspark_markov_propose_head(int32_t head, const void* h, int64_t H, const void* W_g,
                                            const float* U, int64_t B, int64_t gamma, int64_t V,
                                            const int32_t* anchor, const void* A, const void* Bm,

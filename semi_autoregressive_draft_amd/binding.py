@@ -43,6 +43,8 @@ _SIGNATURES = {
     "dspark_verify_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
     "dspark_markov_propose_head_workspace": (C.c_int, [_i32, _i64, _i64, _i64, _i64, C.c_int, _i32,
                                                        C.POINTER(_sz)]),
+    "dspark_markov_propose_workspace_bmt": (C.c_int, [_i32, _i64, _i64, _i64, _i64, C.c_int, _i32,
+                                                      C.POINTER(_sz)]),
     "dspark_markov_propose_head": (C.c_int, [_i32, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                                              C.c_int, _i64, _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp,
                                              _vp, _vp, _sz, _vp]),
@@ -249,6 +251,14 @@ def dspark_markov_propose_head_workspace(head: int, B: int, gamma: int, V: int, 
                                          topk: int = 0) -> int:
     n = _sz(0)
     _check(lib().dspark_markov_propose_head_workspace(head, B, gamma, V, r, wdtype, topk, C.byref(n)))
+    return n.value
+
+
+def dspark_markov_propose_workspace_bmt(head: int, B: int, gamma: int, V: int, r: int, wdtype: int = BF16,
+                                        topk: int = 0) -> int:
+    """Workspace bytes that also hold the transposed Bm of the top-k recompute."""
+    n = _sz(0)
+    _check(lib().dspark_markov_propose_workspace_bmt(head, B, gamma, V, r, wdtype, topk, C.byref(n)))
     return n.value
 
 

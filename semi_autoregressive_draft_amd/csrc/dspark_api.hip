@@ -246,6 +246,11 @@ dspark_status_t propose_impl(
   // the head variants run per position: the prep kernel writes m_j between positions
   const bool resident = head_kind == kHeadLinear && resident_chain(bf16, a.B, a.V, a.r, &nwg, &lds);
   void* mtab = head_kind == kHeadLinear ? nullptr : static_cast<char*>(ws) + markov_ws_bytes(B, gamma, V, topk);
+  // a workspace that also holds the transposed Bm (see the _bmt query) turns on
+  // the contiguous top-k recompute where it pays off
+  const size_t bmt = markov_bmt_bytes(r, V);
+  if (!resident && topk > 0 && bf16 && ws_bytes >= need + bmt && markov_bmt_pays(B, gamma, V, r, topk))
+    a.BmT = static_cast<char*>(ws) + need;
   a.Mrow = mtab;
   a.tile_cols = resident ? 64 : markov_tile_cols(bf16, a.sample, a.B, a.r, a.V);
   a.resident = resident;
@@ -292,6 +297,17 @@ extern "C" dspark_status_t dspark_markov_propose_head_workspace(int32_t head, in
     return fail(DSPARK_EINVAL, "%s: B, gamma, V, r must be positive, topk >= 0", fn);
   if (V > kI32Max || B > kI32Max / 16 || r > kMaxRank) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
   *bytes = markov_ws_bytes(B, gamma, V, topk) + head_table_bytes(head, B, gamma, r, wdt == DSPARK_BF16);
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status_t dspark_markov_propose_workspace_bmt(int32_t head, int64_t B, int64_t gamma, int64_t V,
+                                                               int64_t r, dspark_dtype_t wdt, int32_t topk,
+                                                               size_t* bytes) {
+  const char* fn = "dspark_markov_propose_workspace_bmt";
+  const dspark_status_t st = dspark_markov_propose_head_workspace(head, B, gamma, V, r, wdt, topk, bytes);
+  if (st != DSPARK_OK) return st;
+  if (wdt != DSPARK_F32 && wdt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)wdt);
+  if (topk > 0 && wdt == DSPARK_BF16) *bytes += markov_bmt_bytes(r, V);
   return DSPARK_OK;
 }
 

@@ -42,6 +42,7 @@ struct StepArgs {
   int nlist;
   const void* A;           // [V, r]
   const void* Bm;          // [r, V]
+  const void* BmT;         // [V, r] copy of Bm (bf16) for the top-k recompute, or NULL
   int B, gamma, V, r, j;
   int sample;              // 0 greedy, 1 Gumbel-max
   float inv_temp;
@@ -72,6 +73,11 @@ bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg, size_t* lds
 hipError_t launch_markov_resident(StepArgs a, unsigned* sync, int nwg, size_t lds, hipStream_t s);
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s);
 hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s);
+// bytes of the transposed Bm copy (bf16, [V, r]), and whether building it pays
+// off against the top-k recompute's cache-line amplification on the
+// per-position path
+size_t markov_bmt_bytes(int64_t r, int64_t V);
+bool markov_bmt_pays(int64_t B, int64_t gamma, int64_t V, int64_t r, int32_t topk);
 
 hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
                           int64_t V, float* U, hipStream_t s);

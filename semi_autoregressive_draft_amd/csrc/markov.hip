@@ -710,7 +710,7 @@ __device__ void kth_largest(const float* vals, int n, int k, float* out) {
   __syncthreads();
 }
 
-template <typename WT>
+template <typename WT, bool BMT = false>
 __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile_cols) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x, j = blockIdx.y;
@@ -812,7 +812,29 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
           float acc[kSeg];
 #pragma unroll
           for (int i = 0; i < kSeg; ++i) acc[i] = 0.f;
-          if (on) {
+          if (BMT && on) {
+            // bf16 only: column v0 + i is row v0 + i of BmT (r contiguous
+            // values); the thread takes 8-wide k-chunks q, q + 16, ... of all
+            // 8 columns (whole 16-byte pieces of rows, instead of 16 useful
+            // bytes of each of r Bm rows)
+            const uint16_t* BmT = static_cast<const uint16_t*>(a.BmT);
+            for (int k0 = 8 * q; k0 < a.r; k0 += 8 * kSliceThreads) {
+              u32x4 raw[kSeg];
+#pragma unroll
+              for (int i = 0; i < kSeg; ++i)
+                raw[i] = *reinterpret_cast<const u32x4*>(BmT + static_cast<size_t>(v0 + i) * a.r + k0);
+              float am[8];
+#pragma unroll
+              for (int t = 0; t < 8; ++t) am[t] = arow_s[k0 + t];
+#pragma unroll
+              for (int i = 0; i < kSeg; ++i) {
+                float col[8];
+                SegRows<uint16_t>::unpack(raw[i], col);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[i] = fmaf(am[t], col[t], acc[i]);
+              }
+            }
+          } else if (on) {
             // rows q, q+16, ... of Bm, issued RB at a time in packed form
             constexpr int RB = SegRows<WT>::kBatch;
             for (int k0 = q; k0 < a.r; k0 += RB * kSliceThreads) {
@@ -1108,6 +1130,46 @@ hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Bm [r, V] -> BmT [V, r] (bf16) through a 32 (rows of Bm) x 64 (columns)
+// LDS tile: 16-byte loads along a Bm row, 16-byte stores along a BmT row.
+// V % 8 == 0 and r % 32 == 0, so every 8-element piece is whole.
+constexpr int kTrR = 32, kTrC = 64;
+__global__ __launch_bounds__(256) void transpose_bm_bf16(const uint16_t* __restrict__ Bm,
+                                                        uint16_t* __restrict__ BmT, int r, int V) {
+  __shared__ uint16_t tile[kTrR][kTrC + 8];
+  const int c0 = blockIdx.x * kTrC, k0 = blockIdx.y * kTrR, t = threadIdx.x;
+  {
+    const int kr = t >> 3, cc = (t & 7) * 8;             // Bm row k0 + kr, columns c0 + cc ..
+    if (c0 + cc < V) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Bm + static_cast<size_t>(k0 + kr) * V + c0 + cc);
+      *reinterpret_cast<u32x4*>(&tile[kr][cc]) = v;
+    }
+  }
+  __syncthreads();
+  {
+    const int c = t >> 2, kk = (t & 3) * 8;              // BmT row c0 + c, k0 + kk ..
+    if (c0 + c < V) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = static_cast<uint32_t>(tile[kk + 2 * i][c]) | (static_cast<uint32_t>(tile[kk + 2 * i + 1][c]) << 16);
+      *reinterpret_cast<u32x4*>(BmT + static_cast<size_t>(c0 + c) * r + k0 + kk) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+size_t markov_bmt_bytes(int64_t r, int64_t V) { return (static_cast<size_t>(r) * V * 2 + 255) / 256 * 256; }
+
+// The recompute reads, per (request, position) and per candidate segment of 8
+// columns, 16 bytes from each of r Bm rows (whole 128-byte lines); with BmT it
+// reads 8 rows of r values, after a copy that reads and writes r V values.
+bool markov_bmt_pays(int64_t B, int64_t gamma, int64_t V, int64_t r, int32_t topk) {
+  const double rows = static_cast<double>(B) * gamma, segs = topk;
+  const double strided = rows * segs * r * 128.0;
+  const double copied = 2.0 * r * V * 2.0 + rows * segs * 8.0 * r * 2.0;
+  return copied < strided;
+}
+
 hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s) {
   a.Pn = partial_count(a);
   const dim3 grid(a.B, a.gamma);
@@ -1118,7 +1180,12 @@ hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.topk == 0) return hipSuccess;
-  if (bf16)
+  if (bf16 && a.BmT) {
+    const dim3 tg((a.V + kTrC - 1) / kTrC, a.r / kTrR);
+    hipLaunchKernelGGL(transpose_bm_bf16, tg, dim3(256), 0, s, static_cast<const uint16_t*>(a.Bm),
+                       static_cast<uint16_t*>(const_cast<void*>(a.BmT)), a.r, a.V);
+    hipLaunchKernelGGL((markov_topk<uint16_t, true>), grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
+  } else if (bf16)
     hipLaunchKernelGGL(markov_topk<uint16_t>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
   else
     hipLaunchKernelGGL(markov_topk<float>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);

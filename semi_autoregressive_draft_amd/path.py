@@ -41,9 +41,12 @@ class DraftPath:
         self.topk_idx = torch.empty((B, gamma, topk), dtype=torch.int32, device=dev) if topk else None
         self.topk_prob = torch.empty((B, gamma, topk), **f32) if topk else None
         self.logits = torch.empty((B, gamma, V), **f32) if overlap == "dense" else None
-        # zero-filled once; every propose call leaves it ready for the next
-        self.ws_markov = torch.zeros(bd.dspark_markov_propose_workspace(B, gamma, V, topk),
-                                     dtype=torch.uint8, device=dev)
+        # zero-filled once; every propose call leaves it ready for the next.
+        # With top-k it also holds the transposed Bm that the recompute uses
+        # where that pays off.
+        ws = (bd.dspark_markov_propose_workspace_bmt(bd.HEAD_LINEAR, B, gamma, V, A.shape[1], bd._dtype(A), topk)
+              if topk else bd.dspark_markov_propose_workspace(B, gamma, V, topk))
+        self.ws_markov = torch.zeros(ws, dtype=torch.uint8, device=dev)
         self.conf = torch.empty((B, gamma), **f32)
         self.survival = torch.empty((B, gamma), **f32)
         if overlap:

@@ -58,6 +58,19 @@ def test_workspace_queries(L):
     assert st == bd.OK and n >= 16 * 16 * 8
     assert _ws(L.dspark_overlap_tau_workspace, 10, 17, 100)[0] == bd.EUNSUPPORTED
     assert L.dspark_markov_propose_workspace(1, 7, 100, 0, None) == bd.EINVAL
+    # the larger workspace adds the transposed Bm (bf16 with top-k only)
+    f = L.dspark_markov_propose_workspace_bmt
+    st, base = _ws(L.dspark_markov_propose_head_workspace, bd.HEAD_LINEAR, 256, 7, 151936, 256, bd.BF16, 16)
+    st2, n = _ws(f, bd.HEAD_LINEAR, 256, 7, 151936, 256, bd.BF16, 16)
+    assert st == st2 == bd.OK and n == base + 256 * 151936 * 2
+    st, base = _ws(L.dspark_markov_propose_head_workspace, bd.HEAD_LINEAR, 64, 7, 4096, 32, bd.F32, 16)
+    assert _ws(f, bd.HEAD_LINEAR, 64, 7, 4096, 32, bd.F32, 16) == (bd.OK, base)
+    st, base = _ws(L.dspark_markov_propose_head_workspace, bd.HEAD_LINEAR, 64, 7, 4096, 32, bd.BF16, 0)
+    assert _ws(f, bd.HEAD_LINEAR, 64, 7, 4096, 32, bd.BF16, 0) == (bd.OK, base)
+    assert _ws(f, bd.HEAD_LINEAR, 0, 7, 4096, 32, bd.BF16, 16)[0] == bd.EINVAL
+    assert _ws(f, 9, 4, 7, 4096, 32, bd.BF16, 16)[0] == bd.EINVAL
+    assert _ws(f, bd.HEAD_LINEAR, 4, 7, 4096, 32, 5, 16)[0] == bd.EUNSUPPORTED
+    assert f(bd.HEAD_LINEAR, 4, 7, 4096, 32, bd.BF16, 16, None) == bd.EINVAL
 
 
 def test_lm_head_validation(L):

@@ -41,7 +41,7 @@ def test_lm_head_parity(M, H, V, wdtype):
 
 
 # ----------------------------------------------------------------------------- S2-S4
-def _run_markov(U, anchor, A, Bm, wdtype, *, T=0.0, seeds=None, offset=0, topk=0, dump=True):
+def _run_markov(U, anchor, A, Bm, wdtype, *, T=0.0, seeds=None, offset=0, topk=0, dump=True, ws=None):
     dev = require_gpu()
     B, gamma, V = U.shape
     Ud = to_dev(U)
@@ -54,7 +54,7 @@ def _run_markov(U, anchor, A, Bm, wdtype, *, T=0.0, seeds=None, offset=0, topk=0
     sd = to_dev(seeds) if seeds is not None else None
     bd.dspark_markov_propose(Ud, to_dev(anchor), to_dev(A, wdtype), to_dev(Bm, wdtype), tokens,
                              temperature=T, seeds=sd, offset=offset, topk=topk, tok_logit=tl,
-                             lse=ls, topk_idx=ti, topk_prob=tp, logits_out=lo)
+                             lse=ls, topk_idx=ti, topk_prob=tp, logits_out=lo, ws=ws)
     torch.cuda.synchronize()
     out = dict(tokens=tokens.cpu().numpy(), tok_logit=tl.cpu().numpy(), lse=ls.cpu().numpy())
     if topk:
@@ -128,6 +128,27 @@ def test_markov_resident_chain(B, V, r, T, topk, wg, monkeypatch):
     gpu = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=2, topk=topk)
     check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"),
                 temperature=T, seeds=seeds, offset=2, topk=topk)
+
+
+@pytest.mark.parametrize("B,V,r,T,topk", [
+    (32, 5000, 256, 0.0, 16),      # the copy pays off from B*gamma = 12 rows at this V
+    (24, 3000, 128, 0.9, 32),      # sampled, top-32, r = 128
+    (40, 2008, 64, 0.0, 8),        # ragged last tile of the transpose (2008 = 31 * 64 + 24)
+])
+def test_markov_topk_with_transposed_bm(B, V, r, T, topk):
+    # the larger workspace turns on the transposed-Bm recompute of the top-k
+    # candidates; the smaller one keeps the strided recompute: both exact
+    dev = require_gpu()
+    U, anchor, A, Bm = _markov_case(B, V, r, "bf16", seed=9)
+    seeds = np.arange(B, dtype=np.uint64) * 31 + 5 if T > 0 else None
+    small = bd.dspark_markov_propose_workspace(B, 7, V, topk)
+    big = bd.dspark_markov_propose_workspace_bmt(bd.HEAD_LINEAR, B, 7, V, r, bd.BF16, topk)
+    assert big >= small + r * V * 2
+    for n in (big, small):
+        ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+        gpu = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=4, topk=topk, ws=ws)
+        check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"),
+                    temperature=T, seeds=seeds, offset=4, topk=topk)
 
 
 def test_markov_workspace_is_left_ready_for_the_next_call(monkeypatch):
