@@ -60,6 +60,16 @@ __device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
   LseState ls{kNegInf, 0.f};
   ArgState as{kNegInf, 0x7fffffff, 0.f};
   const size_t base = (static_cast<size_t>(b) * a.gamma + j) * a.P;
+  const int row = b * a.gamma + j;
+  // the chain's final key and the time-out word, loaded beside the partials
+  // (vector loads: a scalar load here would be waited for before the
+  // partials' loads are issued)
+  unsigned long long key = 0ull;
+  unsigned mark = 0u;
+  if (from_key) {
+    key = __hip_atomic_load(a.best + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    mark = __hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kMergeThreads) {
     LseState l[kFoldBatch];
     ArgState g[kFoldBatch];
@@ -88,10 +98,8 @@ __device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
     LseState l = red_l[0];
     ArgState s = red_a[0];
     for (int i = 1; i < kMergeThreads / kWave; ++i) { l = lse_merge(l, red_l[i]); s = arg_merge(s, red_a[i]); }
-    const int row = b * a.gamma + j;
     if (from_key) {
-      const bool timed_out = a.sync[0] == a.epoch;
-      a.tokens[row] = timed_out ? -1 : best_index(a.best[row]);
+      a.tokens[row] = mark == a.epoch ? -1 : best_index(key);
       a.best[row] = 0ull;
     } else {
       a.tokens[row] = s.idx;
@@ -954,11 +962,14 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
   __shared__ unsigned long long sel[kMaxTopk];
 
   const unsigned long long* ck = a.cand_key + row * L * k;
+  // the head's load lands with the fold's (stored after it, so that the fold's
+  // loads are not held back by a wait for it)
   const unsigned long long head = tid < L ? ck[static_cast<size_t>(tid) * k] : 0ull;
   if (tid == 0) nlive = 0;
-  hk[tid] = head;
-  fold_request(a, b, j, true);                        // ends with a barrier: hk complete
+  fold_request(a, b, j, true);
   clear_wait_tree(a);
+  hk[tid] = head;
+  __syncthreads();
   if (head != 0ull) {
     int rank = 0, u = 0;
     for (; u + 8 <= L; u += 8) {

@@ -328,16 +328,20 @@ __global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapA
 // ---- one launch for few rows ----------------------------------------------
 // Grid (chunk, row) with the chunk's teacher (and draft) values held in
 // registers across both passes.  Each chunk publishes its online states with
-// device-scope atomics; the last chunk of a row to arrive (known from the
-// row counter's old value) folds them in chunk order into the normalisers
-// and, in dense mode, publishes them tagged with this call's number (the tag
-// releases the row); every chunk of the row then adds its sum of exp(min(t - L_p,
-// d - L_q)), and the last of those folds the sums into alpha.  In candidate
-// mode the row's last arriver gathers the candidates instead and no chunk
-// waits.  The last row to finish computes tau and the aggregates, and clears
-// the counters for the next call.  Dense mode needs every chunk resident at
-// once (the launcher checks the occupancy); the wait is bounded in time, and
-// a wait that runs out marks the call, which then reports NaN for tau.
+// device-scope atomics (both exchanges in flight together) and counts itself
+// in at its row; the row's last arriver (known from the counter's old value)
+// folds the states in chunk order into the normalisers.
+//   Dense mode: the last arriver publishes them tagged with this call's
+//   number (the tag releases the row); every chunk of the row then adds its
+//   sum of exp(min(t - L_p, d - L_q)) and counts itself in again; the row's
+//   last one counts the row in at the call, and the call's last row folds
+//   every row's sums in chunk order into alpha and computes tau.
+//   Candidate mode: the last arriver gathers the candidates and writes alpha;
+//   no chunk waits, and the last row to finish computes tau.
+// The last workgroup also clears the counters for the next call.  Dense mode
+// needs every chunk resident at once (the launcher checks the occupancy); the
+// wait is bounded in time, and a wait that runs out marks the call, which then
+// reports NaN for tau.
 constexpr int kFusedPer = 4;                    // float4 per thread and array
 constexpr int kOvTimeout = 0;                   // word 0: call number of a timed-out wait
 constexpr int kOvRowsDone = 32;
@@ -363,6 +367,71 @@ __device__ __forceinline__ T ld_dev(const T* p) {
 // keep the value live so that the wave waits for the atomic's return here
 __device__ __forceinline__ void wait_for(unsigned long long v) { asm volatile("" ::"v"(v) : "memory"); }
 
+// By one workgroup: tau of every block, accept_rate@i and the mean tau from
+// the alphas al_s and the validity flags va_s of all rows (<= 64 rows).
+__device__ void fused_tau(const OverlapArgs& a, const float* al_s, const unsigned char* va_s, bool timed_out) {
+  const int tid = threadIdx.x, G = a.gamma;
+  const float nan = __builtin_nanf("");
+  if (tid < a.N) {
+    float run = 1.f, tau_n = 1.f;
+    bool has = false;
+    for (int i = 0; i < G; ++i) {
+      has |= va_s[tid * G + i] != 0;
+      run *= al_s[tid * G + i];
+      tau_n += run;
+    }
+    a.tau[tid] = timed_out ? nan : (has ? tau_n : 0.f);
+  }
+  if (tid < G) {   // accept_rate@i over valid slots, blocks in order
+    double s1 = 0.0, s2 = 0.0;
+    for (int n = 0; n < a.N; ++n)
+      if (va_s[n * G + tid]) { s1 += al_s[n * G + tid]; s2 += 1.0; }
+    if (a.accept_rate_at) a.accept_rate_at[tid] = s2 > 0.0 ? s1 / s2 : 0.0;
+  }
+  if (tid == 0 && a.tau_mean) {   // mean tau over blocks with a valid slot, in order
+    double s1 = 0.0, s2 = 0.0;
+    for (int n = 0; n < a.N; ++n) {
+      float run = 1.f, tn = 1.f;
+      bool hv = false;
+      for (int i = 0; i < G; ++i) {
+        hv |= va_s[n * G + i] != 0;
+        run *= al_s[n * G + i];
+        tn += run;
+      }
+      if (hv) { s1 += tn; s2 += 1.0; }
+    }
+    *a.tau_mean = timed_out ? static_cast<double>(nan) : (s2 > 0.0 ? s1 / s2 : 0.0);
+  }
+}
+
+// By wave 0: the teacher and draft log-normalisers of `row` from its chunk
+// states, in chunk order (lanes take chunks lane and lane + 64, then a
+// butterfly, so every lane ends with the same values).
+__device__ __forceinline__ void fold_row_states(const OverlapArgs& a, int row, int lane, float& Lt, float& Ld) {
+  LseState t{kNegInf, 0.f}, d{kNegInf, 0.f};
+  const unsigned long long* rs = a.ws_fused + static_cast<size_t>(row) * a.nchunk * 3;
+  unsigned long long st[2] = {0ull, 0ull}, sd[2] = {0ull, 0ull};   // all loads issued first
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int k = lane + u * kWave;
+    if (k < a.nchunk) { st[u] = ld_dev(rs + 3 * k); sd[u] = ld_dev(rs + 3 * k + 1); }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (lane + u * kWave < a.nchunk) {
+      t = lse_merge(t, LseState{lo_f(st[u]), hi_f(st[u])});
+      d = lse_merge(d, LseState{lo_f(sd[u]), hi_f(sd[u])});
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    t = lse_merge(t, shfl_xor(t, o));
+    d = lse_merge(d, shfl_xor(d, o));
+  }
+  Lt = t.m + logf(t.s);
+  Ld = d.m + logf(d.s);
+}
+
 template <bool DENSE>
 __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
   constexpr int NW = kSplitThreads / kWave;
@@ -370,6 +439,8 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
   __shared__ float red_f[NW];
   __shared__ int flag_s;
   __shared__ float L_s[2];
+  __shared__ float al_s[kFusedFinishRows];
+  __shared__ unsigned char va_s[kFusedFinishRows];
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rows = a.N * a.gamma;
   const bool valid = !a.valid || a.valid[row];
@@ -399,37 +470,21 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
   const LseState rt = block_lse_state<NW>(lt, red_l);
   const LseState rd = block_lse_state<NW>(ld, red_l);
 
-  // 1. publish the chunk states; the row's last arriver folds them
+  // 1. publish the chunk states and count the chunk in at its row
   if (tid == 0) {
-    wait_for(xchg_dev(slot, pack2(rt.m, rt.s)));
-    wait_for(xchg_dev(slot + 1, pack2(rd.m, rd.s)));
+    const unsigned long long o0 = xchg_dev(slot, pack2(rt.m, rt.s));
+    const unsigned long long o1 = xchg_dev(slot + 1, pack2(rd.m, rd.s));
+    wait_for(o0);
+    wait_for(o1);
     flag_s = add_dev(sy + kOvCnt1 + 32 * row, 1u) == static_cast<unsigned>(a.nchunk) - 1u;
   }
   __syncthreads();
-  bool row_done = false;                   // this workgroup has written alpha[row]
-  if (flag_s && w == 0) {
-    LseState t{kNegInf, 0.f}, d{kNegInf, 0.f};
-    const unsigned long long* rs = a.ws_fused + static_cast<size_t>(row) * a.nchunk * 3;
-    unsigned long long st[2] = {0ull, 0ull}, sd[2] = {0ull, 0ull};   // all loads issued first
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k = lane + u * kWave;
-      if (k < a.nchunk) { st[u] = ld_dev(rs + 3 * k); sd[u] = ld_dev(rs + 3 * k + 1); }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (lane + u * kWave < a.nchunk) {
-        t = lse_merge(t, LseState{lo_f(st[u]), hi_f(st[u])});
-        d = lse_merge(d, LseState{lo_f(sd[u]), hi_f(sd[u])});
-      }
-    }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      t = lse_merge(t, shfl_xor(t, o));
-      d = lse_merge(d, shfl_xor(d, o));
-    }
-    const float Lt = t.m + logf(t.s), Ld = d.m + logf(d.s);
-    if constexpr (DENSE) {
+
+  if constexpr (DENSE) {
+    // 2. the row's last arriver publishes the normalisers; every chunk waits for them
+    if (flag_s && w == 0) {
+      float Lt, Ld;
+      fold_row_states(a, row, lane, Lt, Ld);
       if (lane == 0 && valid && a.lse_draft) a.lse_draft[row] = Ld;
       // each normaliser travels with this call's number in one 64-bit word,
       // so the word is its own release flag
@@ -438,19 +493,7 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
             (static_cast<unsigned long long>(a.epoch) << 32) | __float_as_uint(lane == 0 ? Lt : Ld);
         __hip_atomic_store(a.ws_norm + 2 * row + lane, tagged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-    } else {
-      float sc = valid ? candidate_overlap(a, row, Lt, lane, kWave) : 0.f;
-      sc = wave_sum(sc);
-      if (lane == 0) {
-        const float al = valid ? fminf(fmaxf(sc, 0.f), 1.f) : 0.f;
-        wait_for(__hip_atomic_exchange(reinterpret_cast<unsigned*>(a.alpha) + row, __float_as_uint(al),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      }
-      row_done = true;
     }
-  }
-  if constexpr (DENSE) {
-    // 2. wait for the row's normalisers, add this chunk's overlap sum
     if (tid == 0) {
       const unsigned long long t0 = wall_clock64();
       unsigned long long nt, nd;
@@ -468,6 +511,8 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
       L_s[1] = __uint_as_float(static_cast<uint32_t>(nd));
     }
     __syncthreads();
+    // 3. this chunk's overlap sum; the row's last chunk counts the row in, the
+    //    call's last row finishes every row
     const float Lt = L_s[0], Ld = L_s[1];
     float sm = 0.f;
 #pragma unroll
@@ -476,77 +521,62 @@ __global__ __launch_bounds__(kSplitThreads) void overlap_fused(OverlapArgs a) {
     const float tot = block_sum<NW>(sm, red_f);
     if (tid == 0) {
       wait_for(xchg_dev(slot + 2, __float_as_uint(tot)));
-      flag_s = add_dev(sy + kOvCnt2 + 32 * row, 1u) == static_cast<unsigned>(a.nchunk) - 1u;
+      bool last = add_dev(sy + kOvCnt2 + 32 * row, 1u) == static_cast<unsigned>(a.nchunk) - 1u;
+      if (last) last = add_dev(sy + kOvRowsDone, 1u) == static_cast<unsigned>(rows) - 1u;
+      flag_s = last;
     }
     __syncthreads();
-    if (flag_s && w == 0) {
-      const unsigned long long* rs = a.ws_fused + static_cast<size_t>(row) * a.nchunk * 3;
+    if (!flag_s) return;
+    // 4. alpha of every row from its chunk sums in chunk order
+    for (int r = w; r < rows; r += NW) {
+      const unsigned long long* rs = a.ws_fused + static_cast<size_t>(r) * a.nchunk * 3;
       unsigned long long sv[2] = {0ull, 0ull};                       // all loads issued first
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         if (lane + u * kWave < a.nchunk) sv[u] = ld_dev(rs + 3 * (lane + u * kWave) + 2);
       float s2 = __uint_as_float(static_cast<uint32_t>(sv[0])) + __uint_as_float(static_cast<uint32_t>(sv[1]));
       s2 = wave_sum(s2);
+      const bool vr = !a.valid || a.valid[r];
       if (lane == 0) {
-        if (valid && a.ov_sum) a.ov_sum[row] = s2;
-        const float al = valid ? fminf(fmaxf(s2, 0.f), 1.f) : 0.f;
+        if (vr && a.ov_sum) a.ov_sum[r] = s2;
+        const float al = vr ? fminf(fmaxf(s2, 0.f), 1.f) : 0.f;
+        a.alpha[r] = al;
+        al_s[r] = al;
+        va_s[r] = vr;
+      }
+    }
+    __syncthreads();
+  } else {
+    // 2. the row's last arriver: normalisers, candidate overlap, alpha
+    bool row_done = false;                       // this workgroup has written alpha[row]
+    if (flag_s && w == 0) {
+      float Lt, Ld;
+      fold_row_states(a, row, lane, Lt, Ld);
+      float sc = valid ? candidate_overlap(a, row, Lt, lane, kWave) : 0.f;
+      sc = wave_sum(sc);
+      if (lane == 0) {
+        const float al = valid ? fminf(fmaxf(sc, 0.f), 1.f) : 0.f;
         wait_for(__hip_atomic_exchange(reinterpret_cast<unsigned*>(a.alpha) + row, __float_as_uint(al),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       }
       row_done = true;
     }
-  }
-  // 3. the last row to finish computes tau and clears the counters
-  __syncthreads();
-  if (tid == 0) flag_s = 0;
-  __syncthreads();
-  if (row_done && tid == 0) flag_s = add_dev(sy + kOvRowsDone, 1u) == static_cast<unsigned>(rows) - 1u;
-  __syncthreads();
-  if (!flag_s) return;
-  // tau of every block (rows <= 64: one alpha per thread, all loaded at once)
-  __shared__ float al_s[kFusedFinishRows];
-  __shared__ unsigned char va_s[kFusedFinishRows];
-  const int G = a.gamma;
-  if (tid < rows) {
-    al_s[tid] = __uint_as_float(ld_dev(reinterpret_cast<const unsigned*>(a.alpha) + tid));
-    va_s[tid] = a.valid ? a.valid[tid] : 1;
-  }
-  __syncthreads();
-  const bool timed_out = ld_dev(sy + kOvTimeout) == a.epoch;     // a wait ran out: results invalid
-  const float nan = __builtin_nanf("");
-  float tau_n = 0.f;
-  bool has = false;
-  if (tid < a.N) {
-    float run = 1.f;
-    tau_n = 1.f;
-    for (int i = 0; i < G; ++i) {
-      has |= va_s[tid * G + i] != 0;
-      run *= al_s[tid * G + i];
-      tau_n += run;
+    // 3. the last row to finish computes tau
+    __syncthreads();
+    if (tid == 0) flag_s = 0;
+    __syncthreads();
+    if (row_done && tid == 0) flag_s = add_dev(sy + kOvRowsDone, 1u) == static_cast<unsigned>(rows) - 1u;
+    __syncthreads();
+    if (!flag_s) return;
+    if (tid < rows) {
+      al_s[tid] = __uint_as_float(ld_dev(reinterpret_cast<const unsigned*>(a.alpha) + tid));
+      va_s[tid] = a.valid ? a.valid[tid] : 1;
     }
-    a.tau[tid] = timed_out ? nan : (has ? tau_n : 0.f);
+    __syncthreads();
   }
-  if (tid < G) {   // accept_rate@i over valid slots, blocks in order
-    double s1 = 0.0, s2 = 0.0;
-    for (int n = 0; n < a.N; ++n)
-      if (va_s[n * G + tid]) { s1 += al_s[n * G + tid]; s2 += 1.0; }
-    if (a.accept_rate_at) a.accept_rate_at[tid] = s2 > 0.0 ? s1 / s2 : 0.0;
-  }
-  if (tid == 0 && a.tau_mean) {   // mean tau over blocks with a valid slot, in order
-    double s1 = 0.0, s2 = 0.0;
-    for (int n = 0; n < a.N; ++n) {
-      float run = 1.f, tn = 1.f;
-      bool hv = false;
-      for (int i = 0; i < G; ++i) {
-        hv |= va_s[n * G + i] != 0;
-        run *= al_s[n * G + i];
-        tn += run;
-      }
-      if (hv) { s1 += tn; s2 += 1.0; }
-    }
-    *a.tau_mean = timed_out ? static_cast<double>(nan) : (s2 > 0.0 ? s1 / s2 : 0.0);
-  }
-  // clear the counters used by this call (the release flags hold call numbers)
+  fused_tau(a, al_s, va_s, ld_dev(sy + kOvTimeout) == a.epoch);
+  // clear the counters used by this call (the release words and the time-out
+  // word hold call numbers)
   if (tid < rows) {
     sy[kOvCnt1 + 32 * tid] = 0u;
     sy[kOvCnt2 + 32 * tid] = 0u;
