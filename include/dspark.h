@@ -141,7 +141,10 @@ dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int64_t r, dspa
  * A token of -1 marks a call whose resident chain (see
  * dspark_markov_propose_plan) waited past its time bound (100 ms per
  * position) for a workgroup that had not started, which only other long
- * work on the device can cause; that call's outputs are invalid.
+ * work on the device can cause; that call's outputs are invalid.  On the
+ * per-position path -1 marks a row with no orderable value (every U~_j[v]
+ * NaN).  Rows of A are gathered with the previous token clamped into
+ * [0, V), so invalid anchors or -1 tokens give wrong but bounded reads.
  * Requirements: B, gamma, V, r > 0; gamma <= 16; topk <= 32 and topk <= V;
  * V <= 2^31 - 1.  DSPARK_BF16: r % 32 == 0, r <= 1024, V % 8 == 0.
  * DSPARK_F32: r <= 1024.  Otherwise EUNSUPPORTED.  T must be finite and >= 0.
@@ -320,6 +323,7 @@ dspark_status_t dspark_prefix_schedule(const float* survival, int64_t R, int64_t
  *
  *   U            [B, gamma, V] float32   base logits (the LM head's output)
  *   prev_tokens  [B, gamma] int32        previous token of each position, in [0, V)
+ *                                        (out-of-range values are clamped into it)
  *   A [V, r], Bm [r, V]  dtype wdt       Markov tables, as for dspark_markov_propose
  *   logits_out   [B, gamma, V] float32   (out) corrected logits U~
  * bf16 tables with r in {32, 64, 128, 256}, V % 8 == 0 and 16-byte aligned

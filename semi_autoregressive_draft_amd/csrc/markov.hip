@@ -102,7 +102,7 @@ __device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
       a.tokens[row] = mark == a.epoch ? -1 : best_index(key);
       a.best[row] = 0ull;
     } else {
-      a.tokens[row] = s.idx;
+      a.tokens[row] = (s.idx >= 0 && s.idx < a.V) ? s.idx : -1;   // -1: no orderable value (NaN row)
     }
     if (a.tok_logit) a.tok_logit[row] = s.x;
     if (a.lse) a.lse[row] = l.m + logf(l.s);
@@ -1218,7 +1218,7 @@ __global__ __launch_bounds__(256) void block_logits_generic(const float* __restr
                                                             int r, float* __restrict__ out) {
   __shared__ float arow[kMaxRank];
   const int m = blockIdx.y, tid = threadIdx.x;
-  const int pv = prev[m];
+  const int pv = min(max(prev[m], 0), V - 1);         // the gathered row stays inside A
   for (int k = tid; k < r; k += 256) arow[k] = to_f32(A[static_cast<size_t>(pv) * r + k]);
   __syncthreads();
   const int v = blockIdx.x * 256 + tid;

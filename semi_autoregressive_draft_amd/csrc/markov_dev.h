@@ -59,9 +59,12 @@ __device__ __forceinline__ void load_chunk(const uint16_t* Bm, size_t V, int col
 }
 
 // x_{j-1} of request b on the per-position chain: the anchor for j == 0, else
-// the token the merge of position j-1 wrote
+// the token the merge of position j-1 wrote, clamped into [0, V) so that the
+// gathered table row stays inside the table (a -1 token, from a row with no
+// orderable value, and an out-of-range anchor read row 0 or V - 1 instead)
 __device__ __forceinline__ int prev_token(const StepArgs& a, int b, int j) {
-  return j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + j - 1];
+  const int t = j == 0 ? a.anchor[b] : a.tokens[b * a.gamma + j - 1];
+  return min(max(t, 0), a.V - 1);
 }
 
 // The A-operand row of (request b, position j): row x_{j-1} of A, or, with a

@@ -223,6 +223,24 @@ def test_markov_ties_take_lowest_index_and_slow_topk_path(chain_path):
     assert np.allclose(gpu["lse"], np.log(V), atol=1e-5)
 
 
+@pytest.mark.parametrize("B,V,r,topk", [(20, 2008, 64, 8), (3, 1024, 32, 4)])
+def test_markov_nan_row_keeps_gathers_inside_the_table(B, V, r, topk):
+    # per-position chain (wide step for B > 16, the small-batch step below): a
+    # request whose first row is all NaN has no orderable value; its token is
+    # -1 or some column, the next position gathers a table row clamped into
+    # [0, V), and every other request is unaffected
+    U, anchor, A, Bm = _markov_case(B, V, r, "bf16", seed=12)
+    Un = U.copy()
+    Un[1, 0, :] = np.nan
+    ref = _run_markov(U, anchor, A, Bm, "bf16", topk=topk, dump=False)
+    got = _run_markov(Un, anchor, A, Bm, "bf16", topk=topk, dump=False)
+    t = got["tokens"][1]
+    assert np.all((t >= -1) & (t < V)) and np.all(t[1:] >= 0)
+    others = [b for b in range(B) if b != 1]
+    assert np.array_equal(got["tokens"][others], ref["tokens"][others])
+    assert np.array_equal(got["topk_idx"][others], ref["topk_idx"][others])
+
+
 def test_markov_zero_transition_is_parallel_argmax():
     B, V, r = 4, 3000, 64
     U = synth.base_logits(B, V, seed=8)
