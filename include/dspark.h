@@ -132,7 +132,8 @@ dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int64_t r, dspa
  *   tok_logit  [B, gamma] float32      U~_j at the drafted token (may be NULL)
  *   lse        [B, gamma] float32      log sum_v exp U~_j[v] (may be NULL);
  *                                      exp(tok_logit - lse) is q_j(x_j) at T = 1
- *   topk_idx   [B, gamma, topk] int32  candidate ids (NULL iff topk == 0)
+ *   topk_idx   [B, gamma, topk] int32  candidate ids (NULL iff topk == 0); -1 where a
+ *                                      row has fewer than topk orderable values (NaN)
  *   topk_prob  [B, gamma, topk] float32 softmax of U~ over the candidates
  *   logits_out [B, gamma, V] float32   U~ itself (may be NULL; costs B*gamma*V*4
  *                                      bytes of extra writes)
@@ -258,7 +259,8 @@ dspark_status_t dspark_overlap_tau_workspace(int64_t N, int64_t gamma, int64_t V
  *   teacher    [N, gamma, V] float32   teacher logits, p = softmax(teacher)
  *   draft      [N, gamma, V] float32   draft logits, q = softmax(draft)  -- dense mode
  *              or NULL                 -- candidate mode, then:
- *   cand_idx   [N, gamma, k] int32     candidate ids (distinct, in [0, V))
+ *   cand_idx   [N, gamma, k] int32     candidate ids (distinct, in [0, V)); an id outside
+ *                                      [0, V) marks no candidate and adds nothing
  *   cand_prob  [N, gamma, k] float32   q' on the candidates
  *   k          candidate count (0 in dense mode)
  *   valid      [N, gamma] uint8 or NULL (all valid)

@@ -738,6 +738,10 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
 
   const WT* ar = a_operand_row<WT>(a, b, j);
   for (int i = tid; i < a.r; i += kTopkThreads) arow_s[i] = to_f32(ar[i]);
+  if (tid < kMaxTopk) {            // a row without k orderable values (NaN) reports -1 ids
+    selv[tid] = kNegInf;
+    seli[tid] = -1;
+  }
   const float* pm = a.p_m + row * a.P;
   const float* sm = a.segmax + row * a.S;
   const float* urow = a.U + row * static_cast<size_t>(a.V);

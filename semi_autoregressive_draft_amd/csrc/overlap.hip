@@ -85,12 +85,15 @@ __device__ float block_sum(float v, float* red) {
 }
 
 // candidate-set overlap of one row: this thread's share (candidates first,
-// first + stride, ...) of the sum over the k candidates of min(p, q')
+// first + stride, ...) of the sum over the k candidates of min(p, q'); an id
+// outside [0, V) (no candidate) adds nothing and reads nothing
 __device__ float candidate_overlap(const OverlapArgs& a, int row, float Lt, int first, int stride) {
   float s = 0.f;
   for (int c = first; c < a.k; c += stride) {
     const size_t ci = static_cast<size_t>(row) * a.k + c;
-    const float p = __expf(a.teacher[static_cast<size_t>(row) * a.V + a.cand_idx[ci]] - Lt);
+    const int id = a.cand_idx[ci];
+    if (id < 0 || id >= a.V) continue;
+    const float p = __expf(a.teacher[static_cast<size_t>(row) * a.V + id] - Lt);
     s += fminf(p, a.cand_prob[ci]);
   }
   return s;

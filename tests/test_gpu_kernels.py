@@ -239,6 +239,8 @@ def test_markov_nan_row_keeps_gathers_inside_the_table(B, V, r, topk):
     others = [b for b in range(B) if b != 1]
     assert np.array_equal(got["tokens"][others], ref["tokens"][others])
     assert np.array_equal(got["topk_idx"][others], ref["topk_idx"][others])
+    ids = got["topk_idx"][1]                          # -1 where no candidate was ordered
+    assert np.all((ids >= -1) & (ids < V))
 
 
 def test_markov_zero_transition_is_parallel_argmax():
@@ -385,6 +387,25 @@ def test_overlap_candidates_parity(k, N):
     idx = order.astype(np.int32)
     got = _run_overlap(teacher.astype(np.float32), idx=idx, prob=prob)
     a_raw = o.overlap_sparse(t64, idx, prob.astype(np.float64))
+    assert a_raw.max() > 0.05
+    _check_tau(got, a_raw, None)
+
+
+@pytest.mark.parametrize("N", [5, 300])           # single launch; one workgroup per row
+def test_overlap_candidates_skip_ids_outside_the_vocabulary(N):
+    # an id outside [0, V) marks no candidate: it adds nothing, as a candidate
+    # of probability 0 would, and reads no teacher entry
+    V, k = 5000, 16
+    teacher, _ = synth.overlap_inputs(N, V, 1.0, seed=4)
+    teacher = teacher * 3.0
+    t64 = teacher.astype(np.float64)
+    idx = np.argsort(-t64, axis=-1)[..., :k].astype(np.int32)
+    _, prob = synth.candidates(N, V, k, seed=4)
+    bad = np.zeros(idx.shape, dtype=bool)
+    bad[..., -3:] = True                              # the last three of every list
+    idx_bad = np.where(bad, np.where(np.arange(k) % 2 == 0, -1, V), idx).astype(np.int32)
+    got = _run_overlap(teacher.astype(np.float32), idx=idx_bad, prob=prob)
+    a_raw = o.overlap_sparse(t64, idx, np.where(bad, 0.0, prob.astype(np.float64)))
     assert a_raw.max() > 0.05
     _check_tau(got, a_raw, None)
 
