@@ -36,12 +36,16 @@
 // The wait tree and the keys are zero when a call starts: the workspace is
 // zero-filled before its first use and the finish kernels clear both again.
 //
-// With top-k, the epilogue leaves U~_j in LDS (over the U_j rows it read, two
-// buffers alternating by position), and while wave 0 walks the wait tree the
-// other seven waves select this workgroup's k best U~_j per request into a
+// The epilogue leaves U~_j in LDS (over the U_j rows it read, two buffers
+// alternating by position).  While wave 0 walks the wait tree, with top-k
+// the list waves select this workgroup's k best U~_j per request into a
 // sorted list of 64-bit order keys (best_key: value descending, index
-// ascending; 0 pads lists of workgroups with fewer than k live columns); the
-// finish kernel merges the lists exactly.
+// ascending; 0 pads lists of workgroups with fewer than k live columns; the
+// finish kernel merges the lists exactly), and the helper waves fetch
+// U_{j+1}, copy U~_j to the dump and store the workgroup's partial and the
+// previous position's lists.  The waves that lead the next position (wave 0
+// and the list waves) issue no plain stores, so no wait for store
+// completion falls on them.
 //
 // Group layout: group G covers columns 64G .. 64G+63 and belongs to workgroup
 // G mod nwg.  For each 32-row chunk q of r, lane (g = lane/16, n = lane%16)
@@ -66,7 +70,7 @@ constexpr int kResThreads = 512;
 constexpr int kResWaves = kResThreads / kWave;
 constexpr int kResCols = 64;                  // vocabulary columns per group
 constexpr int kResMaxB = kResidentMaxB;
-constexpr size_t kResLdsMax = 148 * 1024;     // dynamic LDS: LDS groups + U_j rows (static: ~11 KB)
+constexpr size_t kResLdsMax = 144 * 1024;     // dynamic LDS: LDS groups + U_j rows (static: ~15 KB)
 
 struct ResidentArgs {
   int nwg;             // workgroups (one per compute unit)
@@ -126,9 +130,14 @@ __device__ void chain_tree(const StepArgs& a, const ResidentArgs& ra, int wg, in
     int top = 0;
     if (lane == 0) top = atomic_add_dev(sy + kSyncTopCnt, 1u) == static_cast<unsigned>(ng) * (j + 1) - 1;
     top = __shfl(top, 0);
-    if (top && lane < ng)                                // all groups in: release them
-      __hip_atomic_store(sy + kSyncRelease + 64 * lane, static_cast<unsigned>(j + 1), __ATOMIC_RELAXED,
+    if (top && lane < ng) {                              // all groups in: release them
+      // the lane's flag address, formed here: hoisted out of the position
+      // loop it would be spilled and reloaded on this path
+      unsigned off = 64u * static_cast<unsigned>(lane);
+      asm volatile("" : "+v"(off));
+      __hip_atomic_store(sy + kSyncRelease + off, static_cast<unsigned>(j + 1), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (!wait) return;
   if (lane == 0) {
@@ -167,7 +176,6 @@ __device__ __forceinline__ void resident_epilogue(const StepArgs& a, const f32x4
       for (int c = 0; c < 4; ++c) x[c] = acc[c][ii] + u[c];
       const f32x4 xv{x[0], x[1], x[2], x[3]};
       *up = xv;
-      if (a.logits_out) *reinterpret_cast<f32x4*>(a.logits_out + row * V + col) = xv;
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) x[c] = kNegInf;
@@ -232,9 +240,8 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 }
 
 __device__ void local_topk(const StepArgs& a, const ResidentArgs& ra, const float* xs, int b, int wg, int lane,
-                           float* lmx, unsigned long long* ck) {
+                           float* lmx, unsigned long long* ck, unsigned long long* out) {
   const int ncol = ra.T * kResCols, k = a.topk;
-  unsigned long long* out = a.cand_key + ((static_cast<size_t>(b) * a.gamma + a.j) * ra.nwg + wg) * k;
   // U~ of the lane's i-th column (kNegInf and column -1 when dead)
   auto get = [&](int i, float& v, int& col) {
     const int gid = wg + ra.nwg * i;
@@ -317,6 +324,20 @@ __device__ void local_topk(const StepArgs& a, const ResidentArgs& ra, const floa
   }
 }
 
+// Candidate list (k keys in LDS, written by this wave) of request b at
+// position j to its workspace slot: one store per lane < k.
+__device__ __forceinline__ void flush_list(const StepArgs& a, const ResidentArgs& ra, const unsigned long long* src,
+                                           int b, int j, int wg, int lane) {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" : "+v"(lane));        // per-lane address math stays here, not hoisted and spilled
+  if (lane < a.topk) a.cand_key[((static_cast<size_t>(b) * a.gamma + j) * ra.nwg + wg) * a.topk + lane] = src[lane];
+}
+
+// Candidate lists stay in LDS for one position when all of a position's
+// lists fit (B k keys): a wave stores position j's lists while the wait of
+// position j + 1 runs, so no barrier of the chain waits for those stores.
+constexpr int kListKeys = (kResWaves - 1) * kMaxTopk;
+
 template <int KCH, int QN, bool SAMPLE>
 __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, ResidentArgs ra) {
   constexpr int RGW = 8 / KCH;   // register groups per wave (128 VGPRs of operands)
@@ -326,6 +347,7 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
   __shared__ int prev_s[kResMaxB];
   __shared__ float ltk_max[kResWaves - 1][kWave];        // local top-k scratch of waves 1..7
   __shared__ unsigned long long ltk_key[kResWaves - 1][kLocCap];
+  __shared__ unsigned long long lst_s[2][kListKeys];    // candidate lists: [position parity][b * k ..]
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -339,24 +361,50 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
   auto gid_of = [&](int t) { return wg + ra.nwg * t; };
   auto has = [&](int t) { return t < ra.T && gid_of(t) < ra.G; };
 
-  // U_j rows of this workgroup's groups, [t][b][64] floats, into buffer j % 2
-  // by DMA: each wave instruction moves 4 rows of 256 bytes (lane i: row
-  // 4k + i/16, bytes 16 (i%16)); wave wv of nwv takes instructions wv, wv +
-  // nwv, ...
+  // U_j rows of this workgroup's groups, [t][b][64] floats, into buffer j % 2,
+  // through registers: wave wv of nwv moves 16-byte pieces p = 64 (wv + nwv i)
+  // + lane (row p / 16, bytes 16 (p % 16)), four loads in flight before their
+  // LDS writes.  (An LDS DMA here would make the compiler wait for every
+  // global access of the wave, stores included, before its next LDS read.)
   const int nrows = ra.T * a.B;
-  auto issue_u = [&](int j, int wv, int nwv) {
+  auto fetch_u = [&](int j, int wv, int nwv) {
     float* lds_u = lds_u0 + (j & 1) * ubuf;
-    for (int k = wv; 4 * k < nrows; k += nwv) {
-      const int rr = 4 * k + (lane >> 4);
-      const int t = rr / a.B, b = rr - t * a.B;
-      const int col = gid_of(t) * kResCols + 4 * (lane & 15);
-      if (rr < nrows && has(t) && col < a.V) {
-        const float* src = a.U + (static_cast<size_t>(b) * a.gamma + j) * V + col;
-        __builtin_amdgcn_global_load_lds(src, reinterpret_cast<void*>(lds_u + 4 * k * kResCols), 16, 0, 0);
+    const int np = nrows * (kResCols / 4);
+    int ln = lane;                      // opaque: keeps the per-lane address math in here
+    asm volatile("" : "+v"(ln));
+    for (int p0 = kWave * wv; p0 < np; p0 += 4 * kWave * nwv) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + u * kWave * nwv + ln;
+        const int rr = p >> 4, t = rr / a.B, b = rr - t * a.B;
+        const int col = gid_of(t) * kResCols + 4 * (p & 15);
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};      // dead groups and columns past V: never read
+        if (p < np && has(t) && col < a.V)
+          v[u] = *reinterpret_cast<const f32x4*>(a.U + (static_cast<size_t>(b) * a.gamma + j) * V + col);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + u * kWave * nwv + ln;
+        if (p < np) *reinterpret_cast<f32x4*>(lds_u + 4 * p) = v[u];
       }
     }
   };
-  issue_u(0, w, kResWaves);
+  // U~_j (in buffer j % 2 after the epilogue) to the dump, the same pieces
+  auto dump_u = [&](int j, int wv, int nwv) {
+    const float* lds_u = lds_u0 + (j & 1) * ubuf;
+    const int np = nrows * (kResCols / 4);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    for (int p = kWave * wv + ln; p < np; p += kWave * nwv) {
+      const int rr = p >> 4, t = rr / a.B, b = rr - t * a.B;
+      const int col = gid_of(t) * kResCols + 4 * (p & 15);
+      if (has(t) && col < a.V)
+        *reinterpret_cast<f32x4*>(a.logits_out + (static_cast<size_t>(b) * a.gamma + j) * V + col) =
+            *reinterpret_cast<const f32x4*>(lds_u + 4 * p);
+    }
+  };
+  fetch_u(0, w, kResWaves);
 
   // Bm share: register groups t = w*RGW + s, LDS group t = nreg + w
   u32x4 dreg[RGW][KCH][4];
@@ -378,18 +426,19 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
       for (int c = 0; c < 4; ++c) lds_ops[((w * KCH + q) * 4 + c) * kWave + lane] = op[c];
     }
   }
-  __syncthreads();   // LDS operands written, U_0 landed (the barrier waits for all loads)
+  if (w == 0 && lane < a.B) prev_s[lane] = a.anchor[lane];   // x_{-1}
+  __syncthreads();   // LDS operands, U_0 and the anchors written
 
   for (int j = 0; j < a.gamma; ++j) {
     a.j = j;
     float* lds_u = lds_u0 + (j & 1) * ubuf;
-    int prev = n < a.B ? (j == 0 ? a.anchor[n] : prev_s[n]) : 0;
+    int prev = n < a.B ? prev_s[n] : 0;              // LDS only: no global load ahead of the gather
     prev = min(max(prev, 0), a.V - 1);              // guard of the gathered row
+    // lanes of requests n >= B gather row 0: their products are never read
     u32x4 av[KCH];
 #pragma unroll
     for (int q = 0; q < KCH; ++q)
-      av[q] = n < a.B ? *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(prev) * a.r + 32 * q + 8 * g)
-                      : u32x4{0u, 0u, 0u, 0u};
+      av[q] = *reinterpret_cast<const u32x4*>(A + static_cast<size_t>(prev) * a.r + 32 * q + 8 * g);
     ArgState best[QN];
     LseState run[QN];
 #pragma unroll
@@ -452,14 +501,47 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
           wlse[w][4 * g + ii] = run[ii];
         }
     }
-    res_lds_barrier();                                // wave bests in LDS; U_j no longer read
-    // waves 1..7 fetch U_{j+1}; not wave 0: a wave's LDS reads after its own
-    // DMA into LDS wait for the DMA to land (the compiler cannot tell the
-    // buffers apart), and wave 0's reads of the wave bests lead the wait tree
-    if (j + 1 < a.gamma && w > 0) issue_u(j + 1, w - 1, kResWaves - 1);
-    if (a.topk > 0 && w > 0) {                       // local candidate lists, beside the wait
-      for (int b = w - 1; b < a.B; b += kResWaves - 1)
-        local_topk(a, ra, lds_u, b, wg, lane, ltk_max[w - 1], ltk_key[w - 1]);
+    res_lds_barrier();                                // wave bests and U~_j in LDS
+    // Beside wave 0's wait: list waves 1..nl build this position's candidate
+    // lists (LDS only); helper waves (the rest of 1..7) fetch U_{j+1), copy
+    // U~_j from LDS to the dump, write this workgroup's partial and store
+    // position j - 1's lists.  Every plain store of the position is a helper
+    // wave's: the compiler makes a wave wait for its outstanding stores
+    // before it reuses their data registers, which keeps those waits off the
+    // waves that lead the next position.  With lists on every wave (B >= 7)
+    // the list waves are also the helpers and store their lists at once.
+    const int nl = a.topk > 0 ? min(a.B, kResWaves - 1) : 0;
+    const int nh = nl < kResWaves - 1 ? kResWaves - 1 - nl : kResWaves - 1;   // helper waves
+    const int hw = nl < kResWaves - 1 ? w - 1 - nl : w - 1;                  // this wave's helper index
+    const bool defer = nl > 0 && nl < kResWaves - 1 && a.B * a.topk <= kListKeys;
+    if (w > 0 && hw >= 0) {
+      if (j + 1 < a.gamma) fetch_u(j + 1, hw, nh);
+      if (a.logits_out) dump_u(j, hw, nh);
+      if (hw == nh - 1 && lane < a.B) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        ArgState s = wbest[0][ln];
+        LseState l = wlse[0][ln];
+        for (int v = 1; v < kResWaves; ++v) {
+          s = arg_merge(s, wbest[v][ln]);
+          l = lse_merge(l, wlse[v][ln]);
+        }
+        const size_t pq = (static_cast<size_t>(ln) * a.gamma + j) * a.P + wg;
+        a.p_m[pq] = l.m;
+        a.p_s[pq] = l.s;
+        a.p_score[pq] = s.score;
+        a.p_idx[pq] = s.idx;
+        a.p_x[pq] = s.x;
+      }
+      if (defer && j > 0)
+        for (int b = hw; b < a.B; b += nh) flush_list(a, ra, &lst_s[(j - 1) & 1][b * a.topk], b, j - 1, wg, lane);
+    }
+    if (w > 0 && w <= nl) {                          // local candidate lists
+      for (int b = w - 1; b < a.B; b += nl) {
+        unsigned long long* dst = defer ? &lst_s[j & 1][b * a.topk] : &lst_s[0][(w - 1) * kMaxTopk];
+        local_topk(a, ra, lds_u, b, wg, lane, ltk_max[w - 1], ltk_key[w - 1], dst);
+        if (!defer) flush_list(a, ra, dst, b, j, wg, lane);
+      }
     }
     if (w == 0) {
       unsigned long long key = 0;
@@ -471,18 +553,21 @@ __global__ __launch_bounds__(kResThreads) void markov_resident(StepArgs a, Resid
           l = lse_merge(l, wlse[v][lane]);
         }
         key = best_key(s.score, s.idx);
-        const size_t pq = (static_cast<size_t>(lane) * a.gamma + j) * a.P + wg;
-        a.p_m[pq] = l.m;
-        a.p_s[pq] = l.s;
-        a.p_score[pq] = s.score;
-        a.p_idx[pq] = s.idx;
-        a.p_x[pq] = s.x;
       }
       const bool more = j + 1 < a.gamma;
       chain_tree(a, ra, wg, j, key, lane, more);
       if (more && lane < a.B) prev_s[lane] = best_index(load_dev(a.best + lane * a.gamma + j));
     }
-    __syncthreads();                                  // prev_s visible; U_{j+1} landed; lists done
+    // LDS only: U_{j+1} and prev_s written; the workgroup's stores (partials,
+    // lists, U~ dump) stay in flight
+    res_lds_barrier();
+  }
+  {                                                  // the last position's deferred lists
+    const int nl = a.topk > 0 ? min(a.B, kResWaves - 1) : 0;
+    if (nl > 0 && nl < kResWaves - 1 && a.B * a.topk <= kListKeys && w > nl) {
+      const int nh = kResWaves - 1 - nl, hw = w - 1 - nl;
+      for (int b = hw; b < a.B; b += nh) flush_list(a, ra, &lst_s[(a.gamma - 1) & 1][b * a.topk], b, a.gamma - 1, wg, lane);
+    }
   }
 }
 
