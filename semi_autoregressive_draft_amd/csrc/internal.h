@@ -20,6 +20,18 @@ constexpr int kMaxLists = 256;   // workgroups of the resident chain
 constexpr int kResidentMaxB = 16;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
 constexpr int kSyncWords = 12 * 1024;   // 48 KB: the resident chain's wait tree (zero at launch)
+// Wait-tree layout in the sync block (32-bit words; counters and flags each on
+// their own 256-byte line): time-out flag (holds call numbers, never
+// cleared), group counters, top counter, group release flags, then the group
+// keys [position][group][request] (64-bit).  Groups are kFanIn workgroups.
+constexpr int kFanIn = 16;
+constexpr int kSyncTimeout = 0;
+constexpr int kSyncGroupCnt = 64;                       // + 64 * group
+constexpr int kSyncTopCnt = kSyncGroupCnt + 64 * kFanIn;
+constexpr int kSyncRelease = kSyncTopCnt + 64;          // + 64 * group
+constexpr int kSyncKeys = 4096;                         // word offset of the group keys
+static_assert(kSyncRelease + 64 * kFanIn <= kSyncKeys, "wait-tree layout");
+static_assert(kSyncKeys + 2 * kMaxGamma * kFanIn * kResidentMaxB <= kSyncWords, "wait-tree size");
 constexpr int kOvSyncWords = 8192;      // 32 KB: the single-launch overlap's counters (zero at launch)
 
 // Arguments of one Markov position (step + merge kernels).

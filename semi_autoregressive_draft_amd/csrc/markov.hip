@@ -622,11 +622,28 @@ __global__ __launch_bounds__(256) void markov_step_f32(StepArgs a) {
 // The per-position merge, and the fold of every (request, position) after the
 // resident chain.  After the resident chain the finish kernels (markov_fold,
 // markov_topk_lists) leave the wait tree zeroed for the next call: their
-// workgroups clear it in slices (all of its readers have finished); word 0,
-// the time-out mark, holds a call number and is never cleared.
+// workgroups clear, in slices, exactly the words this call's chain used (all
+// of their readers have finished): the counter and release flag of each
+// group of kFanIn workgroups, the top counter, and the keys of the call's
+// positions, groups and requests.  Word 0, the time-out mark, holds a call
+// number and is never cleared.
 __device__ __forceinline__ void clear_wait_tree(const StepArgs& a) {
   const int L = blockIdx.x * a.gamma + blockIdx.y, n = a.B * a.gamma;
-  for (int i = L * blockDim.x + threadIdx.x + 1; i < kSyncWords; i += n * blockDim.x) a.sync[i] = 0u;
+  const int ng = (a.nlist + kFanIn - 1) / kFanIn;
+  const int total = 2 * ng + 1 + a.gamma * ng * a.B;
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(a.sync + kSyncKeys);
+  for (int i = L * blockDim.x + threadIdx.x; i < total; i += n * blockDim.x) {
+    if (i < ng) {
+      a.sync[kSyncGroupCnt + 64 * i] = 0u;
+    } else if (i < 2 * ng) {
+      a.sync[kSyncRelease + 64 * (i - ng)] = 0u;
+    } else if (i == 2 * ng) {
+      a.sync[kSyncTopCnt] = 0u;
+    } else {
+      const int q = i - 2 * ng - 1, b = q % a.B, r = q / a.B, grp = r % ng, j = r / ng;
+      keys[(j * kFanIn + grp) * kResidentMaxB + b] = 0ull;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kMergeThreads) void markov_merge(StepArgs a) {
@@ -954,15 +971,33 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
 // k <= V).
 constexpr int kMaxMergeCand = kMaxTopk * (kMaxTopk + 1) / 2;
 
+// Number of keys[0..n) greater than x, for keys in LDS (16-byte aligned) read
+// by every thread alike: two keys per 16-byte load, 32 keys per batch in
+// flight (the count is bound by LDS latency, not by the compares).
+__device__ __forceinline__ int count_greater(const unsigned long long* keys, int n, unsigned long long x) {
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  const u64x2* k2 = reinterpret_cast<const u64x2*>(keys);
+  int c = 0, f = 0;
+  for (; f + 32 <= n; f += 32) {
+    u64x2 v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = k2[f / 2 + q];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) c += (v[q].x > x) + (v[q].y > x);
+  }
+  for (; f < n; ++f) c += keys[f] > x;
+  return c;
+}
+
 __global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int b = blockIdx.x, j = blockIdx.y;
   const int k = a.topk, L = a.nlist;
   const size_t row = static_cast<size_t>(b) * a.gamma + j;
-  __shared__ unsigned long long hk[kMaxLists];
+  __shared__ __align__(16) unsigned long long hk[kMaxLists];
   __shared__ int act[kMaxTopk];
   __shared__ int nlive;
-  __shared__ unsigned long long mk[kMaxMergeCand];
+  __shared__ __align__(16) unsigned long long mk[kMaxMergeCand];
   __shared__ unsigned long long sel[kMaxTopk];
 
   const unsigned long long* ck = a.cand_key + row * L * k;
@@ -972,21 +1007,18 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
   if (tid == 0) nlive = 0;
   fold_request(a, b, j, true);
   clear_wait_tree(a);
+  // from here on only LDS is shared between threads: the barriers leave the
+  // global stores (outputs, wait-tree clearing) in flight
   hk[tid] = head;
-  __syncthreads();
+  lds_barrier();
   if (head != 0ull) {
-    int rank = 0, u = 0;
-    for (; u + 8 <= L; u += 8) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) rank += hk[u + q] > head;
-    }
-    for (; u < L; ++u) rank += hk[u] > head;
+    const int rank = count_greater(hk, L, head);
     if (rank < k) {
       act[rank] = tid;
       atomicAdd(&nlive, 1);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // candidates of the list of head rank r: entries p < k - r, stored from
   // offset r k - r (r - 1) / 2
   const int na = nlive;
@@ -997,18 +1029,13 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
     const int p = e - (r * k - r * (r - 1) / 2);
     mk[e] = ck[static_cast<size_t>(act[r]) * k + p];
   }
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < nc; e += kTopkThreads) {
     const unsigned long long key = mk[e];
-    int rank = 0, f = 0;
-    for (; f + 8 <= nc; f += 8) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) rank += mk[f + q] > key;
-    }
-    for (; f < nc; ++f) rank += mk[f] > key;
+    const int rank = count_greater(mk, nc, key);
     if (rank < k && key != 0ull) sel[rank] = key;
   }
-  __syncthreads();
+  lds_barrier();
   if (w == 0) {  // softmax over the k candidates at T = 1, summed in rank order
     const size_t o = row * k;
     const float v = lane < k ? best_value(sel[lane]) : 0.f;

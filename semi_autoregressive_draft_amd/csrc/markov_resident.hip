@@ -82,17 +82,7 @@ struct ResidentArgs {
   unsigned long long wait_ticks;   // bound of one grid-wide wait, wall-clock ticks
 };
 
-// Wait-tree layout in the sync block (32-bit words; counters and flags each on
-// their own 256-byte line): time-out flag, group counters, top counter, group
-// release flags, then the group keys [position][group][request] (64-bit).
-constexpr int kFanIn = 16;
-constexpr int kSyncTimeout = 0;
-constexpr int kSyncGroupCnt = 64;                       // + 64 * group
-constexpr int kSyncTopCnt = kSyncGroupCnt + 64 * kFanIn;
-constexpr int kSyncRelease = kSyncTopCnt + 64;          // + 64 * group
-constexpr int kSyncKeys = 4096;                         // word offset of the group keys
-static_assert(kSyncRelease + 64 * kFanIn <= kSyncKeys, "wait-tree layout");
-static_assert(kSyncKeys + 2 * kMaxGamma * kFanIn * kResMaxB <= kSyncWords, "wait-tree size");
+// Wait-tree layout: internal.h (kSync*), shared with the finish kernels that clear it.
 
 __device__ __forceinline__ unsigned atomic_add_dev(unsigned* p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
