@@ -53,7 +53,23 @@ constexpr int kSeg = 8;            // vocabulary columns per top-k segment
 constexpr int kMergeThreads = 256;
 constexpr int kFoldBatch = 4;
 
-__device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
+// The fold's results for (request, position): written by thread 0 at the
+// fold's end, or, when the caller passes `out`, handed back to thread 0 for a
+// later store (a store left outstanding here would hold up the caller's
+// next waits on older loads).
+struct FoldOut {
+  int token;
+  float tok_logit, lse;
+};
+
+__device__ __forceinline__ void store_fold(const StepArgs& a, int row, bool from_key, const FoldOut& f) {
+  a.tokens[row] = f.token;
+  if (from_key) a.best[row] = 0ull;
+  if (a.tok_logit) a.tok_logit[row] = f.tok_logit;
+  if (a.lse) a.lse[row] = f.lse;
+}
+
+__device__ void fold_request(const StepArgs& a, int b, int j, bool from_key, FoldOut* out = nullptr) {
   __shared__ LseState red_l[kMergeThreads / kWave];
   __shared__ ArgState red_a[kMergeThreads / kWave];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -64,10 +80,14 @@ __device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
   // the chain's final key and the time-out word, loaded beside the partials
   // (vector loads: a scalar load here would be waited for before the
   // partials' loads are issued)
-  unsigned long long key = 0ull;
+  // (only the key's low word, the index part, is loaded: a 64-bit load whose
+  // high register the compiler reuses would be waited for before the
+  // partials' loads go out)
+  unsigned key_lo = 0u;
   unsigned mark = 0u;
   if (from_key) {
-    key = __hip_atomic_load(a.best + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    key_lo = __hip_atomic_load(reinterpret_cast<const unsigned*>(a.best + row), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     mark = __hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   for (int p0 = 0; p0 < a.Pn; p0 += kFoldBatch * kMergeThreads) {
@@ -98,14 +118,13 @@ __device__ void fold_request(const StepArgs& a, int b, int j, bool from_key) {
     LseState l = red_l[0];
     ArgState s = red_a[0];
     for (int i = 1; i < kMergeThreads / kWave; ++i) { l = lse_merge(l, red_l[i]); s = arg_merge(s, red_a[i]); }
-    if (from_key) {
-      a.tokens[row] = mark == a.epoch ? -1 : best_index(key);
-      a.best[row] = 0ull;
-    } else {
-      a.tokens[row] = (s.idx >= 0 && s.idx < a.V) ? s.idx : -1;   // -1: no orderable value (NaN row)
-    }
-    if (a.tok_logit) a.tok_logit[row] = s.x;
-    if (a.lse) a.lse[row] = l.m + logf(l.s);
+    FoldOut f;
+    if (from_key) f.token = mark == a.epoch ? -1 : best_index(key_lo);
+    else f.token = (s.idx >= 0 && s.idx < a.V) ? s.idx : -1;   // -1: no orderable value (NaN row)
+    f.tok_logit = s.x;
+    f.lse = l.m + logf(l.s);
+    if (out) *out = f;
+    else store_fold(a, row, from_key, f);
   }
 }
 
@@ -999,20 +1018,46 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
   __shared__ int nlive;
   __shared__ __align__(16) unsigned long long mk[kMaxMergeCand];
   __shared__ unsigned long long sel[kMaxTopk];
+  __shared__ unsigned long long thr_s[kTopkThreads / kWave];
+  __shared__ int nsurv;
 
   const unsigned long long* ck = a.cand_key + row * L * k;
   // the head's load lands with the fold's (stored after it, so that the fold's
   // loads are not held back by a wait for it)
   const unsigned long long head = tid < L ? ck[static_cast<size_t>(tid) * k] : 0ull;
-  if (tid == 0) nlive = 0;
-  fold_request(a, b, j, true);
-  clear_wait_tree(a);
-  // from here on only LDS is shared between threads: the barriers leave the
-  // global stores (outputs, wait-tree clearing) in flight
+  if (tid == 0) {
+    nlive = 0;
+    nsurv = 0;
+  }
+  FoldOut fo{};
+  fold_request(a, b, j, true, &fo);                   // thread 0 stores fo at the end
+  // from here on only LDS is shared between threads
   hk[tid] = head;
   lds_barrier();
-  if (head != 0ull) {
-    const int rank = count_greater(hk, L, head);
+  // The heads of rank < k, exactly, without counting 256 x 256: the k-th
+  // largest head of each wave's 64 is at most the k-th largest of all, so
+  // their maximum t bounds every head of rank < k from below.  Heads >= t
+  // survive (into mk, free until the gather), and a survivor's rank among
+  // the survivors is its rank among all heads, since every larger head is
+  // a survivor too.  (A wave with fewer than k live heads gives t_w = 0.)
+  {
+    const int rw = count_greater(hk + w * kWave, kWave, head);
+    unsigned long long tw = rw == k - 1 ? head : 0ull;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const unsigned long long ot = __shfl_xor(tw, o);
+      tw = ot > tw ? ot : tw;
+    }
+    if (lane == 0) thr_s[w] = tw;
+  }
+  lds_barrier();
+  unsigned long long t = thr_s[0];
+#pragma unroll
+  for (int i = 1; i < kTopkThreads / kWave; ++i) t = thr_s[i] > t ? thr_s[i] : t;
+  if (head != 0ull && head >= t) mk[atomicAdd(&nsurv, 1)] = head;
+  lds_barrier();
+  if (head != 0ull && head >= t) {
+    const int rank = count_greater(mk, nsurv, head);
     if (rank < k) {
       act[rank] = tid;
       atomicAdd(&nlive, 1);
@@ -1047,6 +1092,11 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk_lists(StepArgs a) {
       a.topk_prob[o + lane] = e / ssum;
     }
   }
+  if (tid == 0) store_fold(a, static_cast<int>(row), true, fo);
+  // last: the compiler puts a wait for every outstanding store ahead of a
+  // loop that stores and does not load; here it waits for nothing that the
+  // kernel's end would not wait for anyway
+  clear_wait_tree(a);
 }
 
 // ---------------------------------------------------------------------------
