@@ -84,6 +84,23 @@ dspark_status_t dspark_lm_head(const void* h, const void* w_lm, dspark_dtype_t d
                                hipStream_t stream);
 
 /*
+ * S1 and S5 in one call: dspark_lm_head over M = B*gamma rows, and the
+ * hidden-only confidence head with prefix survival of
+ * dspark_confidence_survival (w_m == NULL), which depends on h alone.  [P4]
+ * §2.2 and §3.1; [P1] Confidence head.  For bf16 with M <= 16 both run in
+ * one launch (the LM head's first workgroup also computes the confidence
+ * from the rows of h it already holds); otherwise each step has its own
+ * launch.  Same arguments, layouts, requirements and errors as the two calls:
+ *   h [B, gamma, H], w_lm [V, H], U [B, gamma, V] as for dspark_lm_head;
+ *   w_c [H] dtype dt, b_c, conf and survival [B, gamma] float32 as for
+ *   dspark_confidence_survival; gamma <= 16.
+ */
+dspark_status_t dspark_lm_head_confidence(const void* h, const void* w_lm, dspark_dtype_t dt,
+                                          int64_t B, int64_t gamma, int64_t H, int64_t V,
+                                          float* U, const void* w_c, float b_c, float* conf,
+                                          float* survival, hipStream_t stream);
+
+/*
  * Workspace size (bytes) needed by dspark_markov_propose for these sizes.
  * The workspace must be zero-filled before its first use (e.g. one
  * hipMemsetAsync at allocation); every call leaves the part that must start

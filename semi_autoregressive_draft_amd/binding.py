@@ -25,6 +25,8 @@ _SIGNATURES = {
     "dspark_last_error": (C.c_char_p, []),
     "dspark_version": (C.c_char_p, []),
     "dspark_lm_head": (C.c_int, [_vp, _vp, C.c_int, _i64, _i64, _i64, _vp, _vp]),
+    "dspark_lm_head_confidence": (C.c_int, [_vp, _vp, C.c_int, _i64, _i64, _i64, _i64, _vp, _vp, C.c_float,
+                                            _vp, _vp, _vp]),
     "dspark_markov_propose_workspace": (C.c_int, [_i64, _i64, _i64, _i32, C.POINTER(_sz)]),
     "dspark_markov_propose_plan": (C.c_int, [_i64, _i64, _i64, C.c_int, C.POINTER(_i32)]),
     "dspark_markov_propose": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64,
@@ -127,6 +129,16 @@ def dspark_lm_head(h, w_lm, U, stream=None) -> None:
     M, H = h.shape
     V = w_lm.shape[0]
     _check(lib().dspark_lm_head(_ptr(h), _ptr(w_lm), _dtype(h), M, H, V, _ptr(U), _stream(stream)))
+
+
+def dspark_lm_head_confidence(h, w_lm, U, w_c, b_c: float, conf, survival, stream=None) -> None:
+    """U [B, gamma, V] and the hidden-only confidence conf/survival [B, gamma]
+    from h [B, gamma, H] in one call."""
+    B, gamma, H = h.shape
+    V = w_lm.shape[0]
+    _check(lib().dspark_lm_head_confidence(_ptr(h), _ptr(w_lm), _dtype(h), B, gamma, H, V, _ptr(U),
+                                           _ptr(w_c), float(b_c), _ptr(conf), _ptr(survival),
+                                           _stream(stream)))
 
 
 def dspark_markov_propose_workspace(B: int, gamma: int, V: int, topk: int = 0) -> int:

@@ -119,25 +119,61 @@ extern "C" const char* dspark_last_error(void) { return g_err; }
 extern "C" const char* dspark_version(void) { return "dspark-mi355x 0.1.0 gfx950"; }
 
 // ---------------------------------------------------------------------------
+namespace {
+// the arguments of the LM head (dspark_lm_head and the fused call)
+dspark_status_t check_lm_head(const char* fn, const void* h, const void* w_lm, dspark_dtype_t dt, int64_t M,
+                              int64_t H, int64_t V, const float* U) {
+  if (!h || !w_lm || !U) return fail(DSPARK_EINVAL, "%s: h, w_lm and U must be non-NULL", fn);
+  if (M <= 0 || H <= 0 || V <= 0) return fail(DSPARK_EINVAL, "%s: M, H, V must be positive", fn);
+  if (V > kI32Max || H > kI32Max || M > kI32Max || M * V > (int64_t(1) << 40))
+    return fail(DSPARK_EINVAL, "%s: sizes too large (M=%lld H=%lld V=%lld)", fn, (long long)M, (long long)H,
+                (long long)V);
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)dt);
+  if (dt == DSPARK_BF16) {
+    if (H % 8 || V % 8) return fail(DSPARK_EUNSUPPORTED, "%s: bf16 needs H %% 8 == 0 and V %% 8 == 0", fn);
+    if (!aligned16(h) || !aligned16(w_lm) || !aligned16(U))
+      return fail(DSPARK_EUNSUPPORTED, "%s: bf16 operands must be 16-byte aligned", fn);
+    if ((M + 127) / 128 > 65535) return fail(DSPARK_EINVAL, "%s: M too large", fn);
+  } else if ((M + 63) / 64 > 65535) {
+    return fail(DSPARK_EINVAL, "%s: M too large", fn);
+  }
+  return DSPARK_OK;
+}
+}  // namespace
+
 extern "C" dspark_status_t dspark_lm_head(const void* h, const void* w_lm, dspark_dtype_t dt,
                                           int64_t M, int64_t H, int64_t V, float* U,
                                           hipStream_t stream) {
-  if (!h || !w_lm || !U) return fail(DSPARK_EINVAL, "dspark_lm_head: h, w_lm and U must be non-NULL");
-  if (M <= 0 || H <= 0 || V <= 0) return fail(DSPARK_EINVAL, "dspark_lm_head: M, H, V must be positive");
-  if (V > kI32Max || H > kI32Max || M > kI32Max || M * V > (int64_t(1) << 40))
-    return fail(DSPARK_EINVAL, "dspark_lm_head: sizes too large (M=%lld H=%lld V=%lld)",
-                (long long)M, (long long)H, (long long)V);
-  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "dspark_lm_head: unknown dtype %d", (int)dt);
+  const dspark_status_t st = check_lm_head("dspark_lm_head", h, w_lm, dt, M, H, V, U);
+  if (st != DSPARK_OK) return st;
+  return hip_status(launch_lm_head(h, w_lm, dt == DSPARK_BF16, M, H, V, U, stream), "dspark_lm_head");
+}
+
+extern "C" dspark_status_t dspark_lm_head_confidence(const void* h, const void* w_lm, dspark_dtype_t dt,
+                                                     int64_t B, int64_t gamma, int64_t H, int64_t V, float* U,
+                                                     const void* w_c, float b_c, float* conf, float* survival,
+                                                     hipStream_t stream) {
+  const char* fn = "dspark_lm_head_confidence";
+  if (!w_c || !conf || !survival) return fail(DSPARK_EINVAL, "%s: w_c, conf and survival must be non-NULL", fn);
+  if (B <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "%s: B and gamma must be positive", fn);
+  if (B > kI32Max || B * gamma > kI32Max) return fail(DSPARK_EINVAL, "%s: sizes too large", fn);
+  if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
+  const int64_t M = B * gamma;
+  const dspark_status_t st = check_lm_head(fn, h, w_lm, dt, M, H, V, U);
+  if (st != DSPARK_OK) return st;
   const bool bf16 = dt == DSPARK_BF16;
-  if (bf16) {
-    if (H % 8 || V % 8) return fail(DSPARK_EUNSUPPORTED, "dspark_lm_head: bf16 needs H %% 8 == 0 and V %% 8 == 0");
-    if (!aligned16(h) || !aligned16(w_lm) || !aligned16(U))
-      return fail(DSPARK_EUNSUPPORTED, "dspark_lm_head: bf16 operands must be 16-byte aligned");
-    if ((M + 127) / 128 > 65535) return fail(DSPARK_EINVAL, "dspark_lm_head: M too large");
-  } else if ((M + 63) / 64 > 65535) {
-    return fail(DSPARK_EINVAL, "dspark_lm_head: M too large");
+  hipError_t e;
+  if (bf16 && lm_head_skinny_fits(M, H) && aligned16(w_c)) {   // one launch
+    e = launch_lm_head_skinny(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_lm), M, H, V, U,
+                              stream, static_cast<const uint16_t*>(w_c), b_c, static_cast<int>(gamma), conf,
+                              survival);
+  } else {                                                     // the two steps' own launches
+    e = launch_lm_head(h, w_lm, bf16, M, H, V, U, stream);
+    if (e == hipSuccess)
+      e = launch_confidence(h, bf16, static_cast<int>(B), static_cast<int>(gamma), static_cast<int>(H), w_c, b_c,
+                            nullptr, nullptr, 0, nullptr, nullptr, conf, survival, stream);
   }
-  return hip_status(launch_lm_head(h, w_lm, bf16, M, H, V, U, stream), "dspark_lm_head");
+  return hip_status(e, fn);
 }
 
 // ---------------------------------------------------------------------------

@@ -94,8 +94,11 @@ bool markov_bmt_pays(int64_t B, int64_t gamma, int64_t V, int64_t r, int32_t top
 hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
                           int64_t V, float* U, hipStream_t s);
 bool lm_head_skinny_fits(int64_t M, int64_t H);
+// with conf != NULL (bf16, M = B gamma <= 16) also the hidden-only confidence
+// head and prefix survival of dspark_confidence_survival, in the same launch
 hipError_t launch_lm_head_skinny(const uint16_t* h, const uint16_t* w, int64_t M, int64_t H, int64_t V,
-                                 float* U, hipStream_t s);
+                                 float* U, hipStream_t s, const uint16_t* w_c = nullptr, float b_c = 0.f,
+                                 int gamma = 1, float* conf = nullptr, float* surv = nullptr);
 
 constexpr int kSchedMaxCand = 16384;   // R * gamma of the prefix scheduler (keys in LDS)
 hipError_t launch_prefix_schedule(const float* survival, int R, int gamma, const double* sps, int kmax,

@@ -31,6 +31,13 @@
 // h reaches LDS by DMA (global_load_lds) issued before the first W loads, and
 // each wave waits only for those older operations (an explicit vmcnt and a
 // bare s_barrier), so the W stream starts without waiting for h.
+//
+// With a confidence head (conf != NULL, the hidden-only head of
+// "Qwen3.8-Flash-Next DSpark 训练实验", Confidence head, and "DSpark 论文精读",
+// §3.1 prefix survival), workgroup 0 also computes c = sigmoid(w_c . h_m + b_c)
+// for its M = B gamma rows of h, already in its LDS, and the running product
+// per request, while its first W_lm batches are in flight: the whole S5 step
+// costs no launch of its own.
 #include "common.h"
 #include "internal.h"
 
@@ -48,12 +55,56 @@ __device__ __forceinline__ void wait_vmcnt_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The confidence head of the M rows in LDS (row m = b gamma + j), by the
+// kSkinnyWaves waves of one workgroup: wave w reduces rows w, w + kSkinnyWaves,
+// ... over 16-byte pieces of h (LDS) and w_c, then thread 0 runs the sigmoid
+// and the running product in position order.
+struct SkinnyConf {
+  const uint16_t* w_c;
+  float b_c;
+  int gamma;
+  float* conf;
+  float* surv;
+};
+
+__device__ void skinny_confidence(const uint16_t* hs, int ld, int M, int H, const SkinnyConf& c, int w, int lane,
+                                  float* part) {
+  for (int m = w; m < M; m += kSkinnyWaves) {
+    float acc = 0.f;
+    for (int i = lane; i < H / 8; i += kWave) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(hs + m * ld + 8 * i);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(c.w_c + 8 * i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(__uint_as_float(x[q] << 16), __uint_as_float(y[q] << 16), acc);
+        acc = fmaf(__uint_as_float(x[q] & 0xFFFF0000u), __uint_as_float(y[q] & 0xFFFF0000u), acc);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) part[m] = acc;
+  }
+  __syncthreads();
+  if (w == 0 && lane == 0) {
+    for (int b = 0; b * c.gamma < M; ++b) {
+      float run = 1.f;
+      for (int j = 0; j < c.gamma; ++j) {
+        const int m = b * c.gamma + j;
+        const float cj = 1.0f / (1.0f + __expf(-(part[m] + c.b_c)));
+        run *= cj;
+        c.conf[m] = cj;
+        c.surv[m] = run;
+      }
+    }
+  }
+}
+
 // PIPE (H >= 512, at least one pair of batches): the pipelined form below;
 // otherwise one chunk of 64 k at a time.
 template <bool PIPE>
 __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, float* __restrict__ U,
-    int M, int H, int V) {
+    int M, int H, int V, SkinnyConf cf) {
+  __shared__ float cpart[16];
   extern __shared__ uint16_t hs[];  // [M][H + 8]
   const int ld = H + 8;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -128,6 +179,7 @@ __global__ __launch_bounds__(kWave* kSkinnyWaves) void lm_head_skinny_bf16(
     wait_vmcnt_le<0>();
   }
   asm volatile("s_barrier" ::: "memory");          // every wave's h DMA has landed
+  if (cf.conf && blockIdx.x == 0) skinny_confidence(hs, ld, M, H, cf, w, lane, cpart);   // uniform per workgroup
   // (waves past V run to the end on row 0 and store nothing: an early exit
   // would let the compiler sink the first batches below it)
   if constexpr (PIPE) {                            // npairs >= 1: the batches above are used
@@ -176,15 +228,17 @@ size_t lm_head_skinny_lds(int64_t M, int64_t H) { return static_cast<size_t>(M) 
 bool lm_head_skinny_fits(int64_t M, int64_t H) { return M <= 16 && lm_head_skinny_lds(M, H) <= kSkinnyMaxLds; }
 
 hipError_t launch_lm_head_skinny(const uint16_t* h, const uint16_t* w, int64_t M, int64_t H, int64_t V,
-                                 float* U, hipStream_t s) {
+                                 float* U, hipStream_t s, const uint16_t* w_c, float b_c, int gamma, float* conf,
+                                 float* surv) {
+  const SkinnyConf cf{w_c, b_c, gamma, conf, surv};
   const int64_t tiles = (V + 15) / 16;
   const dim3 grid(static_cast<unsigned>((tiles + kSkinnyWaves - 1) / kSkinnyWaves));
   if (H >= 128 * kSkinnyUnroll)
     hipLaunchKernelGGL(lm_head_skinny_bf16<true>, grid, dim3(kWave * kSkinnyWaves), lm_head_skinny_lds(M, H), s, h,
-                       w, U, static_cast<int>(M), static_cast<int>(H), static_cast<int>(V));
+                       w, U, static_cast<int>(M), static_cast<int>(H), static_cast<int>(V), cf);
   else
     hipLaunchKernelGGL(lm_head_skinny_bf16<false>, grid, dim3(kWave * kSkinnyWaves), lm_head_skinny_lds(M, H), s,
-                       h, w, U, static_cast<int>(M), static_cast<int>(H), static_cast<int>(V));
+                       h, w, U, static_cast<int>(M), static_cast<int>(H), static_cast<int>(V), cf);
   return hipGetLastError();
 }
 

@@ -1,10 +1,12 @@
 """One pass of the draft-proposal hot path over a batch of blocks.
 
-Sequences the four C-ABI calls on one stream with every output and workspace
+Sequences the C-ABI calls on one stream with every output and workspace
 allocated once up front:
   dspark_lm_head -> dspark_markov_propose -> dspark_confidence_survival
   -> dspark_overlap_tau (against a teacher; dense over U~, or over the top-k
   candidate distribution when topk > 0)
+With the hidden-only confidence head (no w_m) the first and third are one
+call, dspark_lm_head_confidence, which at small batch is one launch.
 (Issuing the hidden-only confidence head on a second stream, beside the LM
 head, measured slower: the cross-stream events cost more than the kernel.)
 """
@@ -60,7 +62,13 @@ class DraftPath:
                                           dtype=torch.uint8, device=dev)
 
     def lm_head(self, stream=None):
-        bd.dspark_lm_head(self.h, self.w_lm, self.U.view(-1, self.V), stream=stream)
+        """S1; with the hidden-only confidence head (no w_m) also S5, in the
+        same call."""
+        if self.w_m is None:
+            bd.dspark_lm_head_confidence(self.h.view(self.B, self.gamma, self.H), self.w_lm, self.U,
+                                         self.w_c, self.b_c, self.conf, self.survival, stream=stream)
+        else:
+            bd.dspark_lm_head(self.h, self.w_lm, self.U.view(-1, self.V), stream=stream)
 
     def propose(self, stream=None):
         bd.dspark_markov_propose(self.U, self.anchor, self.A, self.Bm, self.tokens,
@@ -92,6 +100,7 @@ class DraftPath:
         if lm_done is not None:
             lm_done.record(main)
         self.propose(main)
-        self.confidence(main)
+        if self.w_m is not None:             # else computed with the LM head
+            self.confidence(main)
         if self.overlap:
             self.overlap_tau(main)

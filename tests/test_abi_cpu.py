@@ -85,6 +85,23 @@ def test_lm_head_validation(L):
     assert f(FAKE, FAKE, 7, 7, 2560, 151936, FAKE, None) == bd.EUNSUPPORTED
 
 
+def test_lm_head_confidence_validation(L):
+    f = L.dspark_lm_head_confidence
+    ok = (FAKE, FAKE, bd.BF16, 1, 7, 2560, 151936, FAKE, FAKE, 0.5, FAKE, FAKE, None)
+    def call(**kw):
+        names = ["h", "w", "dt", "B", "gamma", "H", "V", "U", "w_c", "b_c", "conf", "surv", "s"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+    assert call(w_c=None) == bd.EINVAL and "non-NULL" in bd.last_error()
+    assert call(conf=None) == bd.EINVAL
+    assert call(B=0) == bd.EINVAL
+    assert call(gamma=17) == bd.EUNSUPPORTED
+    assert call(h=None) == bd.EINVAL                  # the LM head's own checks
+    assert call(H=2564) == bd.EUNSUPPORTED
+    assert call(dt=7) == bd.EUNSUPPORTED
+
+
 def _propose(L, **kw):
     a = dict(U=FAKE, B=1, gamma=7, V=151936, anchor=FAKE, A=FAKE, Bm=FAKE, wdt=bd.BF16, r=256,
              T=0.0, seeds=None, offset=0, topk=0, tokens=FAKE, tok_logit=None, lse=None,

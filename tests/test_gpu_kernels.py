@@ -261,6 +261,31 @@ def test_markov_is_deterministic(B):
         assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
 
 
+# ----------------------------------------------------------------------------- S1 + S5
+@pytest.mark.parametrize("B,gamma,H,V,wdtype", [
+    (1, 7, 2560, 3000, "bf16"),     # one launch (skinny LM head, workgroup 0 adds S5)
+    (2, 8, 512, 1032, "bf16"),      # one launch, M = 16
+    (3, 7, 264, 520, "bf16"),       # M = 21: the GEMM and the S5 kernel
+    (1, 5, 96, 300, "f32"),         # fp32: two launches
+])
+def test_lm_head_confidence_parity(B, gamma, H, V, wdtype):
+    dev = require_gpu()
+    h = synth.normal((B, gamma, H), 1.0, 5, synth.TID_H, wdtype)
+    w = synth.normal((V, H), 0.05, 5, synth.TID_WLM, wdtype)
+    w_c = synth.normal((H,), 0.05, 5, synth.TID_WC, wdtype)
+    U = torch.empty((B, gamma, V), dtype=torch.float32, device=dev)
+    conf = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    surv = torch.empty_like(conf)
+    bd.dspark_lm_head_confidence(to_dev(h, wdtype), to_dev(w, wdtype), U, to_dev(w_c, wdtype), -0.2, conf, surv)
+    torch.cuda.synchronize()
+    h64 = o.to_f64(h, wdtype)
+    u_ref = o.lm_head(h64.reshape(B * gamma, H), o.to_f64(w, wdtype)).reshape(B, gamma, V)
+    rel_check(U.cpu().numpy(), u_ref, float(np.sqrt(np.mean(u_ref ** 2))), what="U")
+    c_ref, s_ref = o.confidence_survival(h64, o.to_f64(w_c, wdtype), -0.2)
+    assert np.abs(conf.cpu().numpy() - c_ref).max() < 1e-5
+    assert np.abs(surv.cpu().numpy() - s_ref).max() < 1e-5
+
+
 # ----------------------------------------------------------------------------- S5
 @pytest.mark.parametrize("B,H,r,wdtype,with_wm", [
     (5, 2560, 256, "bf16", True),
