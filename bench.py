@@ -347,8 +347,11 @@ def main():
                      seeds=to_dev(inp.seeds) if inp.temperature > 0 else None, offset=inp.offset,
                      topk=inp.topk, teacher=to_dev(inp.teacher), overlap=overlap)
     stream = torch.cuda.current_stream()
-    stages = [("lm_head", path.lm_head), ("markov", path.propose), ("confidence", path.confidence),
-              ("overlap", path.overlap_tau)]
+    # the hidden-only confidence head runs inside the LM-head call (path.lm_head)
+    stages = [("lm_head", path.lm_head), ("markov", path.propose)]
+    if path.w_m is not None:
+        stages.append(("confidence", path.confidence))
+    stages.append(("overlap", path.overlap_tau))
 
     for _ in range(args.warmup):
         path.run()
