@@ -169,6 +169,34 @@ def head_vector(head: str, a_row: np.ndarray, *, h_row: Optional[np.ndarray] = N
     return round_to_dtype(v, wdtype)
 
 
+# RNN head ("DSpark 论文精读", §2.3 heads table row RNNHead, and the RNN head
+# passage of "Baseline 架构"): the head keeps a state s_j of rank r, zero
+# before the block's first position, and at each position reads the input
+# z_j = [s_{j-1}; W_down[x_{j-1}]; h_j] (width 2r + H, in that order).  A
+# sigmoid gate g_j = sigma(W_gate z_j) mixes the old state with the tanh
+# candidate c_j = tanh(W_cand z_j): gate 1 writes the candidate, gate 0 keeps
+# the old state.  The output re-reads the input with the updated state,
+# z'_j = [s_j; W_down[x_{j-1}]; h_j], projects it to rank r and applies the
+# activation; W_up maps the result to the vocabulary.  Readings where the
+# pages' formulas did not survive extraction: the state update is the convex
+# mix (1 - g) * s_{j-1} + g * c_j that the passage's two limiting cases
+# describe; the unnamed output activation is SiLU, the activation of the
+# pages' SiLU-Vanilla head; the state, like m_j, is handed on in the tables'
+# dtype.  W_rnn stacks [W_gate; W_cand; W_out] as [3r, 2r + H].
+
+
+def rnn_head_step(s_prev: np.ndarray, a_row: np.ndarray, h_row: np.ndarray, W_rnn: np.ndarray,
+                  wdtype: str = "bf16"):
+    """(s_j, m_j) from s_{j-1}, A[x_{j-1}] = a_row, h_j and W_rnn [3r, 2r + H]."""
+    r = a_row.shape[0]
+    z = np.concatenate([s_prev, a_row, h_row])
+    gate = 1.0 / (1.0 + np.exp(-(W_rnn[:r] @ z)))
+    cand = np.tanh(W_rnn[r:2 * r] @ z)
+    s_new = round_to_dtype((1.0 - gate) * s_prev + gate * cand, wdtype)
+    o = W_rnn[2 * r:] @ np.concatenate([s_new, a_row, h_row])
+    return s_new, round_to_dtype(o / (1.0 + np.exp(-o)), wdtype)
+
+
 # --------------------------------------------------------------------------
 # S2-S4: the sequential Vanilla-Markov stage.
 # [P1] Markov 顺序修正: m_i = W_1[t_{i-1}] (t_0 = anchor), b_i = W_2 m_i,
@@ -187,8 +215,9 @@ def markov_chain(U: np.ndarray, anchor: np.ndarray, A: np.ndarray, Bm: np.ndarra
     temperature 0 selects greedily; otherwise token = argmax(U~/T + G).
     ``forced`` [B, gamma] (int, -1 = free) overrides the selected token at a
     position (used to continue a chain along another valid choice).
-    ``head`` selects the sequential head (see ``head_vector``; h [B, gamma, H]
-    and W_g for 'gated'; wdtype the tables' dtype for the rounding of m_j).
+    ``head`` selects the sequential head (see ``head_vector`` and
+    ``rnn_head_step``; h [B, gamma, H] and W_g for 'gated', or W_g = W_rnn
+    [3r, 2r + H] for 'rnn'; wdtype the tables' dtype for the rounding of m_j).
 
     Returns tokens [B,gamma], tok_logit (U~ at the token), lse (log-sum-exp of
     U~), gap (best minus second-best of the selection score), score_max and
@@ -208,8 +237,12 @@ def markov_chain(U: np.ndarray, anchor: np.ndarray, A: np.ndarray, Bm: np.ndarra
         out["logits"] = np.zeros((B, gamma, V), dtype=np.float64)
     for b in range(B):
         prev = int(anchor[b])
+        s = np.zeros(A.shape[1])                            # RNN state before the block
         for j in range(gamma):
-            m = head_vector(head, A[prev], h_row=None if h is None else h[b, j], W_g=W_g, wdtype=wdtype)
+            if head == "rnn":
+                s, m = rnn_head_step(s, A[prev], h[b, j], W_g, wdtype)
+            else:
+                m = head_vector(head, A[prev], h_row=None if h is None else h[b, j], W_g=W_g, wdtype=wdtype)
             ut = U[b, j] + m @ Bm                           # U~_j = U_j + W_2 m_j
             mx = ut.max()
             out["lse"][b, j] = mx + math.log(np.exp(ut - mx).sum())
@@ -256,6 +289,13 @@ def teacher_forced_logits(U: np.ndarray, prev_tokens: np.ndarray, A: np.ndarray,
     if head == "linear":
         return U + np.einsum("bjr,rv->bjv", A[prev_tokens], Bm)
     B, gamma = prev_tokens.shape
+    if head == "rnn":                                       # the state runs along the known tokens
+        M = np.zeros((B, gamma, A.shape[1]))
+        for b in range(B):
+            s = np.zeros(A.shape[1])
+            for j in range(gamma):
+                s, M[b, j] = rnn_head_step(s, A[prev_tokens[b, j]], h[b, j], W_g, wdtype)
+        return U + np.einsum("bjr,rv->bjv", M, Bm)
     M = np.stack([np.stack([head_vector(head, A[prev_tokens[b, j]], h_row=None if h is None else h[b, j],
                                         W_g=W_g, wdtype=wdtype) for j in range(gamma)]) for b in range(B)])
     return U + np.einsum("bjr,rv->bjv", M, Bm)

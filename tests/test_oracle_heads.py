@@ -76,3 +76,80 @@ def test_gated_vector_against_a_loop():
         want.append(a[k] / (1.0 + math.exp(-z)))
     got = o.head_vector("gated", a, h_row=hr, W_g=W_g)
     assert np.array_equal(got, o.round_to_dtype(np.array(want), "bf16"))
+
+
+# ----------------------------------------------------------------------------- RNN head
+# Pins from the RNN head passage's own statements: a gate of 1 writes the
+# candidate, a gate of 0 keeps the old state, the state starts at zero, and
+# the input concatenates [state; W_down[x_{j-1}]; h_j].
+
+def _rnn_blocks(r, H, gate=None, cand=None, out=None):
+    W = np.zeros((3 * r, 2 * r + H))
+    for i, blk in enumerate((gate, cand, out)):
+        if blk is not None:
+            W[i * r:(i + 1) * r] = blk
+    return W
+
+
+def test_rnn_with_identity_output_and_no_state_is_the_silu_head():
+    U, A, Bm, h, _, anchor = _case(seed=11)
+    r, H = A.shape[1], h.shape[-1]
+    out = np.zeros((r, 2 * r + H))
+    out[:, r:2 * r] = np.eye(r)                             # W_out picks W_down[x_{j-1}]
+    W = _rnn_blocks(r, H, out=out)                          # candidate 0: the state stays 0
+    rnn = o.markov_chain(U, anchor, A, Bm, head="rnn", h=h, W_g=W, keep_logits=True)
+    silu = o.markov_chain(U, anchor, A, Bm, head="silu", keep_logits=True)
+    assert np.array_equal(rnn["tokens"], silu["tokens"])
+    assert np.allclose(rnn["logits"], silu["logits"], rtol=0, atol=1e-12)
+
+
+def test_rnn_open_gate_writes_the_candidate_and_closed_gate_keeps_zero_state():
+    U, A, Bm, h, _, anchor = _case(seed=12)
+    r, H = A.shape[1], h.shape[-1]
+    ones = np.ones_like(h)
+    gate = np.zeros((r, 2 * r + H))
+    cand = np.zeros((r, 2 * r + H))
+    cand[:, 2 * r:] = 0.5 / H                               # with h = 1: candidate tanh(0.5) everywhere
+    out = np.zeros((r, 2 * r + H))
+    out[:, :r] = 3.0 * np.eye(r)                            # m_j = SiLU(3 s_j)
+    want_open = o.round_to_dtype(math.tanh(0.5), "f32")
+    for sign, s_want in ((1.0, want_open), (-1.0, 0.0)):
+        gate[:, 2 * r:] = sign * 40.0 / H                   # gate pre-activation +-40: sigma = 1 or 0 in fp64
+        W = _rnn_blocks(r, H, gate, cand, out)
+        s = np.zeros(r)
+        for j in range(3):
+            s, m = o.rnn_head_step(s, A[5], ones[0, j], W, "f32")
+            assert np.allclose(s, s_want, rtol=0, atol=1e-7)
+            x = 3.0 * s_want
+            assert np.allclose(m, x / (1.0 + math.exp(-x)), rtol=1e-6, atol=1e-7)
+
+
+def test_rnn_state_starts_at_zero_and_carries_the_previous_position():
+    r, H = 4, 6
+    g = np.random.default_rng(13)
+    A = g.standard_normal((10, r))
+    h = g.standard_normal((1, 3, H))
+    cand = np.zeros((r, 2 * r + H))
+    cand[:, :r] = 2.0 * np.eye(r)                           # candidate tanh(2 s_{j-1}) + tanh of the h block
+    cand[:, 2 * r:2 * r + r] = np.eye(r)
+    W = _rnn_blocks(r, H, None, cand, np.hstack([np.eye(r), np.zeros((r, r + H))]))
+    # gate weights 0: sigma(0) = 1/2, so s_j = (s_{j-1} + tanh(2 s_{j-1} + h_j[:r])) / 2 with s_{-1} = 0
+    s_ref = np.zeros(r)
+    s = np.zeros(r)
+    for j in range(3):
+        s_ref = (s_ref + np.tanh(2.0 * s_ref + h[0, j, :r])) / 2.0
+        s, _ = o.rnn_head_step(s, A[j], h[0, j], W, "f32")
+        assert np.allclose(s, s_ref, rtol=1e-6, atol=1e-7)
+    s0, _ = o.rnn_head_step(np.zeros(r), A[0], h[0, 0], W, "f32")
+    assert np.allclose(s0, np.tanh(h[0, 0, :r]) / 2.0, rtol=1e-6)
+
+
+def test_rnn_teacher_forced_form_reproduces_the_chain():
+    U, A, Bm, h, _, anchor = _case(seed=14)
+    r, H = A.shape[1], h.shape[-1]
+    g = np.random.default_rng(15)
+    W = o.round_to_dtype(g.standard_normal((3 * r, 2 * r + H)) * 0.3, "bf16")
+    ch = o.markov_chain(U, anchor, A, Bm, head="rnn", h=h, W_g=W, keep_logits=True)
+    prev = np.concatenate([anchor[:, None], ch["tokens"][:, :-1]], axis=1)
+    tf = o.teacher_forced_logits(U, prev, A, Bm, head="rnn", h=h, W_g=W)
+    assert np.allclose(tf, ch["logits"], rtol=0, atol=1e-12)
