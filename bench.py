@@ -269,17 +269,20 @@ def bench_heads(dev, stream, B=256, gamma=7, V=151936, r=256, H=2560, reps=5):
     Bm = bf(synth.normal((r, V), 0.02, 0, synth.TID_BM, "bf16"))
     h = bf(synth.normal((B, gamma, H), 1.0, 0, synth.TID_H, "bf16"))
     Wg = bf(synth.normal((r, H + r), 0.02, 0, synth.TID_WG, "bf16"))
+    Wrnn = bf(synth.normal((3 * r, 2 * r + H), 0.02, 1, synth.TID_WG, "bf16"))
     anchor = torch.randint(0, V, (B,), generator=g, device=dev, dtype=torch.int32)
     tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
     out = {"B": B, "gamma": gamma, "V": V, "r": r, "H": H}
     byt = gamma * (2.0 * r * V + 4.0 * B * V)
-    for name, code in (("linear", bd.HEAD_LINEAR), ("silu", bd.HEAD_SILU), ("gated", bd.HEAD_GATED)):
+    weights = {bd.HEAD_GATED: Wg, bd.HEAD_RNN: Wrnn}
+    for name, code in (("linear", bd.HEAD_LINEAR), ("silu", bd.HEAD_SILU), ("gated", bd.HEAD_GATED),
+                       ("rnn", bd.HEAD_RNN)):
         ws = torch.zeros(bd.dspark_markov_propose_head_workspace(code, B, gamma, V, r), dtype=torch.uint8,
                          device=dev)
 
         def call():
-            bd.dspark_markov_propose_head(code, U, anchor, A, Bm, tokens, h=h if code == bd.HEAD_GATED else None,
-                                          W_g=Wg if code == bd.HEAD_GATED else None, ws=ws)
+            bd.dspark_markov_propose_head(code, U, anchor, A, Bm, tokens, h=h if code in weights else None,
+                                          W_g=weights.get(code), ws=ws)
 
         for _ in range(2):
             call()

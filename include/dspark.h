@@ -180,6 +180,13 @@ dspark_status_t dspark_markov_propose(const float* U, int64_t B, int64_t gamma, 
  *   DSPARK_HEAD_SILU  (VanillaMarkov): b_j = W_up SiLU(W_down[x_{j-1}]),
  *   DSPARK_HEAD_GATED (GatedMarkovHead): g_j = sigmoid(W_g [h_j; W_down[x_{j-1}]]),
  *                     b_j = W_up (g_j * W_down[x_{j-1}]),
+ *   DSPARK_HEAD_RNN   (RNNHead; the RNN head passage of "Baseline 架构"): a
+ *                     state s_j of rank r, zero before the block, over the
+ *                     input z_j = [s_{j-1}; W_down[x_{j-1}]; h_j]:
+ *                     s_j = (1 - g_j) s_{j-1} + g_j tanh(W_cand z_j) with
+ *                     g_j = sigmoid(W_gate z_j), and
+ *                     b_j = W_up SiLU(W_out [s_j; W_down[x_{j-1}]; h_j]);
+ *                     s_j is kept in the tables' dtype,
  * with W_down = A [V, r] and W_up = Bm^T; DSPARK_HEAD_LINEAR is
  * dspark_markov_propose itself.  The r-vector the up-projection receives is
  * rounded to the tables' dtype (bf16: to nearest, ties to even), as a module
@@ -187,17 +194,22 @@ dspark_status_t dspark_markov_propose(const float* U, int64_t B, int64_t gamma, 
  * (no resident chain); every other argument, output and rule is that of
  * dspark_markov_propose.
  *
- *   head   DSPARK_HEAD_LINEAR (0), DSPARK_HEAD_SILU (1) or DSPARK_HEAD_GATED (2)
- *   h      [B, gamma, H] dtype wdt   hidden state h_j of each position (gated only)
- *   W_g    [r, H + r] dtype wdt      gate weights over [h_j; A[x_{j-1}]] (gated only)
+ *   head   DSPARK_HEAD_LINEAR (0), DSPARK_HEAD_SILU (1), DSPARK_HEAD_GATED (2)
+ *          or DSPARK_HEAD_RNN (3)
+ *   h      [B, gamma, H] dtype wdt   hidden state h_j of each position (gated, RNN)
+ *   W_g    gated: [r, H + r] dtype wdt, gate weights over [h_j; A[x_{j-1}]];
+ *          RNN: [3r, 2r + H] dtype wdt, the rows of W_gate, W_cand and W_out
+ *          stacked, each over [state; A[x_{j-1}]; h_j]
  *   ws     at least dspark_markov_propose_head_workspace bytes, zero-filled
  *          before its first use
- * Requirements: those of dspark_markov_propose; gated: h, W_g non-NULL,
- * 0 < H <= 16384.
+ * Requirements: those of dspark_markov_propose; gated and RNN: h, W_g
+ * non-NULL, 0 < H <= 16384.  The RNN workspace also holds the state table
+ * [B, gamma, r].
  */
 #define DSPARK_HEAD_LINEAR 0
 #define DSPARK_HEAD_SILU 1
 #define DSPARK_HEAD_GATED 2
+#define DSPARK_HEAD_RNN 3
 
 dspark_status_t dspark_markov_propose_head_workspace(int32_t head, int64_t B, int64_t gamma, int64_t V,
                                                      int64_t r, dspark_dtype_t wdt, int32_t topk,

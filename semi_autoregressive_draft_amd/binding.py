@@ -256,7 +256,7 @@ def dspark_verify(target_logits, draft_logits, draft_tokens, seeds, accepted, ne
         _stream(stream)))
 
 
-HEAD_LINEAR, HEAD_SILU, HEAD_GATED = 0, 1, 2
+HEAD_LINEAR, HEAD_SILU, HEAD_GATED, HEAD_RNN = 0, 1, 2, 3
 
 
 def dspark_markov_propose_head_workspace(head: int, B: int, gamma: int, V: int, r: int, wdtype: int = BF16,
@@ -277,7 +277,8 @@ def dspark_markov_propose_workspace_bmt(head: int, B: int, gamma: int, V: int, r
 def dspark_markov_propose_head(head: int, U, anchor, A, Bm, tokens, *, h=None, W_g=None, temperature: float = 0.0,
                                seeds=None, offset: int = 0, topk: int = 0, tok_logit=None, lse=None,
                                topk_idx=None, topk_prob=None, logits_out=None, ws=None, stream=None) -> None:
-    """dspark_markov_propose with a sequential-head variant (HEAD_SILU, HEAD_GATED)."""
+    """dspark_markov_propose with a sequential-head variant (HEAD_SILU, HEAD_GATED, HEAD_RNN;
+    W_g is the gated head's [r, H + r] or the RNN head's stacked [3r, 2r + H])."""
     import torch
     B, gamma, V = U.shape
     r = A.shape[1]

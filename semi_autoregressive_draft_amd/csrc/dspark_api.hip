@@ -201,8 +201,10 @@ extern "C" dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int6
 }
 
 // head vectors of the sequential-head variants, after the chain's workspace
+// (the RNN head's state table follows its m_j table)
 size_t head_table_bytes(int head, int64_t B, int64_t gamma, int64_t r, bool bf16) {
-  return head == kHeadLinear ? 0 : align_up(static_cast<size_t>(B) * gamma * r * (bf16 ? 2 : 4));
+  const size_t one = static_cast<size_t>(B) * gamma * r * (bf16 ? 2 : 4);
+  return head == kHeadLinear ? 0 : align_up(head == kHeadRnn ? 2 * one : one);
 }
 
 dspark_status_t propose_impl(
@@ -327,7 +329,7 @@ extern "C" dspark_status_t dspark_markov_propose_head_workspace(int32_t head, in
                                                                 size_t* bytes) {
   const char* fn = "dspark_markov_propose_head_workspace";
   if (!bytes) return fail(DSPARK_EINVAL, "%s: bytes is NULL", fn);
-  if (head != kHeadLinear && head != kHeadSilu && head != kHeadGated)
+  if (head != kHeadLinear && head != kHeadSilu && head != kHeadGated && head != kHeadRnn)
     return fail(DSPARK_EINVAL, "%s: unknown head %d", fn, head);
   if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0 || topk < 0)
     return fail(DSPARK_EINVAL, "%s: B, gamma, V, r must be positive, topk >= 0", fn);
@@ -355,10 +357,10 @@ extern "C" dspark_status_t dspark_markov_propose_head(
     int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
     hipStream_t stream) {
   const char* fn = "dspark_markov_propose_head";
-  if (head != kHeadLinear && head != kHeadSilu && head != kHeadGated)
+  if (head != kHeadLinear && head != kHeadSilu && head != kHeadGated && head != kHeadRnn)
     return fail(DSPARK_EINVAL, "%s: unknown head %d", fn, head);
-  if (head == kHeadGated) {
-    if (!h || !W_g || H <= 0) return fail(DSPARK_EINVAL, "%s: the gated head needs h, W_g and H > 0", fn);
+  if (head == kHeadGated || head == kHeadRnn) {
+    if (!h || !W_g || H <= 0) return fail(DSPARK_EINVAL, "%s: the gated and RNN heads need h, W_g and H > 0", fn);
     if (H > kMaxHeadHidden) return fail(DSPARK_EUNSUPPORTED, "%s: H > %d", fn, kMaxHeadHidden);
   }
   return propose_impl(fn, head, h, H, W_g, U, B, gamma, V, anchor, A, Bm, wdt, r, temperature, seeds, offset, topk,

@@ -159,8 +159,8 @@ hipError_t launch_block_logits(const float* U, const int32_t* prev, const void* 
                                int M, int V, int r, float* out, hipStream_t s, bool bf16);
 
 // sequential-head variants (markov_head_prep writes m_j before each position)
-constexpr int kHeadLinear = 0, kHeadSilu = 1, kHeadGated = 2;
-constexpr int kMaxHeadHidden = 16384;   // H of the gated head (h_j and A[x] in LDS)
+constexpr int kHeadLinear = 0, kHeadSilu = 1, kHeadGated = 2, kHeadRnn = 3;
+constexpr int kMaxHeadHidden = 16384;   // H of the gated and RNN heads (their input in LDS)
 hipError_t launch_head_prep(const StepArgs& a, bool bf16, int head, const void* h, int H, const void* Wg, void* M,
                             hipStream_t s);
 

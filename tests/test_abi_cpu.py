@@ -234,7 +234,9 @@ def test_head_variant_validation(L):
     st0, n0 = _ws(L.dspark_markov_propose_workspace, 4, 7, 151936, 16)
     assert st == bd.OK and st0 == bd.OK and n >= n0 + 4 * 7 * 256 * 2
     assert _ws(L.dspark_markov_propose_head_workspace, 0, 4, 7, 151936, 256, bd.BF16, 16)[1] == n0
-    assert _ws(L.dspark_markov_propose_head_workspace, 3, 4, 7, 151936, 256, bd.BF16, 16)[0] == bd.EINVAL
+    st3, n3 = _ws(L.dspark_markov_propose_head_workspace, 3, 4, 7, 151936, 256, bd.BF16, 16)
+    assert st3 == bd.OK and n3 >= n0 + 2 * 4 * 7 * 256 * 2                  # RNN: m_j and state tables
+    assert _ws(L.dspark_markov_propose_head_workspace, 4, 4, 7, 151936, 256, bd.BF16, 16)[0] == bd.EINVAL
     f = L.dspark_markov_propose_head
     args = lambda **k: [k.get(n, d) for n, d in (
         ("head", 2), ("h", FAKE), ("H", 2560), ("Wg", FAKE), ("U", FAKE), ("B", 4), ("gamma", 7),
@@ -247,3 +249,7 @@ def test_head_variant_validation(L):
     assert f(*args(H=16385)) == bd.EUNSUPPORTED
     assert f(*args()) == bd.EWORKSPACE
     assert f(*args(head=1, h=None, Wg=None, H=0)) == bd.EWORKSPACE     # SiLU needs no h
+    assert f(*args(head=3, h=None)) == bd.EINVAL                       # the RNN head reads h and W
+    assert f(*args(head=3, Wg=None)) == bd.EINVAL
+    assert f(*args(head=3, H=16385)) == bd.EUNSUPPORTED
+    assert f(*args(head=3)) == bd.EWORKSPACE

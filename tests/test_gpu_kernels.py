@@ -8,7 +8,8 @@ import torch
 import synth
 from oracle import dspark_oracle as o
 from semi_autoregressive_draft_amd import binding as bd
-from tests.parity import (ALPHA_ABS, check_chain, rel_check, require_gpu, tight_check, to_dev)
+from tests.parity import (ALPHA_ABS, REL, TIGHT, check_chain, check_topk, rel_check, require_gpu, tight_check,
+                          to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -736,3 +737,75 @@ def test_markov_head_variants_parity(head, B, V, r, wdtype, T, topk):
         kw.update(h=o.to_f64(h, wdtype), W_g=o.to_f64(W_g, wdtype))
     check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, wdtype), o.to_f64(Bm, wdtype), temperature=T,
                 seeds=seeds, offset=3, topk=topk, oracle_kw=kw)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,V,r,H,wdtype,T,topk", [
+    (5, 3000, 128, 96, "bf16", 0.0, 8),          # MFMA state and output kernels
+    (33, 2008, 64, 96, "bf16", 0.7, 16),         # wide step, sampled, top-16, ragged request block
+    (1, 4000, 256, 200, "bf16", 0.0, 16),        # one request, full rank
+    (3, 1000, 32, 90, "bf16", 0.0, 0),           # H % 8 != 0: one workgroup per request
+    (3, 1000, 48, 96, "f32", 0.0, 5),            # float32 tables
+])
+def test_markov_rnn_head_parity(B, V, r, H, wdtype, T, topk):
+    dev = require_gpu()
+    gamma, seed = 7, 31
+    print(f"rnn head B={B} V={V} r={r} H={H} {wdtype} T={T} topk={topk}", flush=True)
+    U, anchor, A, Bm = _markov_case(B, V, r, wdtype, seed=seed)
+    h = synth.normal((B, gamma, H), 1.0, seed, synth.TID_H, wdtype)
+    W = synth.normal((3 * r, 2 * r + H), 0.1, seed, synth.TID_WG, wdtype)
+    seeds = np.arange(B, dtype=np.uint64) + np.uint64(5) if T > 0 else None
+    tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    tl = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    ls = torch.empty_like(tl)
+    ti = torch.empty((B, gamma, topk), dtype=torch.int32, device=dev) if topk else None
+    tp = torch.empty((B, gamma, topk), dtype=torch.float32, device=dev) if topk else None
+    lo = torch.empty((B, gamma, V), dtype=torch.float32, device=dev)
+    wdt = bd.BF16 if wdtype == "bf16" else bd.F32
+    ws = torch.zeros(bd.dspark_markov_propose_head_workspace(bd.HEAD_RNN, B, gamma, V, r, wdt, topk),
+                     dtype=torch.uint8, device=dev)
+    bd.dspark_markov_propose_head(bd.HEAD_RNN, to_dev(U), to_dev(anchor), to_dev(A, wdtype), to_dev(Bm, wdtype),
+                                  tokens, h=to_dev(h, wdtype), W_g=to_dev(W, wdtype), temperature=T,
+                                  seeds=None if seeds is None else to_dev(seeds), offset=2, topk=topk,
+                                  tok_logit=tl, lse=ls, topk_idx=ti, topk_prob=tp, logits_out=lo, ws=ws)
+    torch.cuda.synchronize()
+    gpu = dict(tokens=tokens.cpu().numpy(), tok_logit=tl.cpu().numpy(), lse=ls.cpu().numpy(), logits=lo.cpu().numpy())
+    if topk:
+        gpu["topk_idx"], gpu["topk_prob"] = ti.cpu().numpy(), tp.cpu().numpy()
+    kw = dict(head="rnn", wdtype=wdtype, h=o.to_f64(h, wdtype), W_g=o.to_f64(W, wdtype))
+    # one step at a time: the workspace holds the m_j table and then the state
+    # table ([B, gamma, r] each, tables' dtype); every position must be the
+    # oracle's step from the GPU's own previous state and token, to within the
+    # rounding of s_j and m_j to the tables' dtype
+    es = 2 if wdtype == "bf16" else 4
+    off = bd.dspark_markov_propose_workspace(B, gamma, V, topk)
+    raw = ws[off:off + 2 * B * gamma * r * es].cpu().numpy()
+    if wdtype == "bf16":
+        tab = (raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        tab = raw.view(np.float32).astype(np.float64)
+    M_gpu, S_gpu = tab[:B * gamma * r].reshape(B, gamma, r), tab[B * gamma * r:].reshape(B, gamma, r)
+    A64, h64, W64 = o.to_f64(A, wdtype), kw["h"], kw["W_g"]
+    step_tol = 2.0 ** -7 if wdtype == "bf16" else 1e-5      # one bf16 ulp of the value, or fp32 accumulation
+    for b in range(B):
+        for j in range(gamma):
+            prev = int(anchor[b]) if j == 0 else int(gpu["tokens"][b, j - 1])
+            s_prev = S_gpu[b, j - 1] if j > 0 else np.zeros(r)
+            s_ref, m_ref = o.rnn_head_step(s_prev, A64[prev], h64[b, j], W64, wdtype)
+            for got, want, what in ((S_gpu[b, j], s_ref, "state"), (M_gpu[b, j], m_ref, "m")):
+                lim = step_tol * np.maximum(np.abs(want), np.sqrt((want ** 2).mean())) + 1e-6
+                err = np.abs(got - want)
+                assert (err <= (2 if what == "m" else 1) * lim).all(), (
+                    f"{what} b={b} j={j}: max err {err.max():.3g}")
+    # the chain: bf16 rounding flips of s_j and m_j carry into later positions,
+    # so the chain-level comparison keeps the 2e-2 bar; the step check is the tight one
+    tight = REL if wdtype == "bf16" else TIGHT
+    check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, wdtype), o.to_f64(Bm, wdtype), temperature=T,
+                seeds=seeds, offset=2, topk=0, oracle_kw=kw, tight=tight)
+    if topk:                # ranked on U + m_j Bm from the step-checked m_j table
+        Ut = U.astype(np.float64) + np.einsum("bjr,rv->bjv", M_gpu, o.to_f64(Bm, wdtype))
+        for b in range(B):
+            for j in range(gamma):
+                ridx = o.topk_indices(Ut[b, j], topk)
+                e = np.exp(Ut[b, j, ridx] - Ut[b, j, ridx[0]])
+                check_topk(gpu["topk_idx"][b, j], gpu["topk_prob"][b, j], Ut[b, j], ridx, e / e.sum())
