@@ -24,7 +24,7 @@
 // (tables' dtype, one row per position) follows the m_j table in the
 // workspace.  bf16 with H % 8 == 0: two MFMA launches per position, the state
 // (gate and candidate rows share each input fragment) and then the output,
-// laid out as the gated head's.  Otherwise one workgroup per request with z in LDS.
+// laid out as the gated head's with K split over four waves.  Otherwise one workgroup per request with z in LDS.
 #include "common.h"
 #include "internal.h"
 #include "markov_dev.h"
@@ -164,13 +164,17 @@ __device__ __forceinline__ u32x4 rnn_input8(const uint16_t* srow, bool has_s, co
   return *reinterpret_cast<const u32x4*>(hrow + (k - 2 * r));
 }
 
-// grid (ceil(r / 16), ceil(B / 16)), one wave each; OUT = false: gate and
-// candidate rows -> S[b, j]; OUT = true: output rows over [S[b, j]; ...] -> M[b, j]
+// grid (ceil(r / 16), ceil(B / 16)), kRnnWaves waves each, wave w taking the
+// 32-deep K chunks c = w mod kRnnWaves; wave 0 adds the others' partial sums
+// from LDS and finishes.  OUT = false: gate and candidate rows -> S[b, j];
+// OUT = true: output rows over [S[b, j]; ...] -> M[b, j]
+constexpr int kRnnWaves = 4;
 template <bool OUT>
-__global__ __launch_bounds__(kWave) void markov_head_rnn_bf16(StepArgs a, const uint16_t* __restrict__ h, int H,
+__global__ __launch_bounds__(kRnnWaves * kWave) void markov_head_rnn_bf16(StepArgs a, const uint16_t* __restrict__ h, int H,
                                                               const uint16_t* __restrict__ W,
                                                               uint16_t* __restrict__ M, uint16_t* __restrict__ S) {
-  const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+  __shared__ f32x4 red[2][kRnnWaves - 1][kWave];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, n = lane & 15;
   const int o0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
   const int r = a.r, D = 2 * r + H;
   const int bx = min(b0 + n, a.B - 1);                 // this lane's request row (A operand)
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(kWave) void markov_head_rnn_bf16(StepArgs a, const 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int nk = (D + 31) / 32;
 #pragma unroll 4
-  for (int c = 0; c < nk; ++c) {
+  for (int c = wv; c < nk; c += kRnnWaves) {
     const int k = 32 * c + 8 * g;
     u32x4 xa = {0u, 0u, 0u, 0u}, wa = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
     if (k < D) {
@@ -196,6 +200,17 @@ __global__ __launch_bounds__(kWave) void markov_head_rnn_bf16(StepArgs a, const 
     }
     acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(wa), acc0, 0, 0, 0);
     if (!OUT) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(wb), acc1, 0, 0, 0);
+  }
+  if (wv > 0) {
+    red[0][wv - 1][lane] = acc0;
+    if (!OUT) red[1][wv - 1][lane] = acc1;
+  }
+  __syncthreads();
+  if (wv > 0) return;
+#pragma unroll
+  for (int q = 0; q < kRnnWaves - 1; ++q) {
+    acc0 += red[0][q][lane];
+    if (!OUT) acc1 += red[1][q][lane];
   }
   const int o = o0 + n;
 #pragma unroll
@@ -226,8 +241,8 @@ hipError_t launch_head_rnn(const StepArgs& a, bool bf16, const void* h, int H, c
     const uint16_t* Wb = static_cast<const uint16_t*>(W);
     uint16_t* Mb = static_cast<uint16_t*>(M);
     uint16_t* Sb = static_cast<uint16_t*>(S);
-    hipLaunchKernelGGL(markov_head_rnn_bf16<false>, grid, dim3(kWave), 0, s, a, hb, H, Wb, Mb, Sb);
-    hipLaunchKernelGGL(markov_head_rnn_bf16<true>, grid, dim3(kWave), 0, s, a, hb, H, Wb, Mb, Sb);
+    hipLaunchKernelGGL(markov_head_rnn_bf16<false>, grid, dim3(kRnnWaves * kWave), 0, s, a, hb, H, Wb, Mb, Sb);
+    hipLaunchKernelGGL(markov_head_rnn_bf16<true>, grid, dim3(kRnnWaves * kWave), 0, s, a, hb, H, Wb, Mb, Sb);
     return hipGetLastError();
   }
   const size_t lds = static_cast<size_t>(3 * a.r + H) * 4;
