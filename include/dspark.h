@@ -36,6 +36,19 @@
  *     a message for the last non-OK status of the calling thread.
  *   - Token and anchor ids must lie in [0, V); this is the caller's contract
  *     and is not checked on the device.
+ *   - Device status word.  The calls whose kernels may wait for other
+ *     workgroups of the same launch (dspark_markov_propose and
+ *     dspark_markov_propose_head on the resident chain, dspark_overlap_tau and
+ *     dspark_compute_loss on the single-launch path for few rows) take an
+ *     optional `status` argument: a device pointer to one int32 (4-byte
+ *     aligned) or NULL.  The call's last kernel sets it to DSPARK_OK, or to
+ *     DSPARK_ETIMEOUT when one of those waits ran past its bound; the call's
+ *     outputs are then invalid.  Read it after synchronising the stream.
+ *     These waits rely on every workgroup of the launch being resident on
+ *     the device at once.  On an otherwise idle device that holds (the host
+ *     checks the occupancy before choosing such a launch); long-running
+ *     kernels on other streams can keep workgroups from starting, which is
+ *     the only way a wait can run out (100 ms bound per wait).
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -53,7 +66,9 @@ typedef enum {
   DSPARK_EINVAL = 1,       /* NULL where required, non-positive or too large size, inconsistent pointers */
   DSPARK_EUNSUPPORTED = 2, /* valid but not implemented: a dtype, an alignment, gamma > 16, topk > 32 ... */
   DSPARK_EWORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace query returned */
-  DSPARK_EHIP = 4          /* a HIP launch failed; dspark_last_error() has the HIP error string */
+  DSPARK_EHIP = 4,         /* a HIP launch failed; dspark_last_error() has the HIP error string */
+  DSPARK_ETIMEOUT = 5      /* never returned by a call: the value the device status word takes when a
+                              bounded wait inside a launch ran out (see the conventions above) */
 } dspark_status_t;
 
 typedef enum {
@@ -156,13 +171,17 @@ dspark_status_t dspark_markov_propose_plan(int64_t B, int64_t V, int64_t r, dspa
  *                                      bytes of extra writes)
  *   ws, ws_bytes  workspace of at least dspark_markov_propose_workspace() bytes,
  *                 zero-filled before its first use (see above)
- * A token of -1 marks a call whose resident chain (see
- * dspark_markov_propose_plan) waited past its time bound (100 ms per
- * position) for a workgroup that had not started, which only other long
- * work on the device can cause; that call's outputs are invalid.  On the
- * per-position path -1 marks a row with no orderable value (every U~_j[v]
- * NaN).  Rows of A are gathered with the previous token clamped into
- * [0, V), so invalid anchors or -1 tokens give wrong but bounded reads.
+ *   status     [1] int32 or NULL       device status word (see the conventions):
+ *                                      DSPARK_ETIMEOUT when the resident chain (see
+ *                                      dspark_markov_propose_plan) waited past its
+ *                                      time bound (100 ms per position) for a
+ *                                      workgroup that had not started; its tokens
+ *                                      are then -1 and every output is invalid
+ * On the per-position path a token of -1 marks a row with no orderable value
+ * (every U~_j[v] NaN); the status stays DSPARK_OK.  Rows of A are gathered
+ * with the previous token clamped into [0, V), so invalid anchors or -1
+ * tokens give wrong but bounded reads.  A status pointer that is not 4-byte
+ * aligned is EINVAL.
  * Requirements: B, gamma, V, r > 0; gamma <= 16; topk <= 32 and topk <= V;
  * V <= 2^31 - 1.  DSPARK_BF16: r % 32 == 0, r <= 1024, V % 8 == 0.
  * DSPARK_F32: r <= 1024.  Otherwise EUNSUPPORTED.  T must be finite and >= 0.
@@ -173,7 +192,7 @@ dspark_status_t dspark_markov_propose(const float* U, int64_t B, int64_t gamma, 
                                       float temperature, const uint64_t* seeds, uint64_t offset,
                                       int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
                                       int32_t* topk_idx, float* topk_prob, float* logits_out,
-                                      void* ws, size_t ws_bytes, hipStream_t stream);
+                                      void* ws, size_t ws_bytes, int32_t* status, hipStream_t stream);
 
 /*
  * Sequential-head variants of dspark_markov_propose.  [P4] §2.3 heads table:
@@ -186,7 +205,10 @@ dspark_status_t dspark_markov_propose(const float* U, int64_t B, int64_t gamma, 
  *                     s_j = (1 - g_j) s_{j-1} + g_j tanh(W_cand z_j) with
  *                     g_j = sigmoid(W_gate z_j), and
  *                     b_j = W_up SiLU(W_out [s_j; W_down[x_{j-1}]; h_j]);
- *                     s_j is kept in the tables' dtype,
+ *                     s_j is kept in the tables' dtype.  The passage's
+ *                     gate values did not survive its extraction, so "gate
+ *                     1 writes the candidate" is a chosen convention (the
+ *                     other one is this head with W_gate negated),
  * with W_down = A [V, r] and W_up = Bm^T; DSPARK_HEAD_LINEAR is
  * dspark_markov_propose itself.  The r-vector the up-projection receives is
  * rounded to the tables' dtype (bf16: to nearest, ties to even), as a module
@@ -244,7 +266,7 @@ dspark_status_t dspark_markov_propose_head(int32_t head, const void* h, int64_t 
                                            const uint64_t* seeds, uint64_t offset, int32_t topk,
                                            int32_t* tokens, float* tok_logit, float* lse,
                                            int32_t* topk_idx, float* topk_prob, float* logits_out,
-                                           void* ws, size_t ws_bytes, hipStream_t stream);
+                                           void* ws, size_t ws_bytes, int32_t* status, hipStream_t stream);
 
 /*
  * S5 -- confidence head and prefix survival.  [P1] Confidence head:
@@ -305,6 +327,8 @@ dspark_status_t dspark_overlap_tau_workspace(int64_t N, int64_t gamma, int64_t V
  *                  launch whose chunks wait for their row's normalisers; if
  *                  such a wait runs past its bound (100 ms, only possible when
  *                  other long work occupies the device) tau and tau_mean are NaN.
+ *   status         [1] int32 or NULL   device status word: DSPARK_ETIMEOUT when
+ *                  such a wait ran out (outputs invalid), else DSPARK_OK
  * Requirements: N, gamma, V > 0; gamma <= 16; V % 4 == 0 (16-byte rows);
  * dense mode: k == 0 and cand_* NULL; candidate mode: 1 <= k <= 64 and cand_*
  * non-NULL.
@@ -313,7 +337,7 @@ dspark_status_t dspark_overlap_tau(const float* teacher, const float* draft,
                                    const int32_t* cand_idx, const float* cand_prob, int32_t k,
                                    const uint8_t* valid, int64_t N, int64_t gamma, int64_t V,
                                    float* alpha, float* tau, double* accept_rate_at,
-                                   double* tau_mean, void* ws, size_t ws_bytes,
+                                   double* tau_mean, void* ws, size_t ws_bytes, int32_t* status,
                                    hipStream_t stream);
 
 /*
@@ -399,6 +423,8 @@ dspark_status_t dspark_compute_loss_workspace(int64_t B, int64_t gamma, int64_t 
  *                   out (only possible when other work occupies the device)
  *   ws, ws_bytes    workspace of at least dspark_compute_loss_workspace bytes,
  *                   zero-filled before its first use (a call leaves it ready)
+ *   status          [1] int32 or NULL: device status word, DSPARK_ETIMEOUT when
+ *                   the overlap pass's bounded wait ran out (losses are then NaN)
  * Requirements: B, gamma, V > 0; gamma <= 16; V % 4 == 0; decay_gamma > 0.
  */
 dspark_status_t dspark_compute_loss(const float* draft, const float* teacher, const int32_t* target,
@@ -406,7 +432,7 @@ dspark_status_t dspark_compute_loss(const float* draft, const float* teacher, co
                                     int64_t gamma, int64_t V, float lambda_ce, float lambda_l1,
                                     float lambda_conf, float decay_gamma, int32_t conf_decay,
                                     float* per_pos, double* losses, void* ws, size_t ws_bytes,
-                                    hipStream_t stream);
+                                    int32_t* status, hipStream_t stream);
 
 /*
  * Workspace size (bytes) needed by dspark_verify for these sizes.

@@ -174,15 +174,20 @@ def head_vector(head: str, a_row: np.ndarray, *, h_row: Optional[np.ndarray] = N
 # before the block's first position, and at each position reads the input
 # z_j = [s_{j-1}; W_down[x_{j-1}]; h_j] (width 2r + H, in that order).  A
 # sigmoid gate g_j = sigma(W_gate z_j) mixes the old state with the tanh
-# candidate c_j = tanh(W_cand z_j): gate 1 writes the candidate, gate 0 keeps
-# the old state.  The output re-reads the input with the updated state,
+# candidate c_j = tanh(W_cand z_j) (with the convention chosen below, gate 1
+# writes the candidate and gate 0 keeps the old state).  The output re-reads the input with the updated state,
 # z'_j = [s_j; W_down[x_{j-1}]; h_j], projects it to rank r and applies the
 # activation; W_up maps the result to the vocabulary.  Readings where the
-# pages' formulas did not survive extraction: the state update is the convex
-# mix (1 - g) * s_{j-1} + g * c_j that the passage's two limiting cases
-# describe; the unnamed output activation is SiLU, the activation of the
-# pages' SiLU-Vanilla head; the state, like m_j, is handed on in the tables'
-# dtype.  W_rnn stacks [W_gate; W_cand; W_out] as [3r, 2r + H].
+# pages' formulas did not survive extraction: the state update is a convex
+# mix of the old state and the candidate under the gate, as the passage's two
+# limiting cases describe (one gate value keeps the old state, the other
+# writes the candidate), but the gate values themselves are missing from the
+# extracted text, so which end writes the candidate is a chosen convention,
+# not one the page fixes: here s_j = (1 - g) * s_{j-1} + g * c_j (gate 1
+# writes).  The opposite convention is the same model with W_gate negated.
+# The unnamed output activation is SiLU, the activation of the pages'
+# SiLU-Vanilla head; the state, like m_j, is handed on in the tables' dtype.
+# W_rnn stacks [W_gate; W_cand; W_out] as [3r, 2r + H].
 
 
 def rnn_head_step(s_prev: np.ndarray, a_row: np.ndarray, h_row: np.ndarray, W_rnn: np.ndarray,

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdspark.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "dspark.h")
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ETIMEOUT = range(6)
 F32, BF16 = 0, 1
 
 _vp, _i64, _i32, _f32, _u64, _sz = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_uint64, C.c_size_t
@@ -31,17 +31,17 @@ _SIGNATURES = {
     "dspark_markov_propose_plan": (C.c_int, [_i64, _i64, _i64, C.c_int, C.POINTER(_i32)]),
     "dspark_markov_propose": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64,
                                         _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
-                                        _vp, _sz, _vp]),
+                                        _vp, _sz, _vp, _vp]),
     "dspark_confidence_survival": (C.c_int, [_vp, C.c_int, _i64, _i64, _i64, _vp, _f32, _vp, _vp,
                                              _i64, _vp, _vp, _vp, _vp, _vp]),
     "dspark_overlap_tau_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
     "dspark_overlap_tau": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _vp,
-                                     _vp, _vp, _vp, _sz, _vp]),
+                                     _vp, _vp, _vp, _sz, _vp, _vp]),
     "dspark_prefix_schedule": (C.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
     "dspark_apply_block_logits": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64, _vp, _vp]),
     "dspark_compute_loss_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
     "dspark_compute_loss": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _f32, _f32, _f32,
-                                      _i32, _vp, _vp, _vp, _sz, _vp]),
+                                      _i32, _vp, _vp, _vp, _sz, _vp, _vp]),
     "dspark_verify_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
     "dspark_markov_propose_head_workspace": (C.c_int, [_i32, _i64, _i64, _i64, _i64, C.c_int, _i32,
                                                        C.POINTER(_sz)]),
@@ -49,7 +49,7 @@ _SIGNATURES = {
                                                       C.POINTER(_sz)]),
     "dspark_markov_propose_head": (C.c_int, [_i32, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                                              C.c_int, _i64, _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp,
-                                             _vp, _vp, _sz, _vp]),
+                                             _vp, _vp, _sz, _vp, _vp]),
     "dspark_verify": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _u64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
@@ -96,6 +96,20 @@ def version() -> str:
 def _check(status: int) -> None:
     if status != OK:
         raise DsparkError(status, last_error())
+
+
+def check_device_status(status, what: str = "dspark") -> None:
+    """Raise DsparkError(ETIMEOUT) if a device status word (an int32 tensor
+    that a call's ``status`` argument pointed at) reports a bounded wait that
+    ran out.  Reading a device tensor synchronises with its stream, so the
+    call's kernels have finished when the word is read."""
+    vals = status.detach().reshape(-1).cpu().tolist()
+    for v in vals:
+        if v == ETIMEOUT:
+            raise DsparkError(ETIMEOUT, f"{what}: a bounded wait inside the launch ran out (other work kept "
+                                        "its workgroups from starting); the outputs are invalid")
+        if v != OK:
+            raise DsparkError(int(v), f"{what}: unexpected device status {v}")
 
 
 # ---------------------------------------------------------------------------
@@ -156,8 +170,9 @@ def dspark_markov_propose_plan(B: int, V: int, r: int, wdtype: int = BF16) -> in
 
 def dspark_markov_propose(U, anchor, A, Bm, tokens, *, temperature: float = 0.0, seeds=None,
                           offset: int = 0, topk: int = 0, tok_logit=None, lse=None, topk_idx=None,
-                          topk_prob=None, logits_out=None, ws=None, stream=None) -> None:
-    """Sequential Markov proposal over U [B, gamma, V]; writes tokens [B, gamma]."""
+                          topk_prob=None, logits_out=None, ws=None, status=None, stream=None) -> None:
+    """Sequential Markov proposal over U [B, gamma, V]; writes tokens [B, gamma]
+    (status: optional int32 device word, see check_device_status)."""
     import torch
     B, gamma, V = U.shape
     r = A.shape[1]
@@ -167,7 +182,8 @@ def dspark_markov_propose(U, anchor, A, Bm, tokens, *, temperature: float = 0.0,
     _check(lib().dspark_markov_propose(
         _ptr(U), B, gamma, V, _ptr(anchor), _ptr(A), _ptr(Bm), _dtype(A), r, float(temperature),
         _ptr(seeds), int(offset), int(topk), _ptr(tokens), _ptr(tok_logit), _ptr(lse),
-        _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(ws), ws.numel(), _ptr(status),
+        _stream(stream)))
 
 
 def dspark_confidence_survival(h, w_c, b_c: float, conf, survival, *, w_m=None, A=None,
@@ -187,7 +203,8 @@ def dspark_overlap_tau_workspace(N: int, gamma: int, V: int) -> int:
 
 
 def dspark_overlap_tau(teacher, alpha, tau, *, draft=None, cand_idx=None, cand_prob=None,
-                       valid=None, accept_rate_at=None, tau_mean=None, ws=None, stream=None) -> None:
+                       valid=None, accept_rate_at=None, tau_mean=None, ws=None, status=None,
+                       stream=None) -> None:
     """alpha [N, gamma], tau [N] (+ aggregates) from teacher [N, gamma, V]."""
     import torch
     N, gamma, V = teacher.shape
@@ -198,7 +215,7 @@ def dspark_overlap_tau(teacher, alpha, tau, *, draft=None, cand_idx=None, cand_p
     _check(lib().dspark_overlap_tau(
         _ptr(teacher), _ptr(draft), _ptr(cand_idx), _ptr(cand_prob), k, _ptr(valid), N, gamma, V,
         _ptr(alpha), _ptr(tau), _ptr(accept_rate_at), _ptr(tau_mean), _ptr(ws), ws.numel(),
-        _stream(stream)))
+        _ptr(status), _stream(stream)))
 
 
 def dspark_prefix_schedule(survival, sps, lengths, stats, stream=None) -> None:
@@ -224,7 +241,8 @@ def dspark_compute_loss_workspace(B: int, gamma: int, V: int) -> int:
 
 def dspark_compute_loss(draft, teacher, target, losses, *, conf_logit=None, valid=None, per_pos=None,
                         lambda_ce: float = 0.1, lambda_l1: float = 0.9, lambda_conf: float = 1.0,
-                        decay_gamma: float = 4.0, conf_decay: bool = False, ws=None, stream=None) -> None:
+                        decay_gamma: float = 4.0, conf_decay: bool = False, ws=None, status=None,
+                        stream=None) -> None:
     """losses [4] float64 (total, CE, L1, conf) and optional per_pos [B, gamma, 4]."""
     import torch
     B, gamma, V = draft.shape
@@ -233,7 +251,7 @@ def dspark_compute_loss(draft, teacher, target, losses, *, conf_logit=None, vali
     _check(lib().dspark_compute_loss(
         _ptr(draft), _ptr(teacher), _ptr(target), _ptr(conf_logit), _ptr(valid), B, gamma, V,
         float(lambda_ce), float(lambda_l1), float(lambda_conf), float(decay_gamma), int(bool(conf_decay)),
-        _ptr(per_pos), _ptr(losses), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(per_pos), _ptr(losses), _ptr(ws), ws.numel(), _ptr(status), _stream(stream)))
 
 
 def dspark_verify_workspace(B: int, gamma: int, V: int) -> int:
@@ -276,7 +294,8 @@ def dspark_markov_propose_workspace_bmt(head: int, B: int, gamma: int, V: int, r
 
 def dspark_markov_propose_head(head: int, U, anchor, A, Bm, tokens, *, h=None, W_g=None, temperature: float = 0.0,
                                seeds=None, offset: int = 0, topk: int = 0, tok_logit=None, lse=None,
-                               topk_idx=None, topk_prob=None, logits_out=None, ws=None, stream=None) -> None:
+                               topk_idx=None, topk_prob=None, logits_out=None, ws=None, status=None,
+                               stream=None) -> None:
     """dspark_markov_propose with a sequential-head variant (HEAD_SILU, HEAD_GATED, HEAD_RNN;
     W_g is the gated head's [r, H + r] or the RNN head's stacked [3r, 2r + H])."""
     import torch
@@ -289,4 +308,5 @@ def dspark_markov_propose_head(head: int, U, anchor, A, Bm, tokens, *, h=None, W
     _check(lib().dspark_markov_propose_head(
         head, _ptr(h), H, _ptr(W_g), _ptr(U), B, gamma, V, _ptr(anchor), _ptr(A), _ptr(Bm), _dtype(A), r,
         float(temperature), _ptr(seeds), int(offset), int(topk), _ptr(tokens), _ptr(tok_logit), _ptr(lse),
-        _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(ws), ws.numel(), _ptr(status),
+        _stream(stream)))

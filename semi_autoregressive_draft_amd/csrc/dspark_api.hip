@@ -30,6 +30,7 @@ dspark_status_t hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -213,7 +214,7 @@ dspark_status_t propose_impl(
     const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
     uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
     int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
-    hipStream_t stream) {
+    int32_t* status, hipStream_t stream) {
   if (!U || !anchor || !A || !Bm || !tokens)
     return fail(DSPARK_EINVAL, "%s: U, anchor, A, Bm and tokens must be non-NULL", fn);
   if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0)
@@ -229,6 +230,7 @@ dspark_status_t propose_impl(
   if (topk == 0 && (topk_idx || topk_prob))
     return fail(DSPARK_EINVAL, "%s: topk_idx/topk_prob must be NULL when topk == 0", fn);
   if (topk > V) return fail(DSPARK_EINVAL, "%s: topk > V", fn);
+  if (!aligned4(status)) return fail(DSPARK_EINVAL, "%s: status must be 4-byte aligned", fn);
   if (gamma > kMaxGamma) return fail(DSPARK_EUNSUPPORTED, "%s: gamma > %d", fn, kMaxGamma);
   if (topk > kMaxTopk) return fail(DSPARK_EUNSUPPORTED, "%s: topk > %d", fn, kMaxTopk);
   if (wdt != DSPARK_F32 && wdt != DSPARK_BF16) return fail(DSPARK_EUNSUPPORTED, "%s: unknown dtype %d", fn, (int)wdt);
@@ -279,6 +281,7 @@ dspark_status_t propose_impl(
   a.topk = topk;
   a.topk_idx = topk_idx;
   a.topk_prob = topk_prob;
+  a.status = status;
   int nwg = 0;
   size_t lds = 0;
   // the head variants run per position: the prep kernel writes m_j between positions
@@ -318,10 +321,10 @@ extern "C" dspark_status_t dspark_markov_propose(
     const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
     uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
     int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
-    hipStream_t stream) {
+    int32_t* status, hipStream_t stream) {
   return propose_impl("dspark_markov_propose", kHeadLinear, nullptr, 0, nullptr, U, B, gamma, V, anchor, A, Bm,
                       wdt, r, temperature, seeds, offset, topk, tokens, tok_logit, lse, topk_idx, topk_prob,
-                      logits_out, ws, ws_bytes, stream);
+                      logits_out, ws, ws_bytes, status, stream);
 }
 
 extern "C" dspark_status_t dspark_markov_propose_head_workspace(int32_t head, int64_t B, int64_t gamma, int64_t V,
@@ -355,7 +358,7 @@ extern "C" dspark_status_t dspark_markov_propose_head(
     const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
     uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
     int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
-    hipStream_t stream) {
+    int32_t* status, hipStream_t stream) {
   const char* fn = "dspark_markov_propose_head";
   if (head != kHeadLinear && head != kHeadSilu && head != kHeadGated && head != kHeadRnn)
     return fail(DSPARK_EINVAL, "%s: unknown head %d", fn, head);
@@ -364,7 +367,7 @@ extern "C" dspark_status_t dspark_markov_propose_head(
     if (H > kMaxHeadHidden) return fail(DSPARK_EUNSUPPORTED, "%s: H > %d", fn, kMaxHeadHidden);
   }
   return propose_impl(fn, head, h, H, W_g, U, B, gamma, V, anchor, A, Bm, wdt, r, temperature, seeds, offset, topk,
-                      tokens, tok_logit, lse, topk_idx, topk_prob, logits_out, ws, ws_bytes, stream);
+                      tokens, tok_logit, lse, topk_idx, topk_prob, logits_out, ws, ws_bytes, status, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -401,7 +404,7 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
                                               int32_t k, const uint8_t* valid, int64_t N,
                                               int64_t gamma, int64_t V, float* alpha, float* tau,
                                               double* accept_rate_at, double* tau_mean, void* ws,
-                                              size_t ws_bytes, hipStream_t stream) {
+                                              size_t ws_bytes, int32_t* status, hipStream_t stream) {
   const char* fn = "dspark_overlap_tau";
   if (!teacher || !alpha || !tau) return fail(DSPARK_EINVAL, "%s: teacher, alpha, tau must be non-NULL", fn);
   if (N <= 0 || gamma <= 0 || V <= 0) return fail(DSPARK_EINVAL, "%s: N, gamma, V must be positive", fn);
@@ -419,6 +422,7 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
   if (V % 4) return fail(DSPARK_EUNSUPPORTED, "%s: V %% 4 != 0", fn);
   if (!aligned16(teacher) || (draft && !aligned16(draft)))
     return fail(DSPARK_EUNSUPPORTED, "%s: teacher/draft must be 16-byte aligned", fn);
+  if (!aligned4(status)) return fail(DSPARK_EINVAL, "%s: status must be 4-byte aligned", fn);
   const size_t need = overlap_ws_bytes(N, gamma, V);
   if (!ws || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
@@ -436,6 +440,7 @@ extern "C" dspark_status_t dspark_overlap_tau(const float* teacher, const float*
   a.tau = tau;
   a.accept_rate_at = accept_rate_at;
   a.tau_mean = tau_mean;
+  a.status = status;
   carve_overlap_ws(a, ws, N, gamma, V);
   return hip_status(launch_overlap_tau(a, stream), fn);
 }
@@ -493,7 +498,7 @@ extern "C" dspark_status_t dspark_compute_loss(const float* draft, const float* 
                                                int64_t gamma, int64_t V, float lambda_ce, float lambda_l1,
                                                float lambda_conf, float decay_gamma, int32_t conf_decay,
                                                float* per_pos, double* losses, void* ws, size_t ws_bytes,
-                                               hipStream_t stream) {
+                                               int32_t* status, hipStream_t stream) {
   const char* fn = "dspark_compute_loss";
   if (!draft || !teacher || !target || !losses)
     return fail(DSPARK_EINVAL, "%s: draft, teacher, target and losses must be non-NULL", fn);
@@ -507,6 +512,7 @@ extern "C" dspark_status_t dspark_compute_loss(const float* draft, const float* 
   if (V % 4) return fail(DSPARK_EUNSUPPORTED, "%s: V %% 4 != 0", fn);
   if (!aligned16(teacher) || !aligned16(draft))
     return fail(DSPARK_EUNSUPPORTED, "%s: teacher/draft must be 16-byte aligned", fn);
+  if (!aligned4(status)) return fail(DSPARK_EINVAL, "%s: status must be 4-byte aligned", fn);
   const size_t need = loss_ws_bytes(B, gamma, V);
   if (!ws || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
@@ -527,6 +533,7 @@ extern "C" dspark_status_t dspark_compute_loss(const float* draft, const float* 
   o.tau = tau;
   o.lse_draft = lse_d;
   o.ov_sum = ov;
+  o.status = status;
   carve_overlap_ws(o, ws, B, gamma, V);
   hipError_t e = launch_overlap_tau(o, stream);
   if (e != hipSuccess) return hip_status(e, fn);

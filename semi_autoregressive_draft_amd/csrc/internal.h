@@ -33,6 +33,9 @@ constexpr int kSyncKeys = 4096;                         // word offset of the gr
 static_assert(kSyncRelease + 64 * kFanIn <= kSyncKeys, "wait-tree layout");
 static_assert(kSyncKeys + 2 * kMaxGamma * kFanIn * kResidentMaxB <= kSyncWords, "wait-tree size");
 constexpr int kOvSyncWords = 8192;      // 32 KB: the single-launch overlap's counters (zero at launch)
+// values of the optional device status word (the header's dspark_status_t)
+constexpr int32_t kStatusOk = 0;
+constexpr int32_t kStatusTimeout = 5;
 
 // Arguments of one Markov position (step + merge kernels).
 struct StepArgs {
@@ -76,6 +79,9 @@ struct StepArgs {
   int topk;
   int32_t* topk_idx;       // [B, gamma, topk]
   float* topk_prob;
+  // optional: written once per call by the fold of the last position of
+  // request 0 (kStatusTimeout when the resident chain's wait ran out)
+  int32_t* status;
 };
 
 size_t markov_partials(int64_t V);
@@ -137,6 +143,9 @@ struct OverlapArgs {
   // log-normaliser and the unclamped sum of min(p, q)
   float* lse_draft;
   float* ov_sum;
+  // optional: written once per call by the workgroup that finishes tau
+  // (kStatusTimeout when a wait of the single-launch path ran out)
+  int32_t* status;
 };
 
 // training-loss finish: per-row CE, L1, alpha, BCE and the weighted aggregates

@@ -123,6 +123,9 @@ __device__ void fold_request(const StepArgs& a, int b, int j, bool from_key, Fol
     else f.token = (s.idx >= 0 && s.idx < a.V) ? s.idx : -1;   // -1: no orderable value (NaN row)
     f.tok_logit = s.x;
     f.lse = l.m + logf(l.s);
+    // every fold of a call reads the same time-out word, so one of them reports it
+    if (a.status && b == 0 && j == a.gamma - 1)
+      *a.status = (from_key && mark == a.epoch) ? kStatusTimeout : kStatusOk;
     if (out) *out = f;
     else store_fold(a, row, from_key, f);
   }

@@ -291,6 +291,7 @@ __device__ void tau_range(const OverlapArgs& a, int blk) {
     __syncthreads();
     if (tid < G && a.accept_rate_at) a.accept_rate_at[tid] = tot[G + tid] > 0.0 ? tot[tid] / tot[G + tid] : 0.0;
     if (tid == 0 && a.tau_mean) *a.tau_mean = tot[2 * G + 1] > 0.0 ? tot[2 * G] / tot[2 * G + 1] : 0.0;
+    if (tid == 0 && a.status) *a.status = kStatusOk;   // these paths never wait
   }
 }
 
@@ -405,6 +406,7 @@ __device__ void fused_tau(const OverlapArgs& a, const float* al_s, const unsigne
     }
     *a.tau_mean = timed_out ? static_cast<double>(nan) : (s2 > 0.0 ? s1 / s2 : 0.0);
   }
+  if (tid == 0 && a.status) *a.status = timed_out ? kStatusTimeout : kStatusOk;
 }
 
 // By wave 0: the teacher and draft log-normalisers of `row` from its chunk
@@ -598,6 +600,7 @@ __global__ __launch_bounds__(64) void tau_finish(OverlapArgs a) {
   __syncthreads();
   if (f < G && a.accept_rate_at) a.accept_rate_at[f] = tot[G + f] > 0.0 ? tot[f] / tot[G + f] : 0.0;
   if (f == 0 && a.tau_mean) *a.tau_mean = tot[2 * G + 1] > 0.0 ? tot[2 * G] / tot[2 * G + 1] : 0.0;
+  if (f == 0 && a.status) *a.status = kStatusOk;
 }
 
 int overlap_tau_blocks(int64_t N) { return static_cast<int>((N + kTauThreads - 1) / kTauThreads); }

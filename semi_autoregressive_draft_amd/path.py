@@ -49,6 +49,8 @@ class DraftPath:
         ws = (bd.dspark_markov_propose_workspace_bmt(bd.HEAD_LINEAR, B, gamma, V, A.shape[1], bd._dtype(A), topk)
               if topk else bd.dspark_markov_propose_workspace(B, gamma, V, topk))
         self.ws_markov = torch.zeros(ws, dtype=torch.uint8, device=dev)
+        # device status words of the propose and overlap calls (see check())
+        self.status = torch.zeros((2,), dtype=torch.int32, device=dev)
         self.conf = torch.empty((B, gamma), **f32)
         self.survival = torch.empty((B, gamma), **f32)
         if overlap:
@@ -75,7 +77,8 @@ class DraftPath:
                                  temperature=self.temperature, seeds=self.seeds, offset=self.offset,
                                  topk=self.topk, tok_logit=self.tok_logit, lse=self.lse,
                                  topk_idx=self.topk_idx, topk_prob=self.topk_prob,
-                                 logits_out=self.logits, ws=self.ws_markov, stream=stream)
+                                 logits_out=self.logits, ws=self.ws_markov, status=self.status[0:1],
+                                 stream=stream)
 
     def confidence(self, stream=None):
         bd.dspark_confidence_survival(self.h.view(self.B, self.gamma, self.H), self.w_c, self.b_c,
@@ -86,11 +89,12 @@ class DraftPath:
         if self.overlap == "dense":
             bd.dspark_overlap_tau(self.teacher, self.alpha, self.tau, draft=self.logits,
                                   accept_rate_at=self.accept_rate, tau_mean=self.tau_mean,
-                                  ws=self.ws_overlap, stream=stream)
+                                  ws=self.ws_overlap, status=self.status[1:2], stream=stream)
         elif self.overlap == "topk":
             bd.dspark_overlap_tau(self.teacher, self.alpha, self.tau, cand_idx=self.topk_idx,
                                   cand_prob=self.topk_prob, accept_rate_at=self.accept_rate,
-                                  tau_mean=self.tau_mean, ws=self.ws_overlap, stream=stream)
+                                  tau_mean=self.tau_mean, ws=self.ws_overlap, status=self.status[1:2],
+                                  stream=stream)
 
     def run(self, stream=None, lm_done=None):
         """One pass; lm_done (optional event) is recorded right after the
@@ -104,3 +108,8 @@ class DraftPath:
             self.confidence(main)
         if self.overlap:
             self.overlap_tau(main)
+
+    def check(self):
+        """Wait for the last pass and raise DsparkError(ETIMEOUT) if one of its
+        bounded waits ran out (its outputs are then invalid)."""
+        bd.check_device_status(self.status, "DraftPath")

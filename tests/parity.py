@@ -93,18 +93,19 @@ def check_chain(gpu: dict, U, anchor, A, Bm, *, temperature=0.0, seeds=None, off
     return ties
 
 
-def check_topk(gidx, gprob, ut, ridx, rprob):
+def check_topk(gidx, gprob, ut, ridx, rprob, gap=TOKEN_GAP):
     """Top-k candidates: identical ids unless the oracle's k+1 largest values
-    hold a near-tie, in which case the GPU's ids must carry the same values
-    (to the gap) in non-increasing order; probabilities to the bars."""
+    hold a near-tie (two neighbours closer than ``gap``), in which case the
+    GPU's ids must carry the same values (to the gap) in non-increasing order;
+    probabilities to the bars."""
     k = len(ridx)
     gidx = np.asarray(gidx, dtype=np.int64)
     assert len(set(gidx.tolist())) == k, "duplicate candidate ids"
     top = np.sort(ut)[::-1][:k + 1]
-    near = (np.diff(top) > -TOKEN_GAP).any()
+    near = (np.diff(top) > -gap).any()
     if not near:
         assert np.array_equal(gidx, ridx), f"top-k ids differ: {gidx} vs {ridx}"
     else:
-        assert np.all(np.abs(ut[gidx] - ut[ridx]) < TOKEN_GAP)
+        assert np.all(np.abs(ut[gidx] - ut[ridx]) < gap)
     rel_check(gprob, rprob, np.full(k, 1.0 / k), what="topk_prob")
     assert abs(float(np.sum(gprob)) - 1.0) < 1e-5

@@ -105,13 +105,14 @@ def test_lm_head_confidence_validation(L):
 def _propose(L, **kw):
     a = dict(U=FAKE, B=1, gamma=7, V=151936, anchor=FAKE, A=FAKE, Bm=FAKE, wdt=bd.BF16, r=256,
              T=0.0, seeds=None, offset=0, topk=0, tokens=FAKE, tok_logit=None, lse=None,
-             topk_idx=None, topk_prob=None, logits_out=None, ws=None, ws_bytes=0, stream=None)
+             topk_idx=None, topk_prob=None, logits_out=None, ws=None, ws_bytes=0, status=None,
+             stream=None)
     a.update(kw)
     return L.dspark_markov_propose(a["U"], a["B"], a["gamma"], a["V"], a["anchor"], a["A"], a["Bm"],
                                    a["wdt"], a["r"], a["T"], a["seeds"], a["offset"], a["topk"],
                                    a["tokens"], a["tok_logit"], a["lse"], a["topk_idx"],
                                    a["topk_prob"], a["logits_out"], a["ws"], a["ws_bytes"],
-                                   a["stream"])
+                                   a["status"], a["stream"])
 
 
 def test_markov_validation(L):
@@ -138,6 +139,10 @@ def test_markov_validation(L):
     assert "workspace" in bd.last_error()
     # float32 tables accept any rank and V
     assert _propose(L, wdt=bd.F32, r=48, V=151932) == bd.EWORKSPACE
+    # the optional device status word: NULL or a 4-byte aligned int32
+    assert _propose(L, status=FAKE) == bd.EWORKSPACE
+    assert _propose(L, status=FAKE + 2) == bd.EINVAL
+    assert "status" in bd.last_error()
 
 
 def test_confidence_validation(L):
@@ -154,7 +159,7 @@ def test_overlap_validation(L):
     args = lambda **k: [k.get(n, d) for n, d in (
         ("teacher", FAKE), ("draft", FAKE), ("idx", None), ("prob", None), ("k", 0), ("valid", None),
         ("N", 4), ("gamma", 7), ("V", 151936), ("alpha", FAKE), ("tau", FAKE), ("acc", None),
-        ("mean", None), ("ws", None), ("wsb", 0), ("s", None))]
+        ("mean", None), ("ws", None), ("wsb", 0), ("status", None), ("s", None))]
     assert f(*args(teacher=None)) == bd.EINVAL
     assert f(*args(k=16)) == bd.EINVAL                       # dense with k
     assert f(*args(draft=None)) == bd.EINVAL                 # sparse without candidates
@@ -165,6 +170,8 @@ def test_overlap_validation(L):
     assert f(*args(draft=MISALIGNED)) == bd.EUNSUPPORTED
     assert f(*args()) == bd.EWORKSPACE
     assert f(*args(draft=None, idx=FAKE, prob=FAKE, k=16)) == bd.EWORKSPACE
+    assert f(*args(status=FAKE)) == bd.EWORKSPACE
+    assert f(*args(status=FAKE + 1)) == bd.EINVAL
 
 
 def test_prefix_schedule_validation(L):
@@ -199,7 +206,7 @@ def test_block_logits_and_loss_validation(L):
     largs = lambda **k: [k.get(n, d) for n, d in (
         ("draft", FAKE), ("teacher", FAKE), ("target", FAKE), ("conf", None), ("valid", None), ("B", 4),
         ("gamma", 7), ("V", 151936), ("lce", 0.1), ("ll1", 0.9), ("lcf", 1.0), ("decay", 4.0), ("cd", 0),
-        ("per", None), ("losses", FAKE), ("ws", None), ("wsb", 0), ("s", None))]
+        ("per", None), ("losses", FAKE), ("ws", None), ("wsb", 0), ("status", None), ("s", None))]
     assert g(*largs(target=None)) == bd.EINVAL
     assert g(*largs(losses=None)) == bd.EINVAL
     assert g(*largs(decay=0.0)) == bd.EINVAL
@@ -208,6 +215,7 @@ def test_block_logits_and_loss_validation(L):
     assert g(*largs(V=151934)) == bd.EUNSUPPORTED
     assert g(*largs(draft=MISALIGNED)) == bd.EUNSUPPORTED
     assert g(*largs()) == bd.EWORKSPACE
+    assert g(*largs(status=FAKE + 3)) == bd.EINVAL
 
 
 def test_verify_validation(L):
@@ -242,7 +250,7 @@ def test_head_variant_validation(L):
         ("head", 2), ("h", FAKE), ("H", 2560), ("Wg", FAKE), ("U", FAKE), ("B", 4), ("gamma", 7),
         ("V", 151936), ("anchor", FAKE), ("A", FAKE), ("Bm", FAKE), ("dt", bd.BF16), ("r", 256),
         ("T", 0.0), ("seeds", None), ("off", 0), ("topk", 0), ("tok", FAKE), ("tl", None), ("lse", None),
-        ("ti", None), ("tp", None), ("lo", None), ("ws", None), ("wsb", 0), ("s", None))]
+        ("ti", None), ("tp", None), ("lo", None), ("ws", None), ("wsb", 0), ("status", None), ("s", None))]
     assert f(*args(head=5)) == bd.EINVAL
     assert f(*args(h=None)) == bd.EINVAL
     assert f(*args(Wg=None)) == bd.EINVAL
@@ -253,3 +261,22 @@ def test_head_variant_validation(L):
     assert f(*args(head=3, Wg=None)) == bd.EINVAL
     assert f(*args(head=3, H=16385)) == bd.EUNSUPPORTED
     assert f(*args(head=3)) == bd.EWORKSPACE
+    assert f(*args(head=3, status=FAKE + 2)) == bd.EINVAL
+
+
+def test_device_status_word_host_check():
+    """The host side of the device status word: DSPARK_OK passes, the
+    time-out value raises ETIMEOUT, anything else raises with its value (the
+    words here are host tensors standing in for ones read back from the GPU)."""
+    import torch
+    bd.check_device_status(torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(bd.DsparkError) as e:
+        bd.check_device_status(torch.tensor([0, bd.ETIMEOUT], dtype=torch.int32), "overlap")
+    assert e.value.status == bd.ETIMEOUT and "overlap" in str(e.value)
+    with pytest.raises(bd.DsparkError) as e:
+        bd.check_device_status(torch.tensor([7], dtype=torch.int32))
+    assert e.value.status == 7
+    # the header's value of the time-out status is the binding's
+    with open(bd.HEADER) as f:
+        assert "DSPARK_ETIMEOUT = 5" in f.read()
+    assert bd.ETIMEOUT == 5
