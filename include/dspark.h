@@ -195,6 +195,33 @@ dspark_status_t dspark_markov_propose(const float* U, int64_t B, int64_t gamma, 
                                       void* ws, size_t ws_bytes, int32_t* status, hipStream_t stream);
 
 /*
+ * dspark_markov_propose without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call allocates nothing: its workspace
+ * is a static scratch array of 64 MiB inside the library, one copy per
+ * device, held until the process ends and zero-filled by a kernel on
+ * `stream` at the first call on each device.
+ *   - Limit: sizes whose dspark_markov_propose_workspace() exceeds 64 MiB are
+ *     rejected with DSPARK_EWORKSPACE before any device work (at V = 151936
+ *     with top-16: B = 64 fits, B = 256 does not).
+ *   - Every call on a device shares that device's scratch, which keeps the
+ *     last call's contents: calls that overlap in time on one device (other
+ *     threads, other streams) race and give wrong results; calls issued in
+ *     order on one stream are safe.
+ *   - The top-k recompute of the per-position path reads Bm directly (no
+ *     transposed copy); results equal dspark_markov_propose's with the plain
+ *     workspace.
+ * Every other argument, output, rule and error is dspark_markov_propose's.
+ */
+dspark_status_t dspark_markov_propose_noalloc(const float* U, int64_t B, int64_t gamma, int64_t V,
+                                              const int32_t* anchor, const void* A, const void* Bm,
+                                              dspark_dtype_t wdt, int64_t r,
+                                              float temperature, const uint64_t* seeds, uint64_t offset,
+                                              int32_t topk, int32_t* tokens, float* tok_logit,
+                                              float* lse, int32_t* topk_idx, float* topk_prob,
+                                              float* logits_out, int32_t* status, hipStream_t stream);
+
+/*
  * Sequential-head variants of dspark_markov_propose.  [P4] §2.3 heads table:
  *   DSPARK_HEAD_SILU  (VanillaMarkov): b_j = W_up SiLU(W_down[x_{j-1}]),
  *   DSPARK_HEAD_GATED (GatedMarkovHead): g_j = sigmoid(W_g [h_j; W_down[x_{j-1}]]),

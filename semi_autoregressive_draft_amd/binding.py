@@ -32,6 +32,9 @@ _SIGNATURES = {
     "dspark_markov_propose": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64,
                                         _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp, _vp]),
+    "dspark_markov_propose_noalloc": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, C.c_int, _i64,
+                                                _f32, _vp, _u64, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _vp, _vp]),
     "dspark_confidence_survival": (C.c_int, [_vp, C.c_int, _i64, _i64, _i64, _vp, _f32, _vp, _vp,
                                              _i64, _vp, _vp, _vp, _vp, _vp]),
     "dspark_overlap_tau_workspace": (C.c_int, [_i64, _i64, _i64, C.POINTER(_sz)]),
@@ -184,6 +187,19 @@ def dspark_markov_propose(U, anchor, A, Bm, tokens, *, temperature: float = 0.0,
         _ptr(seeds), int(offset), int(topk), _ptr(tokens), _ptr(tok_logit), _ptr(lse),
         _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(ws), ws.numel(), _ptr(status),
         _stream(stream)))
+
+
+def dspark_markov_propose_noalloc(U, anchor, A, Bm, tokens, *, temperature: float = 0.0, seeds=None,
+                                  offset: int = 0, topk: int = 0, tok_logit=None, lse=None, topk_idx=None,
+                                  topk_prob=None, logits_out=None, status=None, stream=None) -> None:
+    """dspark_markov_propose with the library's static scratch as its workspace
+    (allocates nothing, here or in the library)."""
+    B, gamma, V = U.shape
+    r = A.shape[1]
+    _check(lib().dspark_markov_propose_noalloc(
+        _ptr(U), B, gamma, V, _ptr(anchor), _ptr(A), _ptr(Bm), _dtype(A), r, float(temperature),
+        _ptr(seeds), int(offset), int(topk), _ptr(tokens), _ptr(tok_logit), _ptr(lse),
+        _ptr(topk_idx), _ptr(topk_prob), _ptr(logits_out), _ptr(status), _stream(stream)))
 
 
 def dspark_confidence_survival(h, w_c, b_c: float, conf, survival, *, w_m=None, A=None,

@@ -214,7 +214,7 @@ dspark_status_t propose_impl(
     const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
     uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
     int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
-    int32_t* status, hipStream_t stream) {
+    const ScratchProvider* scratch, int32_t* status, hipStream_t stream) {
   if (!U || !anchor || !A || !Bm || !tokens)
     return fail(DSPARK_EINVAL, "%s: U, anchor, A, Bm and tokens must be non-NULL", fn);
   if (B <= 0 || gamma <= 0 || V <= 0 || r <= 0)
@@ -243,6 +243,14 @@ dspark_status_t propose_impl(
       return fail(DSPARK_EUNSUPPORTED, "%s: U, A, Bm, logits_out must be 16-byte aligned", fn);
   }
   const size_t need = markov_ws_bytes(B, gamma, V, topk) + head_table_bytes(head_kind, B, gamma, r, bf16);
+  if (scratch) {            // the library's own scratch: exactly the plain workspace, no transposed Bm
+    if (need > scratch->capacity)
+      return fail(DSPARK_EWORKSPACE, "%s: these sizes need %zu bytes of scratch; the library's static scratch "
+                  "holds %zu (use the entry point that takes a workspace)", fn, need, scratch->capacity);
+    const hipError_t e = scratch->acquire(stream, &ws);
+    if (e != hipSuccess) return hip_status(e, fn);
+    ws_bytes = need;
+  }
   if (!ws || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
 
@@ -324,7 +332,7 @@ extern "C" dspark_status_t dspark_markov_propose(
     int32_t* status, hipStream_t stream) {
   return propose_impl("dspark_markov_propose", kHeadLinear, nullptr, 0, nullptr, U, B, gamma, V, anchor, A, Bm,
                       wdt, r, temperature, seeds, offset, topk, tokens, tok_logit, lse, topk_idx, topk_prob,
-                      logits_out, ws, ws_bytes, status, stream);
+                      logits_out, ws, ws_bytes, nullptr, status, stream);
 }
 
 extern "C" dspark_status_t dspark_markov_propose_head_workspace(int32_t head, int64_t B, int64_t gamma, int64_t V,
@@ -367,7 +375,8 @@ extern "C" dspark_status_t dspark_markov_propose_head(
     if (H > kMaxHeadHidden) return fail(DSPARK_EUNSUPPORTED, "%s: H > %d", fn, kMaxHeadHidden);
   }
   return propose_impl(fn, head, h, H, W_g, U, B, gamma, V, anchor, A, Bm, wdt, r, temperature, seeds, offset, topk,
-                      tokens, tok_logit, lse, topk_idx, topk_prob, logits_out, ws, ws_bytes, status, stream);
+                      tokens, tok_logit, lse, topk_idx, topk_prob, logits_out, ws, ws_bytes, nullptr, status,
+                      stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -185,4 +185,26 @@ int overlap_split_chunks(int64_t rows, int64_t V);
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s);
 unsigned next_epoch();
 
+// Workspace supplied by the library instead of the caller (the no-allocation
+// propose entry point): `capacity` bytes at an address that `acquire` returns
+// for the current device, zero-filled (by a kernel enqueued on `s`) the first
+// time it is acquired on that device.
+struct ScratchProvider {
+  size_t capacity;
+  hipError_t (*acquire)(hipStream_t s, void** ptr);
+};
+
 }  // namespace dspark
+
+#include "dspark.h"
+
+// dspark_markov_propose and its variants (dspark_api.hip): every argument
+// check, then the chain.  With scratch != NULL, ws and ws_bytes are ignored
+// and the workspace is scratch's (calls with larger needs are rejected).
+dspark_status_t propose_impl(
+    const char* fn, int head_kind, const void* h, int64_t H, const void* Wg,
+    const float* U, int64_t B, int64_t gamma, int64_t V, const int32_t* anchor, const void* A,
+    const void* Bm, dspark_dtype_t wdt, int64_t r, float temperature, const uint64_t* seeds,
+    uint64_t offset, int32_t topk, int32_t* tokens, float* tok_logit, float* lse,
+    int32_t* topk_idx, float* topk_prob, float* logits_out, void* ws, size_t ws_bytes,
+    const dspark::ScratchProvider* scratch, int32_t* status, hipStream_t stream);

@@ -280,3 +280,22 @@ def test_device_status_word_host_check():
     with open(bd.HEADER) as f:
         assert "DSPARK_ETIMEOUT = 5" in f.read()
     assert bd.ETIMEOUT == 5
+
+
+def test_noalloc_validation(L):
+    """The no-allocation propose call checks its arguments like
+    dspark_markov_propose and rejects sizes beyond its static scratch before
+    any device work."""
+    f = L.dspark_markov_propose_noalloc
+    args = lambda **k: [k.get(n, d) for n, d in (
+        ("U", FAKE), ("B", 4), ("gamma", 7), ("V", 151936), ("anchor", FAKE), ("A", FAKE), ("Bm", FAKE),
+        ("dt", bd.BF16), ("r", 256), ("T", 0.0), ("seeds", None), ("off", 0), ("topk", 0), ("tok", FAKE),
+        ("tl", None), ("lse", None), ("ti", None), ("tp", None), ("lo", None), ("status", None), ("s", None))]
+    assert f(*args(U=None)) == bd.EINVAL
+    assert f(*args(T=1.0)) == bd.EINVAL                       # sampling without seeds
+    assert f(*args(status=FAKE + 2)) == bd.EINVAL
+    assert f(*args(gamma=17)) == bd.EUNSUPPORTED
+    assert f(*args(A=MISALIGNED)) == bd.EUNSUPPORTED
+    # B = 256 with top-16 needs 211 MiB of workspace; the scratch holds 64 MiB
+    assert f(*args(B=256, topk=16, ti=FAKE, tp=FAKE)) == bd.EWORKSPACE
+    assert "static scratch" in bd.last_error() and str(64 << 20) in bd.last_error()
