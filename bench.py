@@ -1,13 +1,22 @@
 """Benchmark of the DSpark draft-proposal hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic blocks:
-LM head -> sequential Markov proposal (7 positions, top-16 candidates, U~
-dump) -> confidence + prefix survival -> overlap / tau_prob against a teacher.
-Default workload: one request of the Qwen3-4B-shaped draft head (B=1, gamma=7,
-H=2560, V=151936, r=256, bf16 weights, greedy).
+LM head -> sequential Markov proposal (7 positions, top-16 candidates) ->
+confidence + prefix survival -> overlap / tau_prob against a teacher.
 
-Prints ONE JSON line.  Per-stage durations come from HIP events recorded on
-the stream the kernels run on, inside the timed region.
+Headline workload (the value of the JSON line): the Qwen3.8-Flash-Next-shaped
+high load, B=256 requests x gamma=7 (1,792 LM-head rows), H=2560,
+V=151936, r=256, bf16 weights, greedy, top-16 candidates, sparse overlap
+against a full-vocabulary teacher.  The same line carries the other
+workloads under "configs": one request (B=1, top-16, dense overlap over the
+U~ dump), continuous batching (B=64, Philox-Gumbel sampling at T=1, top-16,
+sparse overlap) and the offline teacher-forced eval (4,096 blocks = 28,672
+rows, sigma=1, 10% truncated blocks).  Each workload reports the mean over
+back-to-back steps, the median/p10/p90 of per-step times, and "cold" steps
+run right after a 512 MiB write that evicts the 256 MB MALL and the L2s.
+
+Prints ONE JSON line.  Durations come from HIP events recorded on the
+stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -24,13 +33,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 METRIC = "draft blocks/sec (γ=7, V=151936) + % HBM/MFMA roofline"
+HEADLINE = "c5_flash_next_b256"
 
 WORKLOADS = {
-    # name: (synth config, overrides, overlap mode)
-    "c2_qwen3_4b_b1": ("c2_qwen3_4b_b1", dict(topk=16), "dense"),
-    "c3_batch64_gumbel": ("c3_batch64_gumbel", dict(topk=16), "topk"),
-    "c5_flash_next_b256": ("c5_flash_next_b256", dict(), "topk"),
+    # name: (requests taken from the 256-request draw, overrides, overlap mode)
+    "c5_flash_next_b256": (256, dict(temperature=0.0, topk=16), "topk"),
+    "c3_batch64_gumbel": (64, dict(temperature=1.0, topk=16), "topk"),
+    "c2_qwen3_4b_b1": (1, dict(temperature=0.0, topk=16), "dense"),
 }
+C4_NAME = "c4_offline_eval"
 
 
 def stage_work(B, gamma, H, V, r, topk, overlap, wbytes=2):
@@ -86,7 +97,8 @@ def traffic_for(kernel, workload, launches_per_step):
 
 def cpu_baseline(inp, overlap, budget_s=10.0, max_reps=100000):
     """The fp64 oracle timed on this host on a bounded sample: repetitions of
-    the first block of the workload (the full path for one request)."""
+    the first block of the workload (the full path for one request: its 7 LM-head
+    rows, the chain with top-k, confidence, overlap and tau)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import dspark_oracle as o
@@ -302,12 +314,202 @@ def bench_heads(dev, stream, B=256, gamma=7, V=151936, r=256, H=2560, reps=5):
     return out
 
 
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def time_steps(run, stream, K, flush, cold_reps, lm_events=False):
+    """K back-to-back steps with an event at every step start (and, with
+    lm_events, one right after the LM-head kernel), then cold_reps steps each
+    right after a write of the flush buffer (not timed).  Returns the mean
+    step, the per-step distribution, the cold distribution and the mean
+    LM-head event window."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    ev_lm = [torch.cuda.Event(enable_timing=True) for _ in range(K)] if lm_events else None
+    t_wall = time.perf_counter()
+    for s in range(K):
+        ev[s].record(stream)
+        if lm_events:
+            run(lm_done=ev_lm[s])
+        else:
+            run()
+    ev[K].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(K)]
+    out = {"ms_mean": ev[0].elapsed_time(ev[K]) / K, "steps": percentiles(per), "wall_s": wall}
+    if lm_events:
+        out["lm_ms"] = sum(ev[s].elapsed_time(ev_lm[s]) for s in range(K)) / K
+    cold = []
+    for i in range(cold_reps):
+        flush.fill_(i + 1)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        run()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    out["cold"] = percentiles(cold) if cold else None
+    return out
+
+
+def roofline_lm(work, lm_ms, kernel, workload):
+    """The LM head's roofline: HBM-bound below the ridge (few rows), MFMA-bound above."""
+    intensity = work["lm_head"]["flops"] / work["lm_head"]["bytes"]
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        ach = work["lm_head"]["bytes"] / (lm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = work["lm_head"]["flops"] / (lm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = kernel
+    roof["traffic"] = traffic_for(kernel, workload, 1)
+    roof["algorithmic_bytes_per_launch"] = work["lm_head"]["bytes"]
+    roof["algorithmic_flops_per_launch"] = work["lm_head"]["flops"]
+    return roof
+
+
+def bench_propose(name, inp, overlap, weights, dev, stream, K, W, flush, cold_reps):
+    """One propose workload through DraftPath: timing, the LM head's roofline
+    and a stage breakdown (a separate pass with an event around every stage)."""
+    import torch
+    from semi_autoregressive_draft_amd.path import DraftPath
+
+    def to_dev(x):
+        return torch.from_numpy(x).to(dev)
+
+    def to_bf(x):
+        return torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
+
+    w_lm, A, Bm, w_c = weights
+    path = DraftPath(to_bf(inp.h), w_lm, A, Bm, to_dev(inp.anchor), w_c, inp.b_c, gamma=inp.gamma,
+                     temperature=inp.temperature,
+                     seeds=to_dev(inp.seeds) if inp.temperature > 0 else None, offset=inp.offset,
+                     topk=inp.topk, teacher=to_dev(inp.teacher), overlap=overlap)
+    for _ in range(W):
+        path.run(stream)
+    torch.cuda.synchronize()
+    path.check()
+    t = time_steps(lambda lm_done=None: path.run(stream, lm_done=lm_done), stream, K, flush, cold_reps,
+                   lm_events=True)
+    path.check()
+
+    stages = [("lm_head", path.lm_head), ("markov", path.propose), ("overlap", path.overlap_tau)]
+    D = min(K, 20)
+    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(D)]
+    for s in range(D):
+        evd[s][0].record(stream)
+        for i, (_, fn) in enumerate(stages):
+            fn(stream)
+            evd[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {n: sum(evd[s][i].elapsed_time(evd[s][i + 1]) for s in range(D)) / D
+                for i, (n, _) in enumerate(stages)}
+    stage_ms["lm_head"] = t["lm_ms"]
+    work = stage_work(inp.B, inp.gamma, inp.H, inp.V, inp.r, inp.topk, overlap)
+    M = inp.B * inp.gamma
+    kern = lm_head_kernel_name(inp.B, inp.gamma, inp.H)
+    info = {}
+    for n, ms in stage_ms.items():
+        gbs = work[n]["bytes"] / (ms * 1e-3) / 1e9
+        info[n] = {"ms": round(ms, 5), "GB/s": round(gbs, 1),
+                   "TFLOP/s": round(work[n]["flops"] / (ms * 1e-3) / 1e12, 2),
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    info["lm_head"]["note"] = "kernel: " + kern + (" (+ the confidence head in its first workgroup)"
+                                                   if kern == "lm_head_skinny_bf16" else "")
+    if path.markov_plan > 0:
+        # The resident chain keeps Bm on chip across the 7 positions: its time is
+        # seven grid-wide exchanges, not a stream of Bm.  The byte count above counts
+        # Bm once per position (what a streaming kernel would move); the measured
+        # HBM bytes come from the committed rocprofv3 counter summary.
+        mk = info["markov"]
+        mk["bound"] = "latency (resident chain: Bm held on chip, 7 grid-wide exchanges)"
+        mk["effective_GBps_if_streamed"] = mk.pop("GB/s")
+        mk.pop("hbm_frac")
+        tr = traffic_for("markov_resident", name, 1)
+        mk["measured_hbm_bytes"] = tr
+        mk["measured_GBps"] = round(tr / (mk["ms"] * 1e-3) / 1e9, 1) if tr else None
+    else:
+        info["markov"]["bound"] = "hbm (Bm and U_j streamed once per position)"
+    roof = roofline_lm(work, t["lm_ms"], kern, name)
+    out = {
+        "B": inp.B, "gamma": inp.gamma, "H": inp.H, "V": inp.V, "r": inp.r, "topk": inp.topk,
+        "sampling": "gumbel T=%g" % inp.temperature if inp.temperature > 0 else "greedy",
+        "overlap": overlap,
+        "blocks_per_s": round(inp.B / (t["ms_mean"] * 1e-3), 2),
+        "ms_per_step": round(t["ms_mean"], 5),
+        "ms_per_step_dist": t["steps"],
+        "blocks_per_s_median": round(inp.B / (t["steps"]["median"] * 1e-3), 2),
+        "cold_ms_per_step": t["cold"],
+        "roofline": roof, "stages": info,
+        "stages_note": "lm_head from the timed region (event right after its kernel); the others from a "
+                       "separate pass with an event around every stage",
+        "wall_s_timed": round(t["wall_s"], 4),
+    }
+    del path
+    return out
+
+
+def bench_offline_eval(dev, stream, K, flush, cold_reps, sigma=1.0):
+    """The offline teacher-forced eval at full size: 4,096 blocks (28,672 rows
+    x V) of draft logits and teacher = draft + sigma N(0,1), 10% of the blocks
+    truncated, dense overlap and tau in one call."""
+    import torch
+    import synth
+    from semi_autoregressive_draft_amd import binding as bd
+    cfg = synth.CONFIGS[C4_NAME]
+    N, V, g = cfg["N"], cfg["V"], synth.GAMMA
+    teacher, draft = synth.device_overlap_inputs(N, V, sigma, dev, seed=0)
+    valid = torch.from_numpy(synth.validity(N, seed=0, trunc_frac=cfg["trunc_frac"])).to(dev)
+    alpha = torch.empty((N, g), dtype=torch.float32, device=dev)
+    tau = torch.empty((N,), dtype=torch.float32, device=dev)
+    acc = torch.empty((g,), dtype=torch.float64, device=dev)
+    mean = torch.empty((1,), dtype=torch.float64, device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
+    ws = torch.zeros(bd.dspark_overlap_tau_workspace(N, g, V), dtype=torch.uint8, device=dev)
+
+    def run(lm_done=None):
+        bd.dspark_overlap_tau(teacher, alpha, tau, draft=draft, valid=valid, accept_rate_at=acc,
+                              tau_mean=mean, ws=ws, status=status, stream=stream)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    t = time_steps(run, stream, K, flush, cold_reps)
+    bd.check_device_status(status, "overlap")
+    byt = 8.0 * N * g * V
+    ach = byt / (t["ms_mean"] * 1e-3) / 1e9
+    out = {"N_blocks": N, "rows": N * g, "V": V, "sigma": sigma, "trunc_frac": cfg["trunc_frac"],
+           "blocks_per_s": round(N / (t["ms_mean"] * 1e-3), 2), "ms_per_call": round(t["ms_mean"], 5),
+           "ms_per_call_dist": t["steps"], "blocks_per_s_median": round(N / (t["steps"]["median"] * 1e-3), 2),
+           "cold_ms_per_call": t["cold"],
+           "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "overlap_rows",
+                        "algorithmic_bytes_per_launch": byt,
+                        "traffic": traffic_for("overlap_rows", C4_NAME, 1)},
+           "tau_mean": round(float(mean.item()), 5)}
+    del teacher, draft, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2_qwen3_4b_b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS) + [C4_NAME],
+                    help="the workload of the headline value (default: the 256-request high load)")
+    ap.add_argument("--only", action="store_true",
+                    help="run the chosen workload alone (no other configs, no next rows): for profiling")
+    ap.add_argument("--cold-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch copy_) 5 times; its "
@@ -320,7 +522,6 @@ def main():
 
     import torch
     import synth
-    from semi_autoregressive_draft_amd.path import DraftPath
 
     if args.calibrate_copy:
         n = 1 << 30
@@ -332,115 +533,68 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
         return
 
-    cfg_name, over, overlap = WORKLOADS[args.workload]
-    cfg = dict(synth.CONFIGS[cfg_name])
-    cfg.update(over)
-    inp = synth.propose_inputs(**cfg)
     dev = torch.device("cuda", 0)
-
-    def to_dev(x, wd="f32"):
-        if wd == "bf16":
-            return torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(x).to(dev)
-
-    wd = inp.wdtype
-    path = DraftPath(to_dev(inp.h, wd), to_dev(inp.w_lm, wd), to_dev(inp.A, wd), to_dev(inp.Bm, wd),
-                     to_dev(inp.anchor), to_dev(inp.w_c, wd), inp.b_c, gamma=inp.gamma,
-                     temperature=inp.temperature,
-                     seeds=to_dev(inp.seeds) if inp.temperature > 0 else None, offset=inp.offset,
-                     topk=inp.topk, teacher=to_dev(inp.teacher), overlap=overlap)
     stream = torch.cuda.current_stream()
-    # the hidden-only confidence head runs inside the LM-head call (path.lm_head)
-    stages = [("lm_head", path.lm_head), ("markov", path.propose)]
-    if path.w_m is not None:
-        stages.append(("confidence", path.confidence))
-    stages.append(("overlap", path.overlap_tau))
+    K, W = args.steps, args.warmup
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)   # evicts the 256 MB MALL
+    results = {}
+    big = None
+    if args.workload != C4_NAME or not args.only:
+        # one draw of the 256-request workload; the smaller workloads are its leading requests
+        big = synth.propose_inputs(**synth.CONFIGS[HEADLINE])
 
-    for _ in range(args.warmup):
-        path.run()
-    torch.cuda.synchronize()
+        def to_bf(x):
+            return torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
 
-    # Timed region: one event at each step start and one after the LM-head
-    # launch (its duration gives the roofline figure); every event record
-    # costs a few microseconds of GPU time, so the stages are not bracketed here.
-    K = args.steps
-    ev_step = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    ev_lm = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    t_wall = time.perf_counter()
-    for s in range(K):
-        ev_step[s].record(stream)
-        path.run(stream, lm_done=ev_lm[s])
-    ev_step[K].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_per_step = ev_step[0].elapsed_time(ev_step[K]) / K
-    lm_ms_live = sum(ev_step[s].elapsed_time(ev_lm[s]) for s in range(K)) / K
-    blocks_per_s = inp.B / (ms_per_step / 1e3)
+        weights = (to_bf(big.w_lm), to_bf(big.A), to_bf(big.Bm), to_bf(big.w_c))
+        names = [args.workload] if args.only else [args.workload] + [n for n in WORKLOADS if n != args.workload]
+        for n in names:
+            if n not in WORKLOADS:
+                continue
+            B, over, overlap = WORKLOADS[n]
+            inp = synth.leading_requests(big, B, **over)
+            print(f"bench: {n}", file=sys.stderr, flush=True)
+            results[n] = bench_propose(n, inp, overlap, weights, dev, stream, K, W, flush, args.cold_reps)
+        del weights
+        torch.cuda.empty_cache()
+    if args.workload == C4_NAME or not args.only:
+        print(f"bench: {C4_NAME}", file=sys.stderr, flush=True)
+        results[C4_NAME] = bench_offline_eval(dev, stream, K, flush, min(args.cold_reps, 3))
 
-    # Stage breakdown (diagnostic, after the timed region): the same steps with
-    # an event around every stage.
-    D = min(K, 20)
-    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(D)]
-    for s in range(D):
-        evd[s][0].record(stream)
-        for i, (_, fn) in enumerate(stages):
-            fn()
-            evd[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    stage_ms = {name: sum(evd[s][i].elapsed_time(evd[s][i + 1]) for s in range(D)) / D
-                for i, (name, _) in enumerate(stages)}
-    stage_ms["lm_head"] = lm_ms_live
-
-    work = stage_work(inp.B, inp.gamma, inp.H, inp.V, inp.r, inp.topk, overlap)
-    dom = max(stage_ms, key=stage_ms.get)
-    M = inp.B * inp.gamma
-    stage_info = {}
-    for name, ms in stage_ms.items():
-        gbs = work[name]["bytes"] / (ms * 1e-3) / 1e9
-        tfl = work[name]["flops"] / (ms * 1e-3) / 1e12
-        stage_info[name] = {"ms": round(ms, 5), "GB/s": round(gbs, 1), "TFLOP/s": round(tfl, 2),
-                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    # the LM head runs as one kernel launch; its bound is HBM at small M and MFMA at large M
-    lm_ms = stage_ms["lm_head"]
-    lm_kernel = lm_head_kernel_name(inp.B, inp.gamma, inp.H)
-    lm_intensity = work["lm_head"]["flops"] / work["lm_head"]["bytes"]
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if lm_intensity < ridge:
-        ach = work["lm_head"]["bytes"] / (lm_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
-    else:
-        ach = work["lm_head"]["flops"] / (lm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["kernel"] = lm_kernel
-    roof["traffic"] = traffic_for(lm_kernel, args.workload, 1)
-    roof["algorithmic_bytes_per_launch"] = work["lm_head"]["bytes"]
-
+    head = results[args.workload]
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, overlap)
-    sched = bench_prefix_schedule(dev, stream, with_oracle=not args.no_cpu_baseline)
-    tfl = bench_teacher_forced_loss(dev, stream)
-    ver = bench_verify(dev, stream)
-    heads = bench_heads(dev, stream)
+    if not args.no_cpu_baseline and args.workload in WORKLOADS:
+        B, over, overlap = WORKLOADS[args.workload]
+        cpu = cpu_baseline(synth.leading_requests(big, B, **over), overlap, budget_s=15.0)
+    next_rows = None
+    if not args.only:
+        print("bench: next rows", file=sys.stderr, flush=True)
+        next_rows = {"prefix_schedule": bench_prefix_schedule(dev, stream, with_oracle=not args.no_cpu_baseline),
+                     "teacher_forced_loss": bench_teacher_forced_loss(dev, stream),
+                     "verify": bench_verify(dev, stream), "heads": bench_heads(dev, stream)}
 
+    if args.workload == C4_NAME:
+        cfg = {"workload": C4_NAME, "N_blocks": head["N_blocks"], "rows": head["rows"], "V": head["V"],
+               "sigma": head["sigma"], "parallelism": "single GPU"}
+        value, ms = head["blocks_per_s"], head["ms_per_call"]
+    else:
+        cfg = {"workload": args.workload, **{k: head[k] for k in ("B", "gamma", "H", "V", "r", "topk",
+                                                                  "sampling", "overlap")},
+               "parallelism": "single GPU"}
+        value, ms = head["blocks_per_s"], head["ms_per_step"]
     out = {
-        "metric": METRIC, "value": round(blocks_per_s, 2), "unit": "blocks/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": value, "unit": "blocks/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) hidden states and teacher logits)",
-        "config": {"workload": args.workload, "B": inp.B, "gamma": inp.gamma, "H": inp.H,
-                   "V": inp.V, "r": inp.r, "topk": inp.topk,
-                   "sampling": "gumbel T=%g" % inp.temperature if inp.temperature > 0 else "greedy",
-                   "overlap": overlap, "parallelism": "single GPU"},
-        "roofline": roof,
-        "dominant_stage": dom,
-        "stages": stage_info,
-        "stages_note": "lm_head from the timed region; the others from a separate pass with an event around every stage",
-        "wall_s_timed": round(wall, 4),
+        "config": cfg,
+        "roofline": head["roofline"],
+        "ms_per_step_dist": head.get("ms_per_step_dist", head.get("ms_per_call_dist")),
+        "cold_ms_per_step": head.get("cold_ms_per_step", head.get("cold_ms_per_call")),
+        "stages": head.get("stages"),
         "cpu_baseline": cpu,
-        "next_rows": {"prefix_schedule": sched, "teacher_forced_loss": tfl, "verify": ver, "heads": heads},
+        "configs": {n: r for n, r in results.items() if n != args.workload},
+        "next_rows": next_rows,
     }
     print(json.dumps(out), flush=True)
 

@@ -49,6 +49,8 @@ class DraftPath:
         ws = (bd.dspark_markov_propose_workspace_bmt(bd.HEAD_LINEAR, B, gamma, V, A.shape[1], bd._dtype(A), topk)
               if topk else bd.dspark_markov_propose_workspace(B, gamma, V, topk))
         self.ws_markov = torch.zeros(ws, dtype=torch.uint8, device=dev)
+        # workgroups of the resident chain for these sizes (0: one step kernel per position)
+        self.markov_plan = bd.dspark_markov_propose_plan(B, V, A.shape[1], bd._dtype(A))
         # device status words of the propose and overlap calls (see check())
         self.status = torch.zeros((2,), dtype=torch.int32, device=dev)
         self.conf = torch.empty((B, gamma), **f32)
@@ -98,13 +100,22 @@ class DraftPath:
 
     def run(self, stream=None, lm_done=None):
         """One pass; lm_done (optional event) is recorded right after the
-        LM-head launch."""
+        LM-head kernel (after the fused LM-head + confidence launch at small
+        batch)."""
         main = stream if stream is not None else torch.cuda.current_stream()
-        self.lm_head(main)
-        if lm_done is not None:
-            lm_done.record(main)
+        M = self.B * self.gamma
+        if self.w_m is None and M <= 16 and self.h.dtype == torch.bfloat16:
+            self.lm_head(main)               # one launch: S1 and the hidden-only S5
+            if lm_done is not None:
+                lm_done.record(main)
+        else:                                # the same two launches dspark_lm_head_confidence makes
+            bd.dspark_lm_head(self.h, self.w_lm, self.U.view(-1, self.V), stream=main)
+            if lm_done is not None:
+                lm_done.record(main)
+            if self.w_m is None:
+                self.confidence(main)
         self.propose(main)
-        if self.w_m is not None:             # else computed with the LM head
+        if self.w_m is not None:             # the Markov term needs the drafted tokens
             self.confidence(main)
         if self.overlap:
             self.overlap_tau(main)

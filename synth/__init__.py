@@ -102,6 +102,19 @@ def propose_inputs(B: int, H: int, V: int, r: int, wdtype: str, *, gamma: int = 
                          w_m, t, float(temperature), seeds, int(offset), int(topk))
 
 
+def leading_requests(inp: ProposeInputs, B: int, **overrides) -> ProposeInputs:
+    """The first B requests of a drawn workload.  Every per-request tensor is
+    drawn as one sequential stream per tensor, so these are the arrays that
+    ``propose_inputs`` draws for B requests with the same seed; the weights
+    are shared, not copied.  ``overrides`` replace scalar fields
+    (temperature, topk, offset)."""
+    g = inp.gamma
+    out = dataclasses.replace(inp, B=B, h=inp.h[:B * g], anchor=inp.anchor[:B],
+                              teacher=None if inp.teacher is None else inp.teacher[:B],
+                              seeds=inp.seeds[:B])
+    return dataclasses.replace(out, **overrides)
+
+
 def base_logits(B: int, V: int, *, gamma: int = GAMMA, seed: int = 0, std: float = 1.0) -> np.ndarray:
     """Synthetic LM-head output U [B, gamma, V] float32, for testing the chain alone."""
     return normal((B, gamma, V), std, seed, TID_U, "f32")

@@ -68,3 +68,17 @@ def test_streams_differ_by_request_position_and_offset():
     assert not np.array_equal(a, o.gumbel(1, 0, 1, 64))
     assert not np.array_equal(a, o.gumbel(1, 1, 0, 64))
     assert np.array_equal(a, o.gumbel(1, 0, 0, 64))
+
+
+def test_leading_requests_equal_a_fresh_draw():
+    """The benchmark takes its one- and 64-request workloads as the leading
+    requests of the 256-request draw; each per-tensor stream is sequential,
+    so they equal fresh draws of the smaller workloads."""
+    import synth
+    big = synth.propose_inputs(B=9, H=64, V=520, r=32, wdtype="bf16", topk=4)
+    for B in (1, 4):
+        small = synth.propose_inputs(B=B, H=64, V=520, r=32, wdtype="bf16", temperature=1.0, topk=0)
+        cut = synth.leading_requests(big, B, temperature=1.0, topk=0)
+        for name in ("h", "w_lm", "A", "Bm", "anchor", "w_c", "teacher", "seeds"):
+            assert np.array_equal(getattr(cut, name), getattr(small, name)), name
+        assert (cut.B, cut.temperature, cut.topk) == (B, 1.0, 0)
