@@ -57,6 +57,7 @@ __device__ __forceinline__ float uniform_from_word(uint32_t w) {
 }
 
 constexpr float kLn2f = 0.693147180559945309f;
+constexpr float kLog2e = 1.44269504088896341f;   // 1 / ln 2
 
 // -ln u for u on that grid, from the hardware base-2 logarithm (v_log_f32).
 // Its result keeps a relative error of about one ulp even next to u = 1, where

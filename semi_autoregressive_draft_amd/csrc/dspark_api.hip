@@ -301,7 +301,7 @@ dspark_status_t propose_impl(
   if (!resident && topk > 0 && bf16 && ws_bytes >= need + bmt && markov_bmt_pays(B, gamma, V, r, topk))
     a.BmT = static_cast<char*>(ws) + need;
   a.Mrow = mtab;
-  a.tile_cols = resident ? 64 : markov_tile_cols(bf16, a.sample, a.B, a.r, a.V);
+  a.tile_cols = resident ? 64 : markov_tile_cols(bf16, a.sample, a.B, a.gamma, a.r, a.V);
   a.resident = resident;
   a.nlist = nwg;
   if (topk > 0) {

@@ -86,7 +86,7 @@ struct StepArgs {
 
 size_t markov_partials(int64_t V);
 size_t markov_segments(int64_t V);
-int markov_tile_cols(bool bf16, bool sample, int B, int r, int V);
+int markov_tile_cols(bool bf16, bool sample, int B, int gamma, int r, int V);
 bool markov_resident_plan(int B, int V, int r, int max_wg, int* nwg, size_t* lds);
 hipError_t launch_markov_resident(StepArgs a, unsigned* sync, int nwg, size_t lds, hipStream_t s);
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s);

@@ -337,10 +337,15 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
 //    (DPP) run once per request per workgroup; the argmax travels as a 64-bit
 //    order key (best_key).  One partial per (request, workgroup range).
 constexpr int kWideCols = 64;
+// cache-policy operand of a buffer store: the non-temporal hint (written once,
+// not read back by this kernel)
+constexpr int kBufferNonTemporal = 2;
 
 // LDS of the wide kernel: two B-operand buffers of nch chunks, then (when
 // sampling) the seeds of up to 8 x 16 requests
-__host__ __device__ constexpr size_t wide_ops_bytes(int nch) { return static_cast<size_t>(nch) * 2 * 4 * kWave * 16; }
+// (each buffer has one spare chunk slot: waves with no chunk of their own store
+// there, so the store needs no branch)
+__host__ __device__ constexpr size_t wide_ops_bytes(int nch) { return static_cast<size_t>(nch + 1) * 2 * 4 * kWave * 16; }
 constexpr size_t kWideSeedBytes = 8 * 16 * 8;
 
 // 16-lane maximum of 64-bit keys
@@ -366,60 +371,94 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// A buffer resource over [base, base + bytes) (bytes < 2^31, which the
+// launcher checks): loads past it read 0 and stores past it are dropped.  The
+// wide kernel addresses every array through such resources with a per-lane
+// 32-bit offset that stays fixed across tiles plus the tile's offset in a
+// scalar register, so a tile's loads and stores cost no vector address
+// arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+constexpr uint32_t kDropOffset = 0x80000000u;   // past every resource: the access is dropped
+// Stores of more than 8 bytes take their whole offset in the vector register
+// and a constant 0 as scalar offset: the compiler then keeps a VALU write of
+// the store's data registers one wait state behind the store.  With the tile
+// offset in a scalar register it inserted none, and on gfx950 the register
+// overwritten right after a 16-byte store reached memory with its new value
+// in some lanes (block logits of one column in four read -inf).
+
 // STATS = false: teacher-forced block logits only (every row's previous token
 // given; each tile's U~ is stored to logits_out and nothing else is kept).
 template <int NCH, int CPW, bool SAMPLE, bool STATS = true>
 __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
   extern __shared__ __align__(16) unsigned char wide_lds[];
-  u32x4* const ops = reinterpret_cast<u32x4*>(wide_lds);   // [2][NCH * 4][64] B operands
+  u32x4* const ops = reinterpret_cast<u32x4*>(wide_lds);   // [2][NCH + 1][4][64] B operands
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int g = lane >> 4, n = lane & 15;
   const int req0 = (blockIdx.y * nw + w) * 16;
-  const size_t V = static_cast<size_t>(a.V);
-  const uint16_t* A = static_cast<const uint16_t*>(a.A);
-  const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm);
   const int tb = blockIdx.x * tpw;                                   // first tile
   const int nt = min(tpw, (a.V + kWideCols - 1) / kWideCols - tb);
   if (nt <= 0) return;                     // padding of the grid (whole workgroup)
   const int last = nt - 1;
+  const uint32_t V = static_cast<uint32_t>(a.V);
+  const size_t rows = static_cast<size_t>(a.B) * a.gamma;
 
-  // the lane's first column in tile t; loads use it clamped to V - 4 (V % 8 == 0)
-  auto col_of = [&](int t) { return (tb + t) * kWideCols + 4 * n; };
-  auto lcol = [&](int t) { return static_cast<size_t>(min(col_of(t), a.V - 4)); };
-  // U_j rows of the lane's requests 4g + ii (clamped to a valid request)
-  const float* urow[4];
+  // Requests past the batch (a ragged last group) are computed as request
+  // B - 1: the same A row and U row, hence the same values, and their stores
+  // repeat that request's; only the final partials skip them.
+  const __amdgpu_buffer_rsrc_t u_rsrc = buf_rsrc(a.U, rows * V * 4);
+  const __amdgpu_buffer_rsrc_t bm_rsrc = buf_rsrc(a.Bm, static_cast<size_t>(a.r) * V * 2);
+  const __amdgpu_buffer_rsrc_t out_rsrc =
+      a.logits_out ? buf_rsrc(a.logits_out, rows * V * 4) : buf_rsrc(a.U, 0);
+  const __amdgpu_buffer_rsrc_t seg_rsrc =
+      a.segmax ? buf_rsrc(a.segmax, rows * a.S * 4) : buf_rsrc(a.U, 0);
+  uint32_t uoff[4], soff[4];     // request 4g + ii: U / U~ row and segment-maxima row at tile 0
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
-    const int b = min(req0 + 4 * g + ii, a.B - 1);
-    urow[ii] = a.U + (static_cast<size_t>(b) * a.gamma + a.j) * V;
+    const uint32_t row = static_cast<uint32_t>(min(req0 + 4 * g + ii, a.B - 1)) * a.gamma + a.j;
+    uoff[ii] = (row * V + tb * kWideCols + 4 * n) * 4;
+    soff[ii] = (row * a.S + tb * (kWideCols / kSeg) + (n >> 1)) * 4;
   }
-  auto load_u = [&](int t, f32x4 (&u)[4]) {
-    const size_t c = lcol(t);
+  // Bm rows of this wave's chunks (chunks w, w + nw, ...; NCH <= CPW * nw)
+  uint32_t boff[CPW][8];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) u[ii] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(urow[ii] + c));
+  for (int s = 0; s < CPW; ++s) {
+    const int q = min(w + s * nw, NCH - 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) boff[s][i] = ((32 * q + 8 * g + i) * V + tb * kWideCols + 4 * n) * 2;
+  }
+  // look-aheads past the range reload the last tile (an L2 hit)
+  auto load_u = [&](int t, f32x4 (&u)[4]) __attribute__((always_inline)) {
+    const int tof = min(t, last) * kWideCols * 4;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      u[ii] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(u_rsrc, static_cast<int>(uoff[ii]), tof,
+                                                                              kBufferNonTemporal));
   };
-  // Bm rows of this wave's chunks of tile t (chunks w, w + nw, ...; NCH <= CPW * nw)
-  auto load_bm = [&](int t, u32x2 (&raw)[CPW][8]) {
-    const size_t c = lcol(t);
+  auto load_bm = [&](int t, u32x2 (&raw)[CPW][8]) __attribute__((always_inline)) {
+    const int tof = min(t, last) * kWideCols * 2;
 #pragma unroll
-    for (int s = 0; s < CPW; ++s) {
-      const int q = min(w + s * nw, NCH - 1);
+    for (int s = 0; s < CPW; ++s)
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        raw[s][i] = *reinterpret_cast<const u32x2*>(Bm + static_cast<size_t>(32 * q + 8 * g + i) * V + c);
-    }
+        raw[s][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(bm_rsrc, static_cast<int>(boff[s][i]),
+                                                                                 tof, 0));
   };
-  auto store_bm = [&](int buf, const u32x2 (&raw)[CPW][8]) {
-    u32x4* const o = ops + buf * NCH * 4 * kWave;
+  auto store_bm = [&](int buf, u32x2 (&raw)[CPW][8]) __attribute__((always_inline)) {
+    u32x4* const o = ops + buf * (NCH + 1) * 4 * kWave;
 #pragma unroll
     for (int s = 0; s < CPW; ++s) {
-      const int q = w + s * nw;
-      if (q < NCH) {
-        u32x4 op[4];
-        transpose_rows4(raw[s], op);
+      const int q = min(w + s * nw, NCH);              // NCH: the spare slot
+      // pin the byte permutes here: as plain register arithmetic they could be
+      // hoisted over the preceding barrier to right after the rows' loads,
+      // which would then be waited for a whole tile early
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[(q * 4 + c) * kWave + lane] = op[c];
-      }
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(raw[s][i]));
+      u32x4 op[4];
+      transpose_rows4(raw[s], op);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[(q * 4 + c) * kWave + lane] = op[c];
     }
   };
 
@@ -440,15 +479,18 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
     if (lane < 16) seeds_s[w * 16 + lane] = a.seeds[min(req0 + lane, a.B - 1)];
   }
 
-  // lane-local states per request 4g + ii
+  // Lane-local states per request 4g + ii over the lane's columns: the
+  // running maximum ml of U~ and the sum sl of exp(U~ - ml) (rescaled when ml
+  // moves); the best score bs with its column bc and U~ there (greedy: the
+  // best score is ml itself and its U~ too).
   float ml[4], sl[4], bs[4], bx[4];
   int bc[4];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) { ml[ii] = kNegInf; sl[ii] = 0.f; bs[ii] = kNegInf; bx[ii] = 0.f; bc[ii] = 0x7fffffff; }
 
-  auto tile = [&](int t, int buf, const f32x4 (&u)[4]) {
-    const u32x4* const o = ops + buf * NCH * 4 * kWave;
-    f32x4 acc[4];
+  // The bias of one tile: NCH x 4 MFMAs from B-operand buffer `buf`.
+  auto mma = [&](int buf, f32x4 (&acc)[4]) __attribute__((always_inline)) {
+    const u32x4* const o = ops + buf * (NCH + 1) * 4 * kWave;
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -457,108 +499,153 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
       for (int c = 0; c < 4; ++c)
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[q]), as_bf16x8(o[(q * 4 + c) * kWave + lane]),
                                                          acc[c], 0, 0, 0);
-    const int col = col_of(t);
-    const bool cok = col < a.V;
-    if constexpr (!STATS) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int b = req0 + 4 * g + ii;
-        if (b < a.B && cok)
-          __builtin_nontemporal_store(
-              f32x4{acc[0][ii] + u[ii][0], acc[1][ii] + u[ii][1], acc[2][ii] + u[ii][2], acc[3][ii] + u[ii][3]},
-              reinterpret_cast<f32x4*>(a.logits_out + (static_cast<size_t>(b) * a.gamma + a.j) * V + col));
-      }
-      return;
-    }
+  };
+  // The epilogue of tile t from its bias `acc` and U_j values `u`; branch-free
+  // (the whole tile pair is one basic block for the scheduler).
+  // MASK: the range's last tiles, where columns may lie past V (the last tile
+  // of the vocabulary) or past the range (the padding tile t == nt of an odd
+  // range): those carry -inf and store nothing.  Every other tile is whole.
+  auto epi = [&](auto mask_tag, int t, const f32x4 (&acc)[4], const f32x4 (&u)[4]) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int col = (tb + t) * kWideCols + 4 * n;
+    const bool cok = !MASK || (t < nt && col < a.V);
+    const int tofx = t * kWideCols * 4, tofs = t * (kWideCols / kSeg) * 4;
+    float xs[4][4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const int b = req0 + 4 * g + ii;
-      const bool live = b < a.B && cok;
-      const size_t row = static_cast<size_t>(b) * a.gamma + a.j;
-      float x[4];
+      float* const x = xs[ii];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) x[c] = live ? acc[c][ii] + u[ii][c] : kNegInf;
-      if (live && a.logits_out)
-        __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(a.logits_out + row * V + col));
+      for (int c = 0; c < 4; ++c) x[c] = acc[c][ii] + u[ii][c];
+      if constexpr (MASK) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = cok ? x[c] : kNegInf;
+      }
+      if constexpr (!STATS) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{x[0], x[1], x[2], x[3]}), out_rsrc,
+                                               static_cast<int>(cok ? uoff[ii] + tofx : kDropOffset), 0,
+                                               kBufferNonTemporal);
+        continue;
+      }
       const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (a.segmax) {
-        const float m8 = fmaxf(m4, dpp_f<kDppXor1>(m4));   // lanes 2s, 2s+1: one 8-column segment
-        if (live && (n & 1) == 0) a.segmax[row * a.S + col / kSeg] = m8;
-      }
-      if (live) {
-        const float mn = fmaxf(ml[ii], m4);
-        sl[ii] = sl[ii] * __expf(ml[ii] - mn) +
-                 ((__expf(x[0] - mn) + __expf(x[1] - mn)) + (__expf(x[2] - mn) + __expf(x[3] - mn)));
-        ml[ii] = mn;
-        float score[4];
-        if constexpr (SAMPLE) {
-          const uint64_t sd = seeds_s[w * 16 + 4 * g + ii];
-          const Philox4 r = philox4x32_10(col >> 2, a.j, a.off_lo, a.off_hi, static_cast<uint32_t>(sd),
-                                          static_cast<uint32_t>(sd >> 32));
-          const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+      // lanes 2s and 2s + 1 hold one 8-column segment; both store its maximum
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaxf(m4, dpp_f<kDppXor1>(m4))), seg_rsrc,
+                                            static_cast<int>(cok ? soff[ii] : kDropOffset), tofs, 0);
+      if constexpr (SAMPLE) {
+        const uint64_t sd = seeds_s[w * 16 + 4 * g + ii];
+        const Philox4 r = philox4x32_10(col >> 2, a.j, a.off_lo, a.off_hi, static_cast<uint32_t>(sd),
+                                        static_cast<uint32_t>(sd >> 32));
+        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-          for (int c = 0; c < 4; ++c) score[c] = x[c] * a.inv_temp + gumbel_from_word(wd[c]);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) score[c] = x[c];
+        for (int c = 0; c < 4; ++c) {
+          const float sc = x[c] * a.inv_temp + gumbel_from_word(wd[c]);
+          const bool up = sc > bs[ii];
+          bs[ii] = up ? sc : bs[ii];
+          bc[ii] = up ? col + c : bc[ii];
+          bx[ii] = up ? x[c] : bx[ii];
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (score[c] > bs[ii]) { bs[ii] = score[c]; bc[ii] = col + c; bx[ii] = x[c]; }
+      } else {
+        // greedy: the score is U~ itself, so the best so far is the running
+        // maximum; it moves only where this tile's maximum exceeds it
+        // (strictly: the lowest column keeps a tie), to the first column
+        // holding that maximum
+        const bool up = m4 > ml[ii];
+        int c4 = 3;                                     // selects, not branches
+        c4 = x[2] == m4 ? 2 : c4;
+        c4 = x[1] == m4 ? 1 : c4;
+        c4 = x[0] == m4 ? 0 : c4;
+        bc[ii] = up ? col + c4 : bc[ii];
       }
+      // sum of exp in base 2: one fused multiply-add and one exp2 per element
+      const float mn = fmaxf(ml[ii], m4);
+      const float mref = mn == kNegInf ? 0.f : mn;     // no column yet: keep s = 0
+      const float nm2 = -mref * kLog2e;
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(x[0], kLog2e, nm2)), e1 = __builtin_amdgcn_exp2f(fmaf(x[1], kLog2e, nm2));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(x[2], kLog2e, nm2)), e3 = __builtin_amdgcn_exp2f(fmaf(x[3], kLog2e, nm2));
+      sl[ii] = fmaf(sl[ii], __builtin_amdgcn_exp2f(fmaf(ml[ii], kLog2e, nm2)), (e0 + e1) + (e2 + e3));
+      ml[ii] = mn;
+    }
+    if constexpr (STATS) {
+      // the U~ dump (a resource of no records when there is none)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{xs[ii][0], xs[ii][1], xs[ii][2], xs[ii][3]}),
+                                               out_rsrc, static_cast<int>(cok ? uoff[ii] + tofx : kDropOffset), 0,
+                                               kBufferNonTemporal);
     }
   };
+  using Whole = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
 
-  // tile t computes from buffer t & 1 and U registers u0 (t even) or u1 (t
-  // odd); look-aheads past the range reload the last tile (an L2 hit).  With
-  // one chunk per wave the Bm rows have two register sets (ra for even
-  // tiles, rb for odd ones) and are fetched two tiles ahead; with two chunks
-  // one set, a tile ahead.
+  // Tile t's bias comes from buffer t & 1.  Each wave issues the MFMAs of
+  // tile t + 1 before the epilogue of tile t, so the matrix unit works on
+  // the next tile while the vector unit runs this one's softmax statistics
+  // (the MFMAs' results are read one step later).  U registers u0 / u1 hold
+  // tiles t / t + 1 and are refilled two tiles ahead; the bias of a tile past
+  // the range is computed but never used.  With one chunk per wave the Bm
+  // rows have two register sets (ra: even tiles, rb: odd ones), fetched two
+  // tiles before their LDS store; with two chunks one set, a tile before.
+  // The loop runs whole tiles; the last pair (the range's last tile, which
+  // may be partial, and the padding tile of an odd range) runs masked.
   f32x4 u0[4], u1[4];
+  f32x4 acc0[4], acc1[4];
   u32x2 ra[CPW][8];
   int t = 0;
   if constexpr (CPW == 1) {
     u32x2 rb[CPW][8];
+    auto pair = [&](auto mask_tag) __attribute__((always_inline)) {
+      mma(1, acc1);                                     // tile t + 1
+      epi(mask_tag, t, acc0, u0);
+      load_u(t + 2, u0);
+      store_bm(0, ra);                                  // tile t + 2
+      load_bm(t + 4, ra);
+      lds_barrier();
+      mma(0, acc0);                                     // tile t + 2
+      epi(mask_tag, t + 1, acc1, u1);
+      load_u(t + 3, u1);
+      store_bm(1, rb);                                  // tile t + 3
+      load_bm(t + 5, rb);
+      lds_barrier();
+    };
     load_bm(0, ra);
     load_u(0, u0);
-    load_bm(min(1, last), rb);
-    load_u(min(1, last), u1);
-    store_bm(0, ra);
-    load_bm(min(2, last), ra);
+    load_bm(1, rb);
+    load_u(1, u1);
+    store_bm(0, ra);                                    // tile 0
+    load_bm(2, ra);
     lds_barrier();
-    do {
-      tile(t, 0, u0);
-      store_bm(1, rb);                                  // tile t + 1
-      load_bm(min(t + 3, last), rb);
-      load_u(min(t + 2, last), u0);
-      lds_barrier();
-      if (t + 1 < nt) tile(t + 1, 1, u1);
-      store_bm(0, ra);                                  // tile t + 2
-      load_bm(min(t + 4, last), ra);
-      load_u(min(t + 3, last), u1);
-      lds_barrier();
-      t += 2;
-    } while (t < nt);
+    mma(0, acc0);
+    store_bm(1, rb);                                    // tile 1
+    load_bm(3, rb);
+    lds_barrier();
+    for (; t + 2 < nt; t += 2) pair(Whole{});
+    pair(Masked{});
   } else {
+    auto pair = [&](auto mask_tag) __attribute__((always_inline)) {
+      mma(1, acc1);                                     // tile t + 1
+      epi(mask_tag, t, acc0, u0);
+      load_u(t + 2, u0);
+      store_bm(0, ra);                                  // tile t + 2
+      load_bm(t + 3, ra);
+      lds_barrier();
+      mma(0, acc0);                                     // tile t + 2
+      epi(mask_tag, t + 1, acc1, u1);
+      load_u(t + 3, u1);
+      store_bm(1, ra);                                  // tile t + 3
+      load_bm(t + 4, ra);
+      lds_barrier();
+    };
     load_bm(0, ra);
     load_u(0, u0);
-    store_bm(0, ra);
-    load_bm(min(1, last), ra);
-    load_u(min(1, last), u1);
+    store_bm(0, ra);                                    // tile 0
+    load_bm(1, ra);
+    load_u(1, u1);
     lds_barrier();
-    do {
-      tile(t, 0, u0);
-      store_bm(1, ra);                                  // tile t + 1
-      load_bm(min(t + 2, last), ra);
-      load_u(min(t + 2, last), u0);
-      lds_barrier();
-      if (t + 1 < nt) tile(t + 1, 1, u1);
-      store_bm(0, ra);                                  // tile t + 2
-      load_bm(min(t + 3, last), ra);
-      load_u(min(t + 3, last), u1);
-      lds_barrier();
-      t += 2;
-    } while (t < nt);
+    mma(0, acc0);
+    store_bm(1, ra);                                    // tile 1
+    load_bm(2, ra);
+    lds_barrier();
+    for (; t + 2 < nt; t += 2) pair(Whole{});
+    pair(Masked{});
   }
 
   // one partial per request: 16-lane reductions of the lane states
@@ -566,6 +653,7 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int b = req0 + 4 * g + ii;
+    if constexpr (!SAMPLE) { bs[ii] = ml[ii]; bx[ii] = ml[ii]; }
     const float M = row16_max(ml[ii]);
     const float ssum = row16_sum(ml[ii] == kNegInf ? 0.f : sl[ii] * __expf(ml[ii] - M));
     const unsigned long long key = row16_max_u64(bs[ii] == kNegInf ? 0ull : best_key(bs[ii], bc[ii]));
@@ -1166,9 +1254,12 @@ static int wide_occupancy(const void* fn, int nw, size_t lds) {
 
 // false: the shape takes another kernel (fp32 tables, a rank other than 32,
 // 64, 128 or 256, or, for the chain, B <= 16)
-static bool wide_plan(bool bf16, bool sample, int B, int r, int V, WidePlan* p, bool stats = true) {
+static bool wide_plan(bool bf16, bool sample, int B, int gamma, int r, int V, WidePlan* p, bool stats = true) {
   const int nch = r / 32;
   if (!bf16 || (stats && B <= 16) || r % 32 || (nch != 1 && nch != 2 && nch != 4 && nch != 8)) return false;
+  // the kernel's buffer offsets are 32-bit and its dropped accesses use 2^31:
+  // every array it addresses must stay below 2 GiB
+  if (static_cast<size_t>(B) * gamma * V * 4 >= (static_cast<size_t>(1) << 31)) return false;
   const int groups = (B + 15) / 16;
   // at least nch / 2 waves, so that a wave loads at most 2 chunks (waves
   // past the last request only load and store operands)
@@ -1194,17 +1285,17 @@ static bool wide_plan(bool bf16, bool sample, int B, int r, int V, WidePlan* p, 
 
 static int partial_count(const StepArgs& a) { return (a.V + a.tile_cols - 1) / a.tile_cols; }
 
-int markov_tile_cols(bool bf16, bool sample, int B, int r, int V) {
+int markov_tile_cols(bool bf16, bool sample, int B, int gamma, int r, int V) {
   if (!bf16) return kMarkovTileF32;
   WidePlan p{};
-  return wide_plan(bf16, sample, B, r, V, &p) ? p.tpw * kWideCols : kMarkovTile;
+  return wide_plan(bf16, sample, B, gamma, r, V, &p) ? p.tpw * kWideCols : kMarkovTile;
 }
 
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
   a.Pn = partial_count(a);
   if (bf16) {
     WidePlan p{};
-    if (wide_plan(bf16, a.sample, a.B, a.r, a.V, &p)) {
+    if (wide_plan(bf16, a.sample, a.B, a.gamma, a.r, a.V, &p)) {
       if (p.tpw * kWideCols != a.tile_cols) return hipErrorInvalidValue;   // plan changed since tile_cols was set
       p.launch(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
     } else if (a.r % 128 == 0) {
@@ -1327,7 +1418,7 @@ hipError_t launch_block_logits(const float* U, const int32_t* prev, const void* 
   a.r = r;
   a.logits_out = out;
   WidePlan p{};
-  if (vec && wide_plan(true, false, M, r, V, &p, false)) {
+  if (vec && wide_plan(true, false, M, 1, r, V, &p, false)) {
     p.launch(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
   } else {
     const dim3 grid((V + 255) / 256, M);
