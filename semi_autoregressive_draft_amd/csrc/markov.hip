@@ -1417,9 +1417,22 @@ hipError_t launch_block_logits(const float* U, const int32_t* prev, const void* 
   a.V = V;
   a.r = r;
   a.logits_out = out;
+  // the wide kernel addresses U and the output with 32-bit offsets: rows go
+  // in chunks of at most 2 GiB of logits each (multiples of 16 rows)
+  const int chunk = static_cast<int>(((static_cast<size_t>(1) << 31) - 1) / (static_cast<size_t>(V) * 4)) / 16 * 16;
   WidePlan p{};
-  if (vec && wide_plan(true, false, M, 1, r, V, &p, false)) {
-    p.launch(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
+  if (vec && chunk > 0 && wide_plan(true, false, min(M, chunk), 1, r, V, &p, false)) {
+    for (int m0 = 0; m0 < M; m0 += chunk) {
+      StepArgs c = a;
+      c.B = min(chunk, M - m0);
+      c.U = U + static_cast<size_t>(m0) * V;
+      c.anchor = prev + m0;
+      c.logits_out = out + static_cast<size_t>(m0) * V;
+      if (m0 > 0 && !wide_plan(true, false, c.B, 1, r, V, &p, false)) return hipErrorInvalidValue;
+      p.launch(c, p.tpw, dim3(p.gx, p.ny), p.nw, s);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   } else {
     const dim3 grid((V + 255) / 256, M);
     if (bf16)

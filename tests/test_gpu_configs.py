@@ -188,3 +188,36 @@ def test_config4_offline_eval_full_size(sigma):
     assert abs(ta[full].mean() - (1 + abar * (1 - abar ** 7) / (1 - abar))) < 0.03
     del teacher, draft
     torch.cuda.empty_cache()
+
+
+def test_teacher_forced_block_logits_full_size():
+    """Teacher-forced block logits at the training shape (512 blocks x 7
+    positions, V = 151936, r = 256): 2.18 GB of logits, which the library
+    splits into row chunks below 2 GiB.  Rows on both sides of the chunk
+    boundary and random rows are recomputed by the oracle one by one."""
+    dev = require_gpu()
+    N, g, V, r = 512, synth.GAMMA, 151936, 256
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(71)
+    U = torch.randn((N, g, V), generator=gen, device=dev)
+    A = (torch.randn((V, r), generator=gen, device=dev) * 0.25).to(torch.bfloat16)
+    Bm = (torch.randn((r, V), generator=gen, device=dev) * 0.25).to(torch.bfloat16)
+    prev = torch.randint(0, V, (N, g), generator=gen, device=dev, dtype=torch.int32)
+    out = torch.full((N, g, V), float("nan"), dtype=torch.float32, device=dev)
+    bd.dspark_apply_block_logits(U, prev, A, Bm, out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rows_total = N * g
+    chunk = (2 ** 31 - 1) // (V * 4) // 16 * 16
+    rows = sorted(set([0, 1, 15, 16, chunk - 1, chunk, chunk + 1, rows_total - 1]
+                      + list(np.random.default_rng(71).choice(rows_total, 8, replace=False))))
+    ridx = torch.as_tensor(rows, device=dev)
+    U_r = U.view(rows_total, V)[ridx].cpu().numpy().astype(np.float64)
+    prev_r = prev.view(rows_total)[ridx].cpu().numpy().reshape(-1, 1)
+    A64 = A.float().cpu().numpy().astype(np.float64)
+    Bm64 = Bm.float().cpu().numpy().astype(np.float64)
+    want = o.teacher_forced_logits(U_r[:, None, :], prev_r, A64, Bm64)[:, 0]
+    got = out.view(rows_total, V)[ridx].cpu().numpy()
+    tight_check(got, want, np.abs(want).max(axis=-1, keepdims=True), what="block logits")
+    del U, out
+    torch.cuda.empty_cache()
