@@ -71,10 +71,14 @@ typedef enum {
                               bounded wait inside a launch ran out (see the conventions above) */
 } dspark_status_t;
 
-typedef enum {
+/* Element types.  The type is a plain 32-bit integer rather than an enum, so
+   that every value a caller passes is well defined for the library to read;
+   values other than these two return DSPARK_EUNSUPPORTED. */
+typedef int32_t dspark_dtype_t;
+enum {
   DSPARK_F32 = 0,  /* IEEE binary32 */
   DSPARK_BF16 = 1  /* bfloat16 (upper half of a binary32) */
-} dspark_dtype_t;
+};
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* dspark_last_error(void);

@@ -13,7 +13,8 @@ import re
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdspark.so")
+# DSPARK_LIB selects another build of the library (the host-sanitized one)
+LIB_PATH = os.environ.get("DSPARK_LIB") or os.path.join(PKG, "libdspark.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "dspark.h")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ETIMEOUT = range(6)
