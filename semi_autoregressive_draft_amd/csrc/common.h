@@ -73,6 +73,15 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   return fmaf(-kLn2f, __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u)), kNegLnLn2);
 }
 
+// A buffer resource over [base, base + bytes) (bytes < 2^31): loads past it
+// read 0 without touching memory and stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+// cache-policy operand of a buffer access: the non-temporal hint (data used
+// once)
+constexpr int kBufferNonTemporal = 2;
+
 // -------------------------------------------------------------------------
 // Online log-sum-exp and argmax states, merged in a fixed order.
 struct LseState { float m, s; };  // value max, sum of exp(x - m)

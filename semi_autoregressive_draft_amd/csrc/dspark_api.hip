@@ -82,6 +82,8 @@ size_t overlap_ws_bytes(int64_t N, int64_t gamma, int64_t V) {
   if (nchunk > 1) {
     s += align_up(static_cast<size_t>(rows) * nchunk * 5 * sizeof(float));
     s += align_up(static_cast<size_t>(rows) * 16) + align_up(static_cast<size_t>(rows) * nchunk * 3 * 8);
+  } else {
+    s += align_up(overlap_resident_ws_bytes(rows));
   }
   return s;
 }
@@ -103,6 +105,11 @@ void carve_overlap_ws(OverlapArgs& a, void* ws, int64_t N, int64_t gamma, int64_
     a.ws_norm = reinterpret_cast<unsigned long long*>(p);
     p += align_up(rows * 16);
     a.ws_fused = reinterpret_cast<unsigned long long*>(p);
+  } else {
+    // the single-read path: tagged chunk-state words, then chunk sums
+    const size_t rows = static_cast<size_t>(N * gamma);
+    a.ws_fused = reinterpret_cast<unsigned long long*>(p);
+    a.ws_split = reinterpret_cast<float*>(p + overlap_resident_ws_bytes(rows) - rows * 16 * sizeof(float));
   }
 }
 

@@ -181,6 +181,9 @@ hipError_t launch_verify(const float* target, const float* draft, const int32_t*
                          int32_t* next_token, float* accept_prob, void* ws, hipStream_t s);
 
 int overlap_tau_blocks(int64_t N);
+// workspace of the single-read path for many rows: [rows][16][4] tagged 64-bit
+// chunk-state words, then [rows][16] float chunk sums
+size_t overlap_resident_ws_bytes(int64_t rows);
 int overlap_split_chunks(int64_t rows, int64_t V);
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s);
 unsigned next_epoch();

@@ -337,9 +337,6 @@ __global__ __launch_bounds__(kWave* KS) void markov_step_bf16(StepArgs a) {
 //    (DPP) run once per request per workgroup; the argmax travels as a 64-bit
 //    order key (best_key).  One partial per (request, workgroup range).
 constexpr int kWideCols = 64;
-// cache-policy operand of a buffer store: the non-temporal hint (written once,
-// not read back by this kernel)
-constexpr int kBufferNonTemporal = 2;
 
 // LDS of the wide kernel: two B-operand buffers of nch chunks, then (when
 // sampling) the seeds of up to 8 x 16 requests
@@ -371,15 +368,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// A buffer resource over [base, base + bytes) (bytes < 2^31, which the
-// launcher checks): loads past it read 0 and stores past it are dropped.  The
-// wide kernel addresses every array through such resources with a per-lane
-// 32-bit offset that stays fixed across tiles plus the tile's offset in a
-// scalar register, so a tile's loads and stores cost no vector address
-// arithmetic.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
+// The wide kernel addresses every array through buffer resources (buf_rsrc,
+// whose sizes the launcher keeps below 2 GiB) with a per-lane 32-bit offset
+// that stays fixed across tiles plus the tile's offset in a scalar register,
+// so a tile's loads and stores cost no vector address arithmetic.
 constexpr uint32_t kDropOffset = 0x80000000u;   // past every resource: the access is dropped
 // Stores of more than 8 bytes take their whole offset in the vector register
 // and a constant 0 as scalar offset: the compiler then keeps a VALU write of

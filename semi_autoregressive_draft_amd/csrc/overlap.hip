@@ -15,6 +15,8 @@
 // 1 touched last.  Few rows (below kSplitRowsMax): each row is split into
 // chunks over several workgroups (statistics, then sums, then a fixed-order
 // finish that also computes tau when one workgroup can).
+#include <cstdlib>
+
 #include "common.h"
 #include "internal.h"
 
@@ -26,6 +28,37 @@ constexpr int kTauThreads = 256;
 constexpr int kSplitChunk = 2048;      // elements per workgroup on the split path
 constexpr int kSplitRowsMax = 1024;    // at and above this many rows, one workgroup per row
 constexpr int kFusedFinishRows = 64;   // up to this many rows, one workgroup finishes rows and tau
+
+// wait words and 64-bit exchange slots of the launches whose workgroups wait
+// for each other (their layout is described where they are used)
+constexpr int kFusedPer = 4;                    // float4 per thread and array
+constexpr int kOvTimeout = 0;                   // word 0: call number of a timed-out wait
+constexpr int kOvRowsDone = 32;
+constexpr int kOvCnt1 = 64;                     // + 32 * row: chunk states published
+constexpr int kOvCnt2 = kOvCnt1 + 32 * kFusedFinishRows;   // + 32 * row: chunk sums published
+static_assert(kOvCnt2 + 32 * kFusedFinishRows <= kOvSyncWords, "overlap wait words");
+
+__device__ __forceinline__ unsigned long long pack2(float x, float y) {
+  return (static_cast<unsigned long long>(__float_as_uint(y)) << 32) | __float_as_uint(x);
+}
+__device__ __forceinline__ float lo_f(unsigned long long v) { return __uint_as_float(static_cast<uint32_t>(v)); }
+__device__ __forceinline__ float hi_f(unsigned long long v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
+__device__ __forceinline__ unsigned long long xchg_dev(unsigned long long* p, unsigned long long v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned add_dev(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// keep the value live so that the wave waits for the atomic's return here
+__device__ __forceinline__ void wait_for(unsigned long long v) { asm volatile("" ::"v"(v) : "memory"); }
+// a wait of this call ran out (only the launches that wait take a call number)
+__device__ __forceinline__ bool call_timed_out(const OverlapArgs& a) {
+  return a.epoch != 0u && a.sync && ld_dev(a.sync + kOvTimeout) == a.epoch;
+}
 
 __device__ __forceinline__ float sum_exp_min4(f32x4 t, f32x4 d, float Lt, float Ld) {
   return (__expf(fminf(t[0] - Lt, d[0] - Ld)) + __expf(fminf(t[1] - Lt, d[1] - Ld))) +
@@ -134,6 +167,272 @@ __global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
     total = block_sum<NW>(candidate_overlap(a, row, rt.m + logf(rt.s), tid, kOvThreads), red_f);
   }
   if (tid == 0) a.alpha[row] = fminf(fmaxf(total, 0.f), 1.f);
+}
+
+// ---- many rows, each read once (dense mode) --------------------------------
+// A resident grid of kResK x S workgroups: slot s = workgroup / kResK takes
+// rows s, s + S, s + 2S, ..., and workgroup c = workgroup % kResK of the slot
+// holds chunk c of each of those rows (its teacher and draft values) in
+// registers across both passes, so every logit is read from memory once.
+// Per row: the chunk's online states are published as four 64-bit words, each
+// tagged with this call's number (a word is its own release flag); wave 0
+// polls the row's kResK x 4 words, folds them in chunk order into the
+// normalisers (every chunk of the row folds the same words in the same order,
+// so all hold the same L_p, L_q), and the data waves add
+// exp(min(t - L_p, d - L_q)) over their registers; the chunk's sum goes to the
+// workspace and a fold kernel adds the kResK sums in chunk order into alpha.
+// Wave 0 does no data loads, so its waits never drain the data waves'
+// look-ahead: while wave 0 waits for the row's partners, waves 1..7 already
+// stream the slot's next row into their second register set.  The wait is
+// bounded in time; a wait that runs out marks the call in the time-out word,
+// and from then on no workgroup of the call waits (alpha and tau become NaN,
+// the status word DSPARK_ETIMEOUT).
+constexpr int kResK = 16;                                  // chunks (workgroups) per row (4 kResK <= 64 words polled)
+constexpr int kResThreads = 512;
+constexpr int kResData = kResThreads - kWave;              // threads of waves 1..7
+constexpr int kResMaxSlotRows = 16384;                     // validity flags of a slot's rows in LDS
+
+template <int P>
+struct ResSet { f32x4 t[P], d[P]; };
+
+// wave-wide max and sum with the in-row steps on DPP and two cross-row
+// shuffles; every lane ends with the same value
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+// (max, sum exp(x - max)) of the wave from each lane's (m, s): the maximum
+// first, then each lane's sum rescaled once
+__device__ __forceinline__ LseState wave_lse(float m, float s) {
+  const float M = wave_max_dpp(m);
+  return LseState{M, wave_sum_dpp(m == kNegInf ? 0.f : s * __expf(m - M))};
+}
+
+template <int P>
+__global__ __launch_bounds__(kResThreads, 1) void overlap_rows_resident(OverlapArgs a, int S) {
+  __shared__ unsigned char va_s[kResMaxSlotRows];
+  __shared__ LseState red_t[2][kResThreads / kWave], red_d[2][kResThreads / kWave];
+  __shared__ float red_f[2][kResThreads / kWave];
+  __shared__ float L_s[2][2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int slot = blockIdx.x / kResK, c = blockIdx.x % kResK;
+  if (slot >= S) return;                                   // padding (whole workgroup)
+  const int rows = a.N * a.gamma;
+  const int n4 = a.V / 4;
+  const int e0 = min(c * a.chunk4, n4), e1 = min(e0 + a.chunk4, n4);
+  const int dt = tid - kWave;                              // data thread index (waves 1..7)
+  const size_t V = static_cast<size_t>(a.V);
+  unsigned* sy = a.sync;
+  // validity of this slot's rows, staged before the loop (a global load in
+  // the loop would wait for the look-ahead loads issued before it)
+  for (int i = tid; i * S + slot < rows; i += kResThreads) va_s[i] = a.valid ? a.valid[i * S + slot] : 1;
+  __syncthreads();
+
+  // the chunk's elements through buffer resources over exactly the chunk:
+  // lanes past its end read 0 without touching memory (and are masked out
+  // of every sum by `in`)
+  const int voff = dt * 16;
+  auto in = [&](int i) __attribute__((always_inline)) { return dt + i * kResData < e1 - e0; };
+  // Every wave issues the same loads at every step, whether or not the row
+  // exists, is valid or is this wave's (wave 0 holds no data): the resource
+  // of a load that is not wanted has no records, so it reads 0 without
+  // touching memory.  With loads behind a branch the compiler cannot count
+  // the loads still in flight, and it waited for all of them (the
+  // look-ahead included) before using a set.
+  auto load = [&](ResSet<P>& X, int it) __attribute__((always_inline)) {
+    const int r = slot + it * S;
+    // uniform over the wave (readfirstlane), so that the resources live in
+    // scalar registers: with a per-lane resource the compiler loops over lanes
+    const bool on = __builtin_amdgcn_readfirstlane(w > 0 && r < rows && va_s[min(it, kResMaxSlotRows - 1)]) != 0;
+    const size_t base = on ? r * V + static_cast<size_t>(e0) * 4 : 0;
+    const size_t bytes = on ? static_cast<size_t>(e1 - e0) * 16 : 0;
+    const __amdgpu_buffer_rsrc_t tr = buf_rsrc(a.teacher + base, bytes);
+    const __amdgpu_buffer_rsrc_t dr = buf_rsrc(a.draft + base, bytes);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      X.t[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, voff, i * kResData * 16,
+                                                                              kBufferNonTemporal));
+      X.d[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, voff, i * kResData * 16,
+                                                                              kBufferNonTemporal));
+    }
+  };
+  // Step it, one barrier at its end.  Data waves: the overlap sum of row
+  // it - 1 (its normalisers came from wave 0 in step it - 1), then set
+  // (it - 1) % 4, free again, starts streaming row it + 3, then the chunk
+  // states of row it + 1 (set (it + 1) % 4, streamed since step it - 2).
+  // Wave 0 meanwhile: the chunk sum of row it - 2 to the workspace, the
+  // chunk states of row it (its waves' states from step it - 1) published,
+  // the row's kResK x 4 words polled and folded into its normalisers.  So
+  // the exchange of a row runs beside a whole step of data work.  Shared
+  // words are double-buffered by row parity.
+  float mth[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, mdh[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  auto valid_row = [&](int it) __attribute__((always_inline)) {
+    return it >= 0 && slot + it * S < rows && va_s[it] != 0;
+  };
+  // chunk states of row it from set X (history slot h), by the data waves
+  auto states = [&](ResSet<P>& X, int it, int h) __attribute__((always_inline)) {
+    if (w == 0 || !valid_row(it)) return;
+    float mt = kNegInf, md = kNegInf;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const float xt = fmaxf(fmaxf(X.t[i][0], X.t[i][1]), fmaxf(X.t[i][2], X.t[i][3]));
+      const float xd = fmaxf(fmaxf(X.d[i][0], X.d[i][1]), fmaxf(X.d[i][2], X.d[i][3]));
+      mt = in(i) ? fmaxf(mt, xt) : mt;
+      md = in(i) ? fmaxf(md, xd) : md;
+    }
+    // the set now keeps exp(x - m) of this thread's maximum m (base 2, one
+    // fused multiply-add and one exponential per element); the overlap sum
+    // rescales it instead of taking a second exponential
+    const float nt = -(mt == kNegInf ? 0.f : mt) * kLog2e, nd = -(md == kNegInf ? 0.f : md) * kLog2e;
+    float st = 0.f, sd = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        X.t[i][k] = __builtin_amdgcn_exp2f(fmaf(X.t[i][k], kLog2e, nt));
+        X.d[i][k] = __builtin_amdgcn_exp2f(fmaf(X.d[i][k], kLog2e, nd));
+      }
+      const float et = (X.t[i][0] + X.t[i][1]) + (X.t[i][2] + X.t[i][3]);
+      const float ed = (X.d[i][0] + X.d[i][1]) + (X.d[i][2] + X.d[i][3]);
+      st += in(i) ? et : 0.f;
+      sd += in(i) ? ed : 0.f;
+    }
+    mth[h] = mt;
+    mdh[h] = md;
+    const LseState lt = wave_lse(mt, st), ld = wave_lse(md, sd);
+    if (lane == 0) { red_t[it & 1][w] = lt; red_d[it & 1][w] = ld; }
+  };
+  // overlap sum of row it from set Z (history slot h), by the data waves:
+  // min(p, q) = min(e_t exp(m_t - L_p), e_d exp(m_d - L_q)) with the kept
+  // e = exp(x - m) of this thread's maxima m
+  auto overlap_sum = [&](ResSet<P>& Z, int it, int h) __attribute__((always_inline)) {
+    if (w == 0 || !valid_row(it)) return;
+    const float mpt = mth[h], mpd = mdh[h];
+    const float at = mpt == kNegInf ? 0.f : __expf(mpt - L_s[it & 1][0]);
+    const float ad = mpd == kNegInf ? 0.f : __expf(mpd - L_s[it & 1][1]);
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const float e = (fminf(Z.t[i][0] * at, Z.d[i][0] * ad) + fminf(Z.t[i][1] * at, Z.d[i][1] * ad)) +
+                      (fminf(Z.t[i][2] * at, Z.d[i][2] * ad) + fminf(Z.t[i][3] * at, Z.d[i][3] * ad));
+      sm += in(i) ? e : 0.f;
+    }
+    sm = wave_sum_dpp(sm);
+    if (lane == 0) red_f[it & 1][w] = sm;
+  };
+  // wave 0's part of step it
+  auto exchange = [&](int it) __attribute__((always_inline)) {
+    if (w != 0) return;
+    if (tid == 0 && valid_row(it - 2)) {                   // the chunk sum of row it - 2
+      const float* rf = red_f[(it - 2) & 1];
+      float tot = rf[1];
+      for (int i = 2; i < kResThreads / kWave; ++i) tot += rf[i];
+      a.ws_split[static_cast<size_t>(slot + (it - 2) * S) * kResK + c] = tot;
+    }
+    if (!valid_row(it)) return;
+    const int r = slot + it * S;
+    const unsigned long long tag = static_cast<unsigned long long>(a.epoch) << 32;
+    unsigned long long* words = a.ws_fused + static_cast<size_t>(r) * kResK * 4;
+    {
+      // the data waves' states: lane i of each 8-lane group takes wave i
+      // (wave 0's entry is empty), then a fixed butterfly over the group
+      const int wi = lane & 7;
+      const LseState rt = wi ? red_t[it & 1][wi] : LseState{kNegInf, 0.f};
+      const LseState rd = wi ? red_d[it & 1][wi] : LseState{kNegInf, 0.f};
+      float mt = rt.m, md = rd.m;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) { mt = fmaxf(mt, __shfl_xor(mt, o)); md = fmaxf(md, __shfl_xor(md, o)); }
+      float st = rt.m == kNegInf ? 0.f : rt.s * __expf(rt.m - mt);
+      float sd = rd.m == kNegInf ? 0.f : rd.s * __expf(rd.m - md);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) { st += __shfl_xor(st, o); sd += __shfl_xor(sd, o); }
+      if (lane < 4) {   // a plain atomic store: nothing waits for it here
+        const float v = lane == 0 ? mt : lane == 1 ? st : lane == 2 ? md : sd;
+        __hip_atomic_store(words + 4 * c + lane, tag | __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // the row's kResK x 4 words, one per lane; waits end at a time-out of
+    // any workgroup of this call
+    unsigned long long v = 0ull;
+    if (ld_dev(sy + kOvTimeout) != a.epoch) {
+      const unsigned long long t0 = wall_clock64();
+      while (true) {
+        v = lane < 4 * kResK ? ld_dev(words + lane) : tag;
+        if (__builtin_amdgcn_ballot_w64((v >> 32) != a.epoch) == 0ull) break;
+        if (wall_clock64() - t0 > a.wait_ticks || ld_dev(sy + kOvTimeout) == a.epoch) {
+          if (lane == 0) __hip_atomic_store(sy + kOvTimeout, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    // fold: lane k < kResK takes chunk k's states; the maxima, then the
+    // rescaled sums, over a fixed butterfly (every lane ends with the same
+    // values, in every workgroup of the row)
+    const float f = __uint_as_float(static_cast<uint32_t>(v));
+    const int k4 = 4 * (lane & (kResK - 1));
+    const float tm = __shfl(f, k4), ts = __shfl(f, k4 + 1), dm = __shfl(f, k4 + 2), ds = __shfl(f, k4 + 3);
+    const float Mt = row16_max(tm), Md = row16_max(dm);
+    const float Lt = Mt + logf(row16_sum(tm == kNegInf ? 0.f : ts * __expf(tm - Mt)));
+    const float Ld = Md + logf(row16_sum(dm == kNegInf ? 0.f : ds * __expf(dm - Md)));
+    if (lane == 0) {
+      L_s[it & 1][0] = Lt;
+      L_s[it & 1][1] = Ld;
+      if (c == 0 && a.lse_draft) a.lse_draft[r] = Ld;
+    }
+  };
+  // set i % 4 holds row i; the four set indices of each step are constants
+  auto step = [&](ResSet<P>& Sm, ResSet<P>& St, int it, int hm, int hs) __attribute__((always_inline)) {
+    exchange(it);
+    overlap_sum(Sm, it - 1, hm);
+    load(Sm, it + 3);                                       // every wave (see load)
+    states(St, it + 1, hs);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  ResSet<P> A, B, C, D;
+  load(A, 0);
+  // keep the rows' loads in row order (the steps count on it)
+  __builtin_amdgcn_sched_barrier(0);
+  load(B, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load(C, 2);
+  states(A, 0, 0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // the last row, n - 1, is published at step n - 1, summed at step n and
+  // stored at step n + 1; the step count is rounded up to whole rotations so
+  // that every step (and its loads) runs unconditionally and the compiler
+  // can count the loads in flight
+  const int n = (rows - slot + S - 1) / S;
+  for (int it = 0; it < n + 2; it += 4) {
+    step(D, B, it, 3, 1);
+    step(A, C, it + 1, 0, 2);
+    step(B, D, it + 2, 1, 3);
+    step(C, A, it + 3, 2, 0);
+  }
+}
+
+// alpha (and the overlap sums) of every row from its kResK chunk sums, in
+// chunk order; NaN for every row when a wait of the call ran out
+__global__ __launch_bounds__(256) void overlap_rows_resident_fold(OverlapArgs a) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.N * a.gamma) return;
+  const bool timed_out = ld_dev(a.sync + kOvTimeout) == a.epoch;
+  const bool vr = !a.valid || a.valid[r];
+  float s = 0.f;
+  if (vr) {
+#pragma unroll
+    for (int k = 0; k < kResK; ++k) s += a.ws_split[static_cast<size_t>(r) * kResK + k];
+    if (a.ov_sum) a.ov_sum[r] = s;
+  }
+  a.alpha[r] = timed_out ? __builtin_nanf("") : (vr ? fminf(fmaxf(s, 0.f), 1.f) : 0.f);
 }
 
 // ---- several workgroups per row (few rows) ---------------------------------
@@ -291,7 +590,7 @@ __device__ void tau_range(const OverlapArgs& a, int blk) {
     __syncthreads();
     if (tid < G && a.accept_rate_at) a.accept_rate_at[tid] = tot[G + tid] > 0.0 ? tot[tid] / tot[G + tid] : 0.0;
     if (tid == 0 && a.tau_mean) *a.tau_mean = tot[2 * G + 1] > 0.0 ? tot[2 * G] / tot[2 * G + 1] : 0.0;
-    if (tid == 0 && a.status) *a.status = kStatusOk;   // these paths never wait
+    if (tid == 0 && a.status) *a.status = call_timed_out(a) ? kStatusTimeout : kStatusOk;
   }
 }
 
@@ -346,30 +645,6 @@ __global__ __launch_bounds__(kTauThreads) void overlap_split_finish_tau(OverlapA
 // needs every chunk resident at once (the launcher checks the occupancy); the
 // wait is bounded in time, and a wait that runs out marks the call, which then
 // reports NaN for tau.
-constexpr int kFusedPer = 4;                    // float4 per thread and array
-constexpr int kOvTimeout = 0;                   // word 0: call number of a timed-out wait
-constexpr int kOvRowsDone = 32;
-constexpr int kOvCnt1 = 64;                     // + 32 * row: chunk states published
-constexpr int kOvCnt2 = kOvCnt1 + 32 * kFusedFinishRows;   // + 32 * row: chunk sums published
-static_assert(kOvCnt2 + 32 * kFusedFinishRows <= kOvSyncWords, "overlap wait words");
-
-__device__ __forceinline__ unsigned long long pack2(float x, float y) {
-  return (static_cast<unsigned long long>(__float_as_uint(y)) << 32) | __float_as_uint(x);
-}
-__device__ __forceinline__ float lo_f(unsigned long long v) { return __uint_as_float(static_cast<uint32_t>(v)); }
-__device__ __forceinline__ float hi_f(unsigned long long v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
-__device__ __forceinline__ unsigned long long xchg_dev(unsigned long long* p, unsigned long long v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned add_dev(unsigned* p, unsigned v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// keep the value live so that the wave waits for the atomic's return here
-__device__ __forceinline__ void wait_for(unsigned long long v) { asm volatile("" ::"v"(v) : "memory"); }
 
 // By one workgroup: tau of every block, accept_rate@i and the mean tau from
 // the alphas al_s and the validity flags va_s of all rows (<= 64 rows).
@@ -600,7 +875,7 @@ __global__ __launch_bounds__(64) void tau_finish(OverlapArgs a) {
   __syncthreads();
   if (f < G && a.accept_rate_at) a.accept_rate_at[f] = tot[G + f] > 0.0 ? tot[f] / tot[G + f] : 0.0;
   if (f == 0 && a.tau_mean) *a.tau_mean = tot[2 * G + 1] > 0.0 ? tot[2 * G] / tot[2 * G + 1] : 0.0;
-  if (f == 0 && a.status) *a.status = kStatusOk;
+  if (f == 0 && a.status) *a.status = call_timed_out(a) ? kStatusTimeout : kStatusOk;
 }
 
 int overlap_tau_blocks(int64_t N) { return static_cast<int>((N + kTauThreads - 1) / kTauThreads); }
@@ -624,6 +899,45 @@ static bool fused_fits(const OverlapArgs& a, int rows) {
   return static_cast<long long>(per_cu) * d.cus >= static_cast<long long>(a.nchunk) * rows;
 }
 
+size_t overlap_resident_ws_bytes(int64_t rows) {
+  return static_cast<size_t>(rows) * kResK * (4 * sizeof(unsigned long long) + sizeof(float));
+}
+
+// The single-read path for many rows when it applies (dense mode, the row's
+// chunk fits the register sets, every workgroup resident at once; the
+// environment variable DSPARK_OVERLAP_RESIDENT=0 turns it off): launches it
+// with a.epoch, a.chunk4 and a.wait_ticks set and returns true.
+static bool resident_rows_launch(OverlapArgs& a, int rows, hipStream_t s) {
+  const char* env = std::getenv("DSPARK_OVERLAP_RESIDENT");
+  if (env && env[0] == '0') return false;
+  const DeviceInfo d = device_info();
+  if (d.cus <= 0 || d.clock_khz <= 0) return false;
+  const int n4 = a.V / 4;
+  const int chunk4 = (n4 + kResK - 1) / kResK;
+  const int need = (chunk4 + kResData - 1) / kResData;           // float4 per thread and array
+  const void* fn = need <= 2 ? reinterpret_cast<const void*>(&overlap_rows_resident<2>)
+                 : need <= 4 ? reinterpret_cast<const void*>(&overlap_rows_resident<4>)
+                 : need <= 6 ? reinterpret_cast<const void*>(&overlap_rows_resident<6>) : nullptr;
+  if (!fn) return false;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kResThreads, 0) != hipSuccess || per_cu < 1)
+    return false;
+  const int S = per_cu * d.cus / kResK;
+  if (S < 1 || static_cast<long long>(S) * kResMaxSlotRows < rows) return false;
+  a.chunk4 = chunk4;
+  a.epoch = next_epoch();
+  // the wait bound: 100 ms, or DSPARK_OVERLAP_WAIT_US microseconds (a test
+  // sets a bound too short to wait out, to take the time-out path)
+  const char* wenv = std::getenv("DSPARK_OVERLAP_WAIT_US");
+  a.wait_ticks = static_cast<unsigned long long>(d.clock_khz) *
+                 (wenv ? static_cast<unsigned long long>(std::strtoull(wenv, nullptr, 10)) : 100000ull) / 1000ull;
+  const dim3 grid(S * kResK);
+  if (need <= 2) hipLaunchKernelGGL(overlap_rows_resident<2>, grid, dim3(kResThreads), 0, s, a, S);
+  else if (need <= 4) hipLaunchKernelGGL(overlap_rows_resident<4>, grid, dim3(kResThreads), 0, s, a, S);
+  else hipLaunchKernelGGL(overlap_rows_resident<6>, grid, dim3(kResThreads), 0, s, a, S);
+  return true;
+}
+
 hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s) {
   a.nblk = overlap_tau_blocks(a.N);
   const int rows = a.N * a.gamma;
@@ -639,7 +953,11 @@ hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  if (a.nchunk <= 1) {
+  if (a.nchunk <= 1 && a.draft && a.sync && a.ws_fused && a.ws_split && resident_rows_launch(a, rows, s)) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(overlap_rows_resident_fold, dim3((rows + 255) / 256), dim3(256), 0, s, a);
+  } else if (a.nchunk <= 1) {
     hipLaunchKernelGGL(overlap_rows, dim3(rows), dim3(kOvThreads), 0, s, a);
   } else {
     const int n4 = a.V / 4;

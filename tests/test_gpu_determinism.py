@@ -44,7 +44,8 @@ def test_lm_head_is_deterministic(M, H, V):
 
 @pytest.mark.parametrize("N,V,k", [(1, 151936, 0),    # one launch with chunk exchanges
                                    (9, 30000, 0),     # split path
-                                   (300, 4096, 0),    # one workgroup per row
+                                   (300, 4096, 0),    # many rows, each read once
+                                   (160, 30004, 0),   # many rows, ragged chunks
                                    (5, 20000, 16),    # candidates, one launch
                                    (300, 4096, 16)])  # candidates, one workgroup per row
 def test_overlap_tau_is_deterministic(N, V, k):

@@ -349,11 +349,16 @@ def _check_tau(got, alpha_raw, valid):
     assert abs(mean - mean_ref) < ALPHA_ABS
 
 
-@pytest.mark.parametrize("sigma,N", [(0.5, 9), (1.0, 9), (2.0, 9),
-                                     (1.0, 20),    # split rows, per-row finish kernel
-                                     (1.0, 200)])  # one workgroup per row, several tau blocks
-def test_overlap_dense_parity(sigma, N):
-    V = 5000
+@pytest.mark.parametrize("sigma,N,V,resident", [
+    (0.5, 9, 5000, True), (1.0, 9, 5000, True), (2.0, 9, 5000, True),
+    (1.0, 20, 5000, True),       # split rows, per-row finish kernel
+    (1.0, 200, 5000, False),     # one workgroup per row (two passes), several tau blocks
+    (1.0, 200, 5000, True),      # many rows read once: 16 chunks per row, 2 float4 per thread
+    (2.0, 160, 30004, True),     # ragged last chunk
+    (0.5, 150, 100000, True),    # 4 float4 per thread and array
+])
+def test_overlap_dense_parity(sigma, N, V, resident, monkeypatch):
+    monkeypatch.setenv("DSPARK_OVERLAP_RESIDENT", "1" if resident else "0")
     teacher, draft = synth.overlap_inputs(N, V, sigma, seed=1)
     valid = synth.validity(N, seed=1, trunc_frac=0.4, n_dummy=1)
     got = _run_overlap(teacher, draft=draft, valid=valid)
@@ -374,7 +379,8 @@ def test_overlap_single_launch_leaves_its_workspace_ready():
     # (and a many-row call on the split path) in turn
     dev = require_gpu()
     cases = [("dense", 9, 5000, 4), ("cand", 5, 5000, 5), ("dense", 2, 151936, 6),
-             ("dense", 20, 5000, 7), ("cand", 9, 151936, 8), ("dense", 9, 5000, 9)]
+             ("dense", 20, 5000, 7), ("dense", 160, 4096, 10), ("cand", 9, 151936, 8),
+             ("dense", 150, 4096, 11), ("dense", 9, 5000, 9)]
     size = max(bd.dspark_overlap_tau_workspace(N, 7, V) for _, N, V, _ in cases)
     ws = torch.zeros(size, dtype=torch.uint8, device=dev)
     status = torch.full((1,), -1, dtype=torch.int32, device=dev)
@@ -404,6 +410,43 @@ def test_overlap_single_launch_leaves_its_workspace_ready():
         status.fill_(-1)
         got = (alpha.cpu().numpy(), tau.cpu().numpy(), acc.cpu().numpy(), float(mean.cpu()[0]))
         _check_tau(got, a_raw, valid)
+
+
+def test_overlap_many_rows_time_out_is_reported(monkeypatch):
+    """The single-read path for many rows waits for the other chunks of each
+    row; a wait bound of 0 (set from the host) makes those waits run out.
+    The kernels still finish, and the call reports it: the status word is
+    ETIMEOUT and alpha, tau and the aggregates are NaN.  The next call with
+    the normal bound is correct again."""
+    dev = require_gpu()
+    N, V = 160, 4096
+    teacher, draft = synth.overlap_inputs(N, V, 1.0, seed=12)
+    valid = synth.validity(N, seed=12, trunc_frac=0.2)
+    ws = torch.zeros(bd.dspark_overlap_tau_workspace(N, 7, V), dtype=torch.uint8, device=dev)
+    status = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    alpha = torch.empty((N, 7), dtype=torch.float32, device=dev)
+    tau = torch.empty((N,), dtype=torch.float32, device=dev)
+    acc = torch.empty((7,), dtype=torch.float64, device=dev)
+    mean = torch.empty((1,), dtype=torch.float64, device=dev)
+    t, d, v = to_dev(teacher), to_dev(draft), to_dev(valid)
+    monkeypatch.setenv("DSPARK_OVERLAP_RESIDENT", "1")
+    monkeypatch.setenv("DSPARK_OVERLAP_WAIT_US", "0")
+    bd.dspark_overlap_tau(t, alpha, tau, draft=d, valid=v, accept_rate_at=acc, tau_mean=mean, ws=ws,
+                          status=status)
+    torch.cuda.synchronize()
+    assert int(status.cpu()[0]) == bd.ETIMEOUT
+    assert np.isnan(alpha.cpu().numpy()).all() and np.isnan(tau.cpu().numpy()).all()
+    assert np.isnan(float(mean.cpu()[0]))
+    with pytest.raises(bd.DsparkError):
+        bd.check_device_status(status, "overlap")
+    monkeypatch.delenv("DSPARK_OVERLAP_WAIT_US")
+    status.fill_(-1)
+    bd.dspark_overlap_tau(t, alpha, tau, draft=d, valid=v, accept_rate_at=acc, tau_mean=mean, ws=ws,
+                          status=status)
+    torch.cuda.synchronize()
+    bd.check_device_status(status, "overlap")
+    a_raw, _ = o.overlap_dense(teacher.astype(np.float64), draft.astype(np.float64))
+    _check_tau((alpha.cpu().numpy(), tau.cpu().numpy(), acc.cpu().numpy(), float(mean.cpu()[0])), a_raw, valid)
 
 
 @pytest.mark.parametrize("k,N", [(16, 5), (64, 5), (16, 20), (16, 300)])
@@ -580,7 +623,7 @@ def _check_loss(per, losses, want_per, want_losses):
     (1, 0.5, False),     # 7 rows: the one-launch overlap path
     (9, 1.0, True),      # 63 rows, decay-weighted confidence term
     (20, 2.0, False),    # 140 rows: chunked rows over several launches
-    (200, 1.0, False),   # 1400 rows: one workgroup per row
+    (200, 1.0, False),   # 1400 rows: many rows, each read once
 ])
 def test_compute_loss_parity(N, sigma, conf_decay):
     V, gamma = 5000, 7
