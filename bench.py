@@ -437,7 +437,12 @@ def bench_propose(name, inp, overlap, weights, dev, stream, K, W, flush, cold_re
         mk["measured_hbm_bytes"] = tr
         mk["measured_GBps"] = round(tr / (mk["ms"] * 1e-3) / 1e9, 1) if tr else None
     else:
-        info["markov"]["bound"] = "hbm (Bm and U_j streamed once per position)"
+        mk = info["markov"]
+        mk["bound"] = "hbm (Bm and U_j streamed once per position)"
+        # the per-position wide step's own HBM bytes (rocprofv3 counters), for
+        # its share of the stage (the top-k recompute and merges are the rest)
+        tr = traffic_for("markov_step_wide", name, 1)
+        mk["wide_step_measured_hbm_bytes_per_position"] = tr
     roof = roofline_lm(work, t["lm_ms"], kern, name)
     out = {
         "B": inp.B, "gamma": inp.gamma, "H": inp.H, "V": inp.V, "r": inp.r, "topk": inp.topk,
