@@ -27,12 +27,15 @@ pytestmark = pytest.mark.gpu
     (600, 136, 2104, "bf16"),     # several row tiles, K tail, vocabulary tail inside an XCD group
     (257, 8, 264, "bf16"),        # tiled, one K stage that is all tail, one row past a tile
     (270, 64, 1032, "bf16"),      # tiled, exactly one full K stage
+    # more tiles than compute units (several rounds of workgroups per XCD)
+    (600, 136, 50000, "bf16"),    # 3 row tiles, K tail
+    (300, 200, 40008, "bf16"),    # ragged M, K tail, vocabulary tail
 ])
 def test_lm_head_parity(M, H, V, wdtype):
     dev = require_gpu()
     h = synth.normal((M, H), 1.0, 11, synth.TID_H, wdtype)
     w = synth.normal((V, H), 0.02, 11, synth.TID_WLM, wdtype)
-    U = torch.empty((M, V), dtype=torch.float32, device=dev)
+    U = torch.full((M, V), float("nan"), dtype=torch.float32, device=dev)
     bd.dspark_lm_head(to_dev(h, wdtype), to_dev(w, wdtype), U)
     got = U.cpu().numpy()
     want = o.lm_head(o.to_f64(h, wdtype), o.to_f64(w, wdtype))
