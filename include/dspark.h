@@ -130,7 +130,8 @@ dspark_status_t dspark_markov_propose_workspace(int64_t B, int64_t gamma, int64_
 
 /*
  * How dspark_markov_propose will run the chain for these sizes on the current
- * device: *resident_workgroups > 0 when one cooperative kernel keeps Bm on chip
+ * device: *resident_workgroups > 0 when one resident kernel (a plain launch of
+ * one workgroup per compute unit, after an occupancy check) keeps Bm on chip
  * for all positions with that many workgroups (bf16, B = 1 with r = 64, 128 or
  * 256, or B <= 16 with r = 256, when the share of Bm fits in registers and
  * LDS), 0 when it runs one step kernel per position.  Environment:
