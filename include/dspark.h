@@ -355,10 +355,19 @@ dspark_status_t dspark_overlap_tau_workspace(int64_t N, int64_t gamma, int64_t V
  *   ws, ws_bytes   workspace of at least dspark_overlap_tau_workspace() bytes,
  *                  zero-filled before its first use; every call leaves the
  *                  part that must start at zero zeroed again (one call at a
- *                  time per workspace).  Few rows (N * gamma <= 64) run as one
- *                  launch whose chunks wait for their row's normalisers; if
- *                  such a wait runs past its bound (100 ms, only possible when
- *                  other long work occupies the device) tau and tau_mean are NaN.
+ *                  time per workspace).  Two paths wait inside one launch:
+ *                  few rows (N * gamma <= 64) run as one launch whose chunks
+ *                  wait for their row's normalisers, and in dense mode many
+ *                  rows (N * gamma >= 1024, V <= 172032) run on a resident
+ *                  grid (one workgroup per compute unit, after an occupancy
+ *                  check) whose 16 workgroups per row exchange their chunk
+ *                  states.  Such waits need every workgroup of the launch
+ *                  resident; if other long work keeps some from starting, a
+ *                  wait runs past its bound (100 ms; on the resident grid the
+ *                  first time-out ends every later wait of the call) and tau
+ *                  and tau_mean (and on the resident grid alpha) are NaN.
+ *                  Environment: DSPARK_OVERLAP_RESIDENT=0 selects the
+ *                  two-pass kernel for many rows instead (no waits).
  *   status         [1] int32 or NULL   device status word: DSPARK_ETIMEOUT when
  *                  such a wait ran out (outputs invalid), else DSPARK_OK
  * Requirements: N, gamma, V > 0; gamma <= 16; V % 4 == 0 (16-byte rows);
