@@ -382,7 +382,9 @@ constexpr uint32_t kDropOffset = 0x80000000u;   // past every resource: the acce
 
 // STATS = false: teacher-forced block logits only (every row's previous token
 // given; each tile's U~ is stored to logits_out and nothing else is kept).
-template <int NCH, int CPW, bool SAMPLE, bool STATS = true>
+// DUMP = false: the chain with no U~ dump requested (no dump store is issued;
+// a store to a resource of no records still costs its issue).
+template <int NCH, int CPW, bool SAMPLE, bool STATS = true, bool DUMP = true>
 __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
   extern __shared__ __align__(16) unsigned char wide_lds[];
   u32x4* const ops = reinterpret_cast<u32x4*>(wide_lds);   // [2][NCH + 1][4][64] B operands
@@ -503,6 +505,7 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
     const bool cok = !MASK || (t < nt && col < a.V);
     const int tofx = t * kWideCols * 4, tofs = t * (kWideCols / kSeg) * 4;
     float xs[4][4];
+    float seg[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       float* const x = xs[ii];
@@ -519,9 +522,16 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
         continue;
       }
       const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      // lanes 2s and 2s + 1 hold one 8-column segment; both store its maximum
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaxf(m4, dpp_f<kDppXor1>(m4))), seg_rsrc,
-                                            static_cast<int>(cok ? soff[ii] : kDropOffset), tofs, 0);
+      // lanes 2s and 2s + 1 both end with the maximum of 8-column segment s
+      seg[ii] = fmaxf(m4, dpp_f<kDppXor1>(m4));
+      if (ii & 1) {
+        // one store for requests ii - 1 and ii: the even lane of each pair
+        // stores the first's segment maximum, the odd lane the second's
+        const bool odd = (n & 1) != 0;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(odd ? seg[ii] : seg[ii - 1]), seg_rsrc,
+                                              static_cast<int>(cok ? (odd ? soff[ii] : soff[ii - 1]) : kDropOffset),
+                                              tofs, 0);
+      }
       if constexpr (SAMPLE) {
         const uint64_t sd = seeds_s[w * 16 + 4 * g + ii];
         const Philox4 r = philox4x32_10(col >> 2, a.j, a.off_lo, a.off_hi, static_cast<uint32_t>(sd),
@@ -556,8 +566,8 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
       sl[ii] = fmaf(sl[ii], __builtin_amdgcn_exp2f(fmaf(ml[ii], kLog2e, nm2)), (e0 + e1) + (e2 + e3));
       ml[ii] = mn;
     }
-    if constexpr (STATS) {
-      // the U~ dump (a resource of no records when there is none)
+    if constexpr (STATS && DUMP) {
+      // the U~ dump
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{xs[ii][0], xs[ii][1], xs[ii][2], xs[ii][3]}),
@@ -1205,13 +1215,16 @@ static void launch_bf16(const StepArgs& a, hipStream_t s) {
 struct WidePlan {
   const void* fn;
   void (*launch)(const StepArgs&, int, dim3, int, hipStream_t);
+  // the same kernel without the U~ dump stores (a chain with no dump): the
+  // same registers and LDS, so the plan (from fn's occupancy) holds for it
+  void (*launch_nodump)(const StepArgs&, int, dim3, int, hipStream_t);
   int nw, ny, tpw, nx, gx;
   size_t lds;
 };
 
-template <int NCH, int CPW, bool SAMPLE, bool STATS>
+template <int NCH, int CPW, bool SAMPLE, bool STATS, bool DUMP = true>
 static void launch_wide_kernel(const StepArgs& a, int tpw, dim3 grid, int nw, hipStream_t s) {
-  hipLaunchKernelGGL((markov_step_wide<NCH, CPW, SAMPLE, STATS>), grid, dim3(kWave * nw),
+  hipLaunchKernelGGL((markov_step_wide<NCH, CPW, SAMPLE, STATS, DUMP>), grid, dim3(kWave * nw),
                      wide_ops_bytes(NCH) + (SAMPLE ? kWideSeedBytes : 0), s, a, tpw);
 }
 
@@ -1221,12 +1234,15 @@ static void pick_wide(bool sample, bool stats, WidePlan* p) {
   if (!stats) {
     p->fn = reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, false, false>);
     p->launch = &launch_wide_kernel<NCH, CPW, false, false>;
+    p->launch_nodump = p->launch;
     p->lds = wide_ops_bytes(NCH);
     return;
   }
   p->fn = sample ? reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, true, true>)
                  : reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, false, true>);
   p->launch = sample ? &launch_wide_kernel<NCH, CPW, true, true> : &launch_wide_kernel<NCH, CPW, false, true>;
+  p->launch_nodump = sample ? &launch_wide_kernel<NCH, CPW, true, true, false>
+                            : &launch_wide_kernel<NCH, CPW, false, true, false>;
   p->lds = wide_ops_bytes(NCH) + (sample ? kWideSeedBytes : 0);
 }
 
@@ -1289,7 +1305,7 @@ hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
     WidePlan p{};
     if (wide_plan(bf16, a.sample, a.B, a.gamma, a.r, a.V, &p)) {
       if (p.tpw * kWideCols != a.tile_cols) return hipErrorInvalidValue;   // plan changed since tile_cols was set
-      p.launch(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
+      (a.logits_out ? p.launch : p.launch_nodump)(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
     } else if (a.r % 128 == 0) {
       // small batches split r over waves so that a step has enough waves in flight
       launch_bf16<1, 4>(a, s);
