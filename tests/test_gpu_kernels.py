@@ -249,6 +249,20 @@ def test_markov_nan_row_keeps_gathers_inside_the_table(B, V, r, topk):
     assert np.all((ids >= -1) & (ids < V))
 
 
+@pytest.mark.parametrize("T", [0.0, 0.8])
+def test_markov_without_dump_matches_with_dump(T):
+    # the per-position wide step has a variant that issues no U~ dump stores
+    # (chain with no dump requested): the same tokens, logits, lse and top-k,
+    # bit for bit
+    B, V, r = 40, 5000, 256
+    U, anchor, A, Bm = _markov_case(B, V, r, "bf16", seed=14)
+    seeds = np.arange(B, dtype=np.uint64) * 7 + 3 if T > 0 else None
+    with_dump = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=2, topk=8, dump=True)
+    no_dump = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=2, topk=8, dump=False)
+    for k in no_dump:
+        assert np.array_equal(no_dump[k].view(np.uint8), with_dump[k].view(np.uint8)), k
+
+
 def test_markov_zero_transition_is_parallel_argmax():
     B, V, r = 4, 3000, 64
     U = synth.base_logits(B, V, seed=8)
