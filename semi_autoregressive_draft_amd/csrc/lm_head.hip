@@ -10,20 +10,22 @@ namespace dspark {
 
 // ---------------------------------------------------------------------------
 // Tiled path (larger M): the bound moves from HBM to MFMA (2MHV flops over
-// 2VH bytes of W_lm).  Workgroup tile 256 (vocabulary) x 256 (rows of h), K in
+// 2VH bytes of W_lm).  Workgroup tile 320 (vocabulary) x 256 (rows of h), K in
 // stages of 64, 8 waves in a 2 (vocabulary) x 4 (rows) layout, each wave
-// 128 x 64 as a 4 x 2 grid of v_mfma_f32_32x32x16_bf16 tiles.  128
+// 160 x 64 as a 5 x 2 grid of v_mfma_f32_32x32x16_bf16 tiles.  160
 // accumulators per wave leave room for two waves per SIMD, so one wave's waits
-// hide under the other's MFMAs.
+// hide under the other's MFMAs.  (A 320-wide tile moves 10% fewer operand
+// bytes per output than a square 256 one, and 475 x 7 tiles at V = 151936,
+// M = 1792 fill 13 whole rounds of the 256 CUs.)
 //
 // Operands move global -> LDS by DMA (global_load_lds_dwordx4: each wave
 // instruction fills 1 KB of LDS in lane order) into a ring of 2 stages of
-// 64 KB.  A stage holds 256 rows x 128 bytes (one whole cache line per row) of
-// W_lm and of h; LDS lines of 256 bytes hold two rows, and 16-byte chunk slots
-// are XOR-swizzled by the line index mod 8, so that the DMA writes stay
-// contiguous and the MFMA operand reads (16 consecutive rows per 16 lanes)
-// touch every bank once.  The DMA of stage st + 2 is issued right after the
-// barrier that ends stage st.
+// 72 KB.  A stage holds 320 rows of W_lm and 256 rows of h, 128 bytes (one
+// whole cache line) per row; LDS lines of 256 bytes hold two rows, and 16-byte
+// chunk slots are XOR-swizzled by the line index mod 8, so that the DMA writes
+// stay contiguous and the MFMA operand reads (16 consecutive rows per 16
+// lanes) touch every bank once.  The DMA of stage st + 2 is issued right after
+// the barrier that ends stage st.
 //
 // Fragment reads are software-pipelined over two register sets: the reads of
 // 16-deep step ks + 1 are in flight while the MFMAs of step ks run.  They are
@@ -35,19 +37,23 @@ namespace dspark {
 // of the 32 x 32 tile and each dword store of 64 lanes writes two whole
 // 128-byte rows of U.
 //
-// Tile order is XCD-aware: workgroup L runs on XCD L % 8, and the k-th
-// workgroup of an XCD takes vocabulary tile 8 (k / MT) + L % 8 and row tile
-// k % MT, so the MT row tiles that share one W_lm tile run back to back on the
-// same XCD and reuse it from that XCD's L2 (W_lm is read from HBM about once).
-constexpr int kGV = 256, kGM = 256, kGK = 64, kGThreads = 512;
-constexpr int kGOpBytes = kGV * kGK * 2;                             // 32 KB
-constexpr int kGStageBytes = 2 * kGOpBytes;                          // 64 KB
+// Tile order is XCD-aware: the tiles, row tile fastest, are cut into 8
+// contiguous runs whose lengths differ by at most one; workgroup L runs on XCD
+// L % 8 and takes tile L / 8 of run L % 8.  The MT row tiles that share one
+// W_lm tile thus run back to back on one XCD and reuse it from that XCD's L2
+// (W_lm is read from HBM about once), and no XCD has a round more than another.
+constexpr int kGNI = 5;                                                // 32-column MFMA tiles per wave
+constexpr int kGV = 64 * kGNI, kGM = 256, kGK = 64, kGThreads = 512;
+constexpr int kGWBytes = kGV * kGK * 2;                                // 40 KB
+constexpr int kGHBytes = kGM * kGK * 2;                                // 32 KB
+constexpr int kGStageBytes = kGWBytes + kGHBytes;                      // 72 KB
 constexpr size_t kGemmLds = 2 * static_cast<size_t>(kGStageBytes);
+constexpr int kGDma = kGNI + 4;                                        // DMA instructions per wave and stage
 
-// LDS byte offset of (row, 16-byte chunk c < 8) inside one 256-row operand
-// block: 256-byte lines of 2 rows, slots XOR-swizzled by the line index so that
-// 16 consecutive rows at one chunk fall in 16 distinct 16-byte bank groups
-// (64 banks of 4 bytes).  Row + 32 adds exactly 4096 bytes.
+// LDS byte offset of (row, 16-byte chunk c < 8) inside one operand block:
+// 256-byte lines of 2 rows, slots XOR-swizzled by the line index so that 16
+// consecutive rows at one chunk fall in 16 distinct 16-byte bank groups (64
+// banks of 4 bytes).  Row + 32 adds exactly 4096 bytes.
 __device__ __forceinline__ int swz(int row, int c) {
   const int line = row >> 1;
   return line * 256 + ((((row & 1) << 3) | c) ^ (line & 7)) * 16;
@@ -60,9 +66,13 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, float* __restrict__ U,
     int M, int H, int V, int VT, int MT) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char gsm[];
-  const int L = blockIdx.x, kx = L >> 3;
-  const int vt = (kx / MT) * 8 + (L & 7), mt = kx % MT;
-  if (vt >= VT) return;                                 // whole workgroup
+  const int L = blockIdx.x, x = L & 7;
+  const int T = VT * MT;
+  const int s0 = static_cast<int>((static_cast<long long>(x) * T) >> 3);
+  const int s1 = static_cast<int>((static_cast<long long>(x + 1) * T) >> 3);
+  const int tile = s0 + (L >> 3);
+  if (tile >= s1) return;                               // whole workgroup
+  const int vt = tile / MT, mt = tile - vt * MT;
   const int v0 = vt * kGV, m0 = mt * kGM;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wv = w & 1, wm = w >> 1;                    // 2 x 4 waves
@@ -73,82 +83,89 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
   // left pending across the loop would also make its LDS waits full drains
   float* Ub = U + static_cast<size_t>(m0) * V + v0;
   asm volatile("" : "+s"(Ub));
+  // the tile's first rows of W_lm and h: the DMA offsets below are relative
+  // to them (at most 320 rows, so 32 bits hold them)
+  const uint16_t* const Wt = W + static_cast<size_t>(v0) * H;
+  const uint16_t* const ht = h + static_cast<size_t>(m0) * H;
 
-  // DMA: wave w fills 1 KB blocks 4w .. 4w + 3 of the W_lm block (instructions
-  // q = 0..3) and of the h block (q = 4..7).  Lane i of an instruction writes
-  // byte 16 i of its block, i.e. line 4 blk + i / 16, slot i % 16, and loads the
-  // (row, chunk) the swizzle places there.  Rows past V or M read the last
-  // valid row (their outputs are never stored); H % 8 == 0, so every chunk is
-  // whole, and chunks past H are clamped into the row and zeroed once landed.
-  const uint16_t* rowp[8];
-  int c8[8];
+  // DMA: wave w fills 1 KB blocks kGNI w .. kGNI w + kGNI - 1 of the W_lm
+  // block (instructions q < kGNI) and blocks 4w .. 4w + 3 of the h block.
+  // Lane i of an instruction writes byte 16 i of its block, i.e. line
+  // 4 blk + i / 16, slot i % 16, and loads the (row, chunk) the swizzle places
+  // there.  Rows past V or M read the last valid row (their outputs are never
+  // stored); H % 8 == 0, so every chunk is whole, and chunks past H are
+  // clamped into the row and zeroed once landed.
+  auto block_of = [&](int q) __attribute__((always_inline)) { return q < kGNI ? w * kGNI + q : w * 4 + (q - kGNI); };
+  auto chunk8 = [&](int q) __attribute__((always_inline)) {
+    const int line = block_of(q) * 4 + (lane >> 4);
+    return 8 * (((lane & 15) ^ (line & 7)) & 7);
+  };
+  uint32_t ro[kGDma];                                   // element offset of the lane's (row, chunk)
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const bool isW = q < 4;
-    const int blk = w * 4 + (q & 3);
-    const int line = blk * 4 + (lane >> 4);
+  for (int q = 0; q < kGDma; ++q) {
+    const bool isW = q < kGNI;
+    const int line = block_of(q) * 4 + (lane >> 4);
     const int slot = (lane & 15) ^ (line & 7);
-    const int row = line * 2 + (slot >> 3);
-    const int gr = min((isW ? v0 : m0) + row, (isW ? V : M) - 1);
-    rowp[q] = (isW ? W : h) + static_cast<size_t>(gr) * H;
-    c8[q] = 8 * (slot & 7);
+    const int row = min(line * 2 + (slot >> 3), (isW ? V - v0 : M - m0) - 1);
+    ro[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(H) + 8 * (slot & 7);
   }
-  auto issue = [&](int st) {
+  auto dst_of = [&](unsigned char* base, int q) __attribute__((always_inline)) {
+    return base + (q < kGNI ? 0 : kGWBytes) + block_of(q) * 1024;
+  };
+  auto issue = [&](int st) __attribute__((always_inline)) {
     unsigned char* base = gsm + (st & 1) * kGStageBytes;
     const bool full = st < nfull;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int off = full ? st * kGK + c8[q] : min(st * kGK + c8[q], H - 8);
-      unsigned char* dst = base + (q < 4 ? 0 : kGOpBytes) + (w * 4 + (q & 3)) * 1024;
-      __builtin_amdgcn_global_load_lds(rowp[q] + off, reinterpret_cast<void*>(dst), 16, 0, 0);
+    for (int q = 0; q < kGDma; ++q) {
+      const uint32_t off = full ? ro[q] + st * kGK : ro[q] - chunk8(q) + min(st * kGK + chunk8(q), H - 8);
+      __builtin_amdgcn_global_load_lds((q < kGNI ? Wt : ht) + off, reinterpret_cast<void*>(dst_of(base, q)), 16, 0, 0);
     }
   };
-  auto zero_tail = [&](int st) {
+  auto zero_tail = [&](int st) __attribute__((always_inline)) {
     if (st < nfull) return;
     unsigned char* base = gsm + (st & 1) * kGStageBytes;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (st * kGK + c8[q] >= H)
-        *reinterpret_cast<u32x4*>(base + (q < 4 ? 0 : kGOpBytes) + (w * 4 + (q & 3)) * 1024 + lane * 16) =
-            u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < kGDma; ++q)
+      if (st * kGK + chunk8(q) >= H) *reinterpret_cast<u32x4*>(dst_of(base, q) + lane * 16) = u32x4{0u, 0u, 0u, 0u};
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[kGNI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kGNI; ++i)
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0.f;
 
-  // fragment registers, two sets: fa = 4 W_lm row groups, fb = 2 h row groups
-  u32x4 fa[2][4], fb[2][2];
+  // fragment registers, two sets: fa = 5 W_lm row groups, fb = 2 h row groups
+  u32x4 fa[2][kGNI], fb[2][2];
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(gsm));
-  uint32_t aw[4], ah[4];                                // per 16-deep step ks
+  // per 16-deep step ks; the h rows sit a wave-uniform distance from the W_lm
+  // rows (both first rows are multiples of 16, so the swizzle is the same)
+  uint32_t aw[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    aw[ks] = lds0 + swz(wv * 128 + l32, 2 * ks + hi);
-    ah[ks] = lds0 + kGOpBytes + swz(wm * 64 + l32, 2 * ks + hi);
-  }
-  auto load_frag = [&](int set, uint32_t so, int ks) {
-    const uint32_t pw = aw[ks] + so, ph = ah[ks] + so;
+  for (int ks = 0; ks < 4; ++ks) aw[ks] = lds0 + swz(wv * 32 * kGNI + l32, 2 * ks + hi);
+  const uint32_t dh = __builtin_amdgcn_readfirstlane(kGWBytes + swz(wm * 64, 0) - swz(wv * 32 * kGNI, 0));
+  auto load_frag = [&](int set, uint32_t so, int ks) __attribute__((always_inline)) {
+    const uint32_t pw = aw[ks] + so, ph = pw + dh;
     asm volatile("ds_read_b128 %0, %1" : "=v"(fa[set][0]) : "v"(pw));
     asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(fa[set][1]) : "v"(pw));
     asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(fa[set][2]) : "v"(pw));
     asm volatile("ds_read_b128 %0, %1 offset:12288" : "=v"(fa[set][3]) : "v"(pw));
+    asm volatile("ds_read_b128 %0, %1 offset:16384" : "=v"(fa[set][4]) : "v"(pw));
     asm volatile("ds_read_b128 %0, %1" : "=v"(fb[set][0]) : "v"(ph));
     asm volatile("ds_read_b128 %0, %1 offset:4096" : "=v"(fb[set][1]) : "v"(ph));
   };
   // at most N of this wave's LDS reads outstanding; the set's registers pass
   // through the wait so that its MFMAs cannot be scheduled above it
 #define DSPARK_GEMM_WAIT_SET(set, n)                                                               \
-  asm volatile("s_waitcnt lgkmcnt(%6)"                                                             \
-               : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]), "+v"(fb[set][0]), \
-                 "+v"(fb[set][1])                                                                  \
+  asm volatile("s_waitcnt lgkmcnt(%7)"                                                             \
+               : "+v"(fa[set][0]), "+v"(fa[set][1]), "+v"(fa[set][2]), "+v"(fa[set][3]), "+v"(fa[set][4]), \
+                 "+v"(fb[set][0]), "+v"(fb[set][1])                                                \
                : "n"(n))
-  auto mma = [&](int set) {
+  auto mma = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kGNI; ++i)
 #pragma unroll
       for (int jn = 0; jn < 2; ++jn)
         acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fb[set][jn]), as_bf16x8(fa[set][i]),
@@ -164,15 +181,15 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
   for (int st = 0; st < nst; ++st) {
     const uint32_t so = (st & 1) * kGStageBytes;
     load_frag(1, so, 1);
-    DSPARK_GEMM_WAIT_SET(0, 6);
+    DSPARK_GEMM_WAIT_SET(0, kGNI + 2);
     mma(0);
     __builtin_amdgcn_sched_barrier(0);
     load_frag(0, so, 2);
-    DSPARK_GEMM_WAIT_SET(1, 6);
+    DSPARK_GEMM_WAIT_SET(1, kGNI + 2);
     mma(1);
     __builtin_amdgcn_sched_barrier(0);
     load_frag(1, so, 3);
-    DSPARK_GEMM_WAIT_SET(0, 6);
+    DSPARK_GEMM_WAIT_SET(0, kGNI + 2);
     mma(0);
     __builtin_amdgcn_sched_barrier(0);
     DSPARK_GEMM_WAIT_SET(1, 0);
@@ -192,8 +209,8 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
 #undef DSPARK_GEMM_WAIT_SET
   // D[m][v] of a 32 x 32 tile: lane column v = l32, rows 8 (e / 4) + 4 hi + e % 4
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int vr = wv * 128 + i * 32 + l32;
+  for (int i = 0; i < kGNI; ++i) {
+    const int vr = wv * 32 * kGNI + i * 32 + l32;
     if (v0 + vr >= V) continue;
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
@@ -248,7 +265,7 @@ hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, in
     return launch_lm_head_skinny(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w), M, H, V, U, s);
   } else {
     const int VT = static_cast<int>((V + kGV - 1) / kGV), MT = static_cast<int>((M + kGM - 1) / kGM);
-    const int grid = 8 * ((VT + 7) / 8) * MT;
+    const int grid = 8 * ((VT * MT + 7) / 8);
     // opt in to more than 64 KB of dynamic LDS (a host-side attribute call)
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(lm_head_gemm_bf16),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -21,10 +21,10 @@ pytestmark = pytest.mark.gpu
     (1, 256, 5000, "bf16"),       # skinny path, ragged vocabulary tail
     (7, 296, 5000, "bf16"),       # skinny, K not a multiple of 32
     (12, 2560, 1000, "bf16"),     # skinny, largest M that keeps h in 64 KB of LDS
-    (13, 2560, 1000, "bf16"),     # tiled path, ragged M
+    (13, 2560, 1000, "bf16"),     # tiled path, ragged M, fewer tiles than XCDs
     (130, 296, 5000, "bf16"),     # tiled, ragged M/K/V tiles
     (448, 320, 3000, "bf16"),
-    (600, 136, 2104, "bf16"),     # several row tiles, K tail, vocabulary tail inside an XCD group
+    (600, 136, 2104, "bf16"),     # several row tiles, K tail, vocabulary tail; 21 tiles over 8 XCD runs
     (257, 8, 264, "bf16"),        # tiled, one K stage that is all tail, one row past a tile
     (270, 64, 1032, "bf16"),      # tiled, exactly one full K stage
     # more tiles than compute units (several rounds of workgroups per XCD)
