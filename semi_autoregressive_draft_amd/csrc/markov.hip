@@ -833,35 +833,72 @@ template <> struct SegRows<float> {
   }
 };
 
-// value of rank k-1 among the n values of `vals` (ties ranked by position);
-// every thread calls it, the result is broadcast through `out`
-__device__ void kth_largest(const float* vals, int n, int k, float* out) {
-  for (int i = threadIdx.x; i < n; i += kTopkThreads) {
-    const float m = vals[i];
-    int rank = 0;
-#pragma unroll 16
-    for (int u = 0; u < n; ++u) rank += (vals[u] > m) || (vals[u] == m && u < i);
-    if (rank == k - 1) *out = m;
-  }
-  if (threadIdx.x == 0 && n < k) *out = kNegInf;
-  __syncthreads();
+// Order-preserving map of floats to unsigned keys (and back).
+__device__ __forceinline__ unsigned float_key(float x) {
+  const unsigned u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(unsigned o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+// The k-th largest of the n values of `vals` (16-byte aligned in LDS), NaNs
+// left out; -inf when fewer than k values are not NaN.  It is the smallest
+// value m with fewer than k values strictly above it, so each thread counts,
+// for its own values, the values above them (one compare each, four per
+// 16-byte LDS read at the same address in every lane), and the values that
+// qualify meet in an LDS minimum over order-preserving keys.  kmin (~0u) and
+// kcnt (0) are set before the barrier that precedes the call.  Every thread
+// calls it and gets the result.
+__device__ float kth_largest(const float* vals, int n, int k, unsigned* kmin, int* kcnt) {
+  constexpr int kBatch = 8;                   // 16-byte reads in flight
+  const f32x4* v4 = reinterpret_cast<const f32x4*>(vals);
+  const int n4 = n >> 2;
+  for (int i0 = 0; i0 < n; i0 += kTopkThreads) {
+    const int i = i0 + static_cast<int>(threadIdx.x);
+    const float m = i < n ? vals[i] : __builtin_nanf("");
+    const bool live = m == m;
+    const unsigned long long bal = __ballot(live);
+    if ((threadIdx.x & (kWave - 1)) == 0 && bal) atomicAdd(kcnt, __popcll(bal));
+    if (!live) continue;
+    int gt = 0, u = 0;
+    for (; u + kBatch <= n4; u += kBatch) {
+      f32x4 q[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) q[t] = v4[u + t];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) gt += q[t][c] > m;
+    }
+    for (u *= 4; u < n; ++u) gt += vals[u] > m;
+    if (gt < k) atomicMin(kmin, float_key(m));
+  }
+  __syncthreads();
+  return *kcnt < k ? kNegInf : key_float(*kmin);
+}
+
+// The second launch bound is an occupancy target (waves per SIMD): 7 for the
+// BmT form, whose 70 registers let 7 workgroups per CU hold a 256 x 7 grid at
+// once, and 4 for the others (their register counts).  Without it the
+// compiler kept the argument block in over 100 scalar registers and spilled a
+// third of them into vector lanes inside the loops (C5: 20% slower).
 template <typename WT, bool BMT = false>
-__global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile_cols) {
+__global__ __launch_bounds__(kTopkThreads, BMT ? 7 : 4) void markov_topk(StepArgs a, int tile_cols) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x, j = blockIdx.y;
   const int k = a.topk;
   const size_t row = static_cast<size_t>(b) * a.gamma + j;
   __shared__ float arow_s[kMaxRank];
-  __shared__ float tmax[kTopkThreads];
+  __shared__ __align__(16) float tmax[kTopkThreads];
   __shared__ int tiles[kTileCap];
   __shared__ int c1s[kCand1Cap];
-  __shared__ float c1v[kCand1Cap];
+  __shared__ __align__(16) float c1v[kCand1Cap];
   __shared__ int c2s[kCand2Cap];
-  __shared__ float ev[kCand2Cap * kSeg];
+  __shared__ __align__(16) float ev[kCand2Cap * kSeg];
   __shared__ int counter[3];
-  __shared__ float theta[2];
+  __shared__ unsigned kmin[2];             // k-th largest searches: minimum key, values counted
+  __shared__ int kcnt[2];
   __shared__ float selv[kMaxTopk];
   __shared__ int seli[kMaxTopk];
 
@@ -889,9 +926,10 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
   for (int p = kKeep * kTopkThreads + tid; p < a.Pn; p += kTopkThreads) mt = fmaxf(mt, pm[p]);
   tmax[tid] = mt;
   if (tid < 3) counter[tid] = 0;
+  if (tid < 2) { kmin[tid] = ~0u; kcnt[tid] = 0; }
   __syncthreads();
-  kth_largest(tmax, kTopkThreads, k, &theta[0]);
-  const float th00 = theta[0];
+  // threads past the partial count hold -inf (no tile): rank among the others
+  const float th00 = kth_largest(tmax, min(kTopkThreads, a.Pn), k, &kmin[0], &kcnt[0]);
   // tiles that can hold a segment >= theta00
 #pragma unroll
   for (int u = 0; u < kKeep; ++u) {
@@ -932,8 +970,7 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
     const int n1 = counter[1];
     overflow = n1 > kCand1Cap;
     if (!overflow) {
-      kth_largest(c1v, n1, k, &theta[1]);
-      const float th = theta[1];
+      const float th = kth_largest(c1v, n1, k, &kmin[1], &kcnt[1]);
       for (int i = tid; i < n1; i += kTopkThreads) {
         if (c1v[i] >= th) {
           const int slot = atomicAdd(&counter[2], 1);
@@ -1015,8 +1052,11 @@ __global__ __launch_bounds__(kTopkThreads) void markov_topk(StepArgs a, int tile
           int rank = 0;
           for (int c = 0; c < n2; ++c) {       // 8 columns of one candidate segment per step
             const int v0 = c2s[c] * kSeg;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(&ev[c * kSeg]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(&ev[c * kSeg + 4]);
 #pragma unroll
-            for (int i = 0; i < kSeg; ++i) rank += ranks_before(ev[c * kSeg + i], v0 + i, x, ix);
+            for (int i = 0; i < 4; ++i)
+              rank += ranks_before(lo[i], v0 + i, x, ix) + ranks_before(hi[i], v0 + 4 + i, x, ix);
           }
           if (rank < k) { selv[rank] = x; seli[rank] = ix; }
         }

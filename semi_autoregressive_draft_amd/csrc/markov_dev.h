@@ -29,8 +29,9 @@ __device__ __forceinline__ float best_value(unsigned long long key) {
 }
 
 // (value descending, index ascending): the order of the top-k candidates
+// (bitwise, not short-circuit, operators: no branch per comparison)
 __device__ __forceinline__ bool ranks_before(float xa, int ia, float xb, int ib) {
-  return xa > xb || (xa == xb && ia < ib);
+  return (xa > xb) | ((xa == xb) & (ia < ib));
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
