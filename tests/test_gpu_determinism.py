@@ -47,7 +47,8 @@ def test_lm_head_is_deterministic(M, H, V):
                                    (300, 4096, 0),    # many rows, each read once
                                    (160, 30004, 0),   # many rows, ragged chunks
                                    (5, 20000, 16),    # candidates, one launch
-                                   (300, 4096, 16)])  # candidates, one workgroup per row
+                                   (300, 4096, 16),   # candidates, one workgroup per row
+                                   (64, 30004, 16)])  # candidates at 448 rows, one workgroup per row
 def test_overlap_tau_is_deterministic(N, V, k):
     dev = require_gpu()
     g = synth.GAMMA

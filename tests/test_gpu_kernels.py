@@ -466,7 +466,12 @@ def test_overlap_many_rows_time_out_is_reported(monkeypatch):
     _check_tau((alpha.cpu().numpy(), tau.cpu().numpy(), acc.cpu().numpy(), float(mean.cpu()[0])), a_raw, valid)
 
 
-@pytest.mark.parametrize("k,N", [(16, 5), (64, 5), (16, 20), (16, 300)])
+@pytest.mark.parametrize("k,N", [
+    (16, 5), (64, 5), (16, 20),
+    (16, 64),     # 448 rows: one workgroup per row (not the split path)
+    (16, 200),    # 1400 rows, one tau block
+    (16, 300),    # two tau blocks
+])
 def test_overlap_candidates_parity(k, N):
     V = 5000
     teacher, _ = synth.overlap_inputs(N, V, 1.0, seed=3)
@@ -480,6 +485,23 @@ def test_overlap_candidates_parity(k, N):
     a_raw = o.overlap_sparse(t64, idx, prob.astype(np.float64))
     assert a_raw.max() > 0.05
     _check_tau(got, a_raw, None)
+
+
+@pytest.mark.parametrize("N", [64, 200])
+def test_overlap_candidates_with_invalid_rows(N):
+    # one workgroup per row: invalid rows get alpha 0, and tau and the
+    # aggregates skip them
+    V, k = 5000, 16
+    teacher, _ = synth.overlap_inputs(N, V, 1.0, seed=6)
+    teacher = teacher * 3.0
+    t64 = teacher.astype(np.float64)
+    idx = np.argsort(-t64, axis=-1)[..., :k].astype(np.int32)
+    _, prob = synth.candidates(N, V, k, seed=6)
+    valid = synth.validity(N, seed=6, trunc_frac=0.4, n_dummy=1)
+    got = _run_overlap(teacher.astype(np.float32), idx=idx, prob=prob, valid=valid)
+    a_raw = o.overlap_sparse(t64, idx, prob.astype(np.float64))
+    assert a_raw.max() > 0.05
+    _check_tau(got, a_raw, valid)
 
 
 @pytest.mark.parametrize("N", [5, 300])           # single launch; one workgroup per row
