@@ -276,9 +276,11 @@ dspark_status_t dspark_markov_propose_head_workspace(int32_t head, int64_t B, in
  * top-k recomputes the U~ of its candidate 8-column segments from Bm; read
  * from Bm [r, V], each segment takes 16 bytes of each of r rows, i.e. r whole
  * cache lines for 16 useful bytes per line.  With this larger workspace,
- * dspark_markov_propose and dspark_markov_propose_head first transpose Bm
- * into the workspace's tail and the recompute reads whole row pieces, when
- * that moves fewer bytes (large B; bf16, topk > 0, not the resident chain).
+ * dspark_markov_propose and dspark_markov_propose_head store the transposed
+ * Bm in the workspace's tail (from position 0's step kernel, or by a copy
+ * kernel when that step cannot, e.g. with logits_out) and the recompute reads
+ * whole row pieces, when that moves fewer bytes (large B; bf16, topk > 0, not
+ * the resident chain).
  * The results are the same top-k (up to float32 summation order in the
  * recomputed values).
  *

@@ -305,8 +305,11 @@ dspark_status_t propose_impl(
   // a workspace that also holds the transposed Bm (see the _bmt query) turns on
   // the contiguous top-k recompute where it pays off
   const size_t bmt = markov_bmt_bytes(r, V);
-  if (!resident && topk > 0 && bf16 && ws_bytes >= need + bmt && markov_bmt_pays(B, gamma, V, r, topk))
+  if (!resident && topk > 0 && bf16 && ws_bytes >= need + bmt && markov_bmt_pays(B, gamma, V, r, topk)) {
     a.BmT = static_cast<char*>(ws) + need;
+    // the step kernel stores BmT at position 0 (its store-only variant has no dump)
+    a.bmt_step = !logits_out && markov_bmt_in_step(a.sample != 0, a.B, a.gamma, a.r, a.V);
+  }
   a.Mrow = mtab;
   a.tile_cols = resident ? 64 : markov_tile_cols(bf16, a.sample, a.B, a.gamma, a.r, a.V);
   a.resident = resident;

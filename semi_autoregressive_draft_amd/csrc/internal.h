@@ -58,6 +58,7 @@ struct StepArgs {
   const void* A;           // [V, r]
   const void* Bm;          // [r, V]
   const void* BmT;         // [V, r] copy of Bm (bf16) for the top-k recompute, or NULL
+  int bmt_step;            // 1: the wide step kernel of position 0 stores BmT (no transpose launch; no dump)
   int B, gamma, V, r, j;
   int sample;              // 0 greedy, 1 Gumbel-max
   float inv_temp;
@@ -96,6 +97,9 @@ hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s);
 // per-position path
 size_t markov_bmt_bytes(int64_t r, int64_t V);
 bool markov_bmt_pays(int64_t B, int64_t gamma, int64_t V, int64_t r, int32_t topk);
+// whether position 0 of the per-position chain runs the wide step kernel, which
+// then stores BmT itself
+bool markov_bmt_in_step(bool sample, int B, int gamma, int r, int V);
 
 hipError_t launch_lm_head(const void* h, const void* w, bool bf16, int64_t M, int64_t H,
                           int64_t V, float* U, hipStream_t s);

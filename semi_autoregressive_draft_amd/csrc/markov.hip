@@ -384,7 +384,8 @@ constexpr uint32_t kDropOffset = 0x80000000u;   // past every resource: the acce
 // given; each tile's U~ is stored to logits_out and nothing else is kept).
 // DUMP = false: the chain with no U~ dump requested (no dump store is issued;
 // a store to a resource of no records still costs its issue).
-template <int NCH, int CPW, bool SAMPLE, bool STATS = true, bool DUMP = true>
+// BMT: position 0 of a chain whose top-k reads BmT: the step also stores it.
+template <int NCH, int CPW, bool SAMPLE, bool STATS = true, bool DUMP = true, bool BMT = false>
 __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
   extern __shared__ __align__(16) unsigned char wide_lds[];
   u32x4* const ops = reinterpret_cast<u32x4*>(wide_lds);   // [2][NCH + 1][4][64] B operands
@@ -414,6 +415,13 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
     uoff[ii] = (row * V + tb * kWideCols + 4 * n) * 4;
     soff[ii] = (row * a.S + tb * (kWideCols / kSeg) + (n >> 1)) * 4;
   }
+  // BMT: the step also stores the transposed Bm (BmT [V, r]) for the top-k
+  // recompute: the B-operand pieces it builds anyway are 16-byte pieces of
+  // BmT rows (column 4n + c, rows 32q + 8g ..).  Request group y stores the
+  // chunks q with q % ny == y, so the stores spread evenly.
+  constexpr bool bmt_w = STATS && BMT;
+  const __amdgpu_buffer_rsrc_t bmt_rsrc =
+      bmt_w ? buf_rsrc(a.BmT, static_cast<size_t>(a.r) * V * 2) : buf_rsrc(a.U, 0);
   // Bm rows of this wave's chunks (chunks w, w + nw, ...; NCH <= CPW * nw)
   uint32_t boff[CPW][8];
 #pragma unroll
@@ -439,7 +447,7 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
         raw[s][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(bm_rsrc, static_cast<int>(boff[s][i]),
                                                                                  tof, 0));
   };
-  auto store_bm = [&](int buf, u32x2 (&raw)[CPW][8]) __attribute__((always_inline)) {
+  auto store_bm = [&](int buf, u32x2 (&raw)[CPW][8], int tt) __attribute__((always_inline)) {
     u32x4* const o = ops + buf * (NCH + 1) * 4 * kWave;
 #pragma unroll
     for (int s = 0; s < CPW; ++s) {
@@ -453,6 +461,17 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
       transpose_rows4(raw[s], op);
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[(q * 4 + c) * kWave + lane] = op[c];
+      if constexpr (bmt_w) {
+        // tile tt's own rows only (a look-ahead past the range reloads the
+        // last tile), one request group per chunk; columns past V fall
+        // outside the resource and are dropped
+        const bool mine = tt <= last && q < NCH && q % static_cast<int>(gridDim.y) == static_cast<int>(blockIdx.y);
+        const uint32_t base = ((static_cast<uint32_t>(tb + tt) * kWideCols + 4 * n) * a.r + 32 * q + 8 * g) * 2;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, op[c]), bmt_rsrc,
+                                                 static_cast<int>(mine ? base + c * a.r * 2 : kDropOffset), 0, 0);
+      }
     }
   };
 
@@ -598,13 +617,13 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
       mma(1, acc1);                                     // tile t + 1
       epi(mask_tag, t, acc0, u0);
       load_u(t + 2, u0);
-      store_bm(0, ra);                                  // tile t + 2
+      store_bm(0, ra, t + 2);                           // tile t + 2
       load_bm(t + 4, ra);
       lds_barrier();
       mma(0, acc0);                                     // tile t + 2
       epi(mask_tag, t + 1, acc1, u1);
       load_u(t + 3, u1);
-      store_bm(1, rb);                                  // tile t + 3
+      store_bm(1, rb, t + 3);                           // tile t + 3
       load_bm(t + 5, rb);
       lds_barrier();
     };
@@ -612,11 +631,11 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
     load_u(0, u0);
     load_bm(1, rb);
     load_u(1, u1);
-    store_bm(0, ra);                                    // tile 0
+    store_bm(0, ra, 0);                                 // tile 0
     load_bm(2, ra);
     lds_barrier();
     mma(0, acc0);
-    store_bm(1, rb);                                    // tile 1
+    store_bm(1, rb, 1);                                 // tile 1
     load_bm(3, rb);
     lds_barrier();
     for (; t + 2 < nt; t += 2) pair(Whole{});
@@ -626,24 +645,24 @@ __global__ __launch_bounds__(512) void markov_step_wide(StepArgs a, int tpw) {
       mma(1, acc1);                                     // tile t + 1
       epi(mask_tag, t, acc0, u0);
       load_u(t + 2, u0);
-      store_bm(0, ra);                                  // tile t + 2
+      store_bm(0, ra, t + 2);                           // tile t + 2
       load_bm(t + 3, ra);
       lds_barrier();
       mma(0, acc0);                                     // tile t + 2
       epi(mask_tag, t + 1, acc1, u1);
       load_u(t + 3, u1);
-      store_bm(1, ra);                                  // tile t + 3
+      store_bm(1, ra, t + 3);                           // tile t + 3
       load_bm(t + 4, ra);
       lds_barrier();
     };
     load_bm(0, ra);
     load_u(0, u0);
-    store_bm(0, ra);                                    // tile 0
+    store_bm(0, ra, 0);                                 // tile 0
     load_bm(1, ra);
     load_u(1, u1);
     lds_barrier();
     mma(0, acc0);
-    store_bm(1, ra);                                    // tile 1
+    store_bm(1, ra, 1);                                 // tile 1
     load_bm(2, ra);
     lds_barrier();
     for (; t + 2 < nt; t += 2) pair(Whole{});
@@ -1258,13 +1277,15 @@ struct WidePlan {
   // the same kernel without the U~ dump stores (a chain with no dump): the
   // same registers and LDS, so the plan (from fn's occupancy) holds for it
   void (*launch_nodump)(const StepArgs&, int, dim3, int, hipStream_t);
+  // no dump, and the step stores BmT as well (position 0 of a top-k chain)
+  void (*launch_nodump_bmt)(const StepArgs&, int, dim3, int, hipStream_t);
   int nw, ny, tpw, nx, gx;
   size_t lds;
 };
 
-template <int NCH, int CPW, bool SAMPLE, bool STATS, bool DUMP = true>
+template <int NCH, int CPW, bool SAMPLE, bool STATS, bool DUMP = true, bool BMT = false>
 static void launch_wide_kernel(const StepArgs& a, int tpw, dim3 grid, int nw, hipStream_t s) {
-  hipLaunchKernelGGL((markov_step_wide<NCH, CPW, SAMPLE, STATS, DUMP>), grid, dim3(kWave * nw),
+  hipLaunchKernelGGL((markov_step_wide<NCH, CPW, SAMPLE, STATS, DUMP, BMT>), grid, dim3(kWave * nw),
                      wide_ops_bytes(NCH) + (SAMPLE ? kWideSeedBytes : 0), s, a, tpw);
 }
 
@@ -1275,6 +1296,7 @@ static void pick_wide(bool sample, bool stats, WidePlan* p) {
     p->fn = reinterpret_cast<const void*>(&markov_step_wide<NCH, CPW, false, false>);
     p->launch = &launch_wide_kernel<NCH, CPW, false, false>;
     p->launch_nodump = p->launch;
+    p->launch_nodump_bmt = nullptr;
     p->lds = wide_ops_bytes(NCH);
     return;
   }
@@ -1283,6 +1305,8 @@ static void pick_wide(bool sample, bool stats, WidePlan* p) {
   p->launch = sample ? &launch_wide_kernel<NCH, CPW, true, true> : &launch_wide_kernel<NCH, CPW, false, true>;
   p->launch_nodump = sample ? &launch_wide_kernel<NCH, CPW, true, true, false>
                             : &launch_wide_kernel<NCH, CPW, false, true, false>;
+  p->launch_nodump_bmt = sample ? &launch_wide_kernel<NCH, CPW, true, true, false, true>
+                                : &launch_wide_kernel<NCH, CPW, false, true, false, true>;
   p->lds = wide_ops_bytes(NCH) + (sample ? kWideSeedBytes : 0);
 }
 
@@ -1339,13 +1363,20 @@ int markov_tile_cols(bool bf16, bool sample, int B, int gamma, int r, int V) {
   return wide_plan(bf16, sample, B, gamma, r, V, &p) ? p.tpw * kWideCols : kMarkovTile;
 }
 
+bool markov_bmt_in_step(bool sample, int B, int gamma, int r, int V) {
+  WidePlan p{};
+  return static_cast<size_t>(r) * V * 2 < (static_cast<size_t>(1) << 31) && wide_plan(true, sample, B, gamma, r, V, &p);
+}
+
 hipError_t launch_markov_position(StepArgs a, bool bf16, hipStream_t s) {
   a.Pn = partial_count(a);
   if (bf16) {
     WidePlan p{};
     if (wide_plan(bf16, a.sample, a.B, a.gamma, a.r, a.V, &p)) {
       if (p.tpw * kWideCols != a.tile_cols) return hipErrorInvalidValue;   // plan changed since tile_cols was set
-      (a.logits_out ? p.launch : p.launch_nodump)(a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
+      if (a.bmt_step && a.logits_out) return hipErrorInvalidValue;      // the BmT variant has no dump
+      (a.logits_out ? p.launch : a.bmt_step && a.j == 0 ? p.launch_nodump_bmt : p.launch_nodump)(
+          a, p.tpw, dim3(p.gx, p.ny), p.nw, s);
     } else if (a.r % 128 == 0) {
       // small batches split r over waves so that a step has enough waves in flight
       launch_bf16<1, 4>(a, s);
@@ -1415,9 +1446,11 @@ hipError_t launch_markov_finish(StepArgs a, bool bf16, hipStream_t s) {
   }
   if (a.topk == 0) return hipSuccess;
   if (bf16 && a.BmT) {
-    const dim3 tg((a.V + kTrC - 1) / kTrC, a.r / kTrR);
-    hipLaunchKernelGGL(transpose_bm_bf16, tg, dim3(256), 0, s, static_cast<const uint16_t*>(a.Bm),
-                       static_cast<uint16_t*>(const_cast<void*>(a.BmT)), a.r, a.V);
+    if (!a.bmt_step) {                     // else position 0's step kernel stored it
+      const dim3 tg((a.V + kTrC - 1) / kTrC, a.r / kTrR);
+      hipLaunchKernelGGL(transpose_bm_bf16, tg, dim3(256), 0, s, static_cast<const uint16_t*>(a.Bm),
+                         static_cast<uint16_t*>(const_cast<void*>(a.BmT)), a.r, a.V);
+    }
     hipLaunchKernelGGL((markov_topk<uint16_t, true>), grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
   } else if (bf16)
     hipLaunchKernelGGL(markov_topk<uint16_t>, grid, dim3(kTopkThreads), 0, s, a, a.tile_cols);
