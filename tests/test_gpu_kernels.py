@@ -143,18 +143,24 @@ def test_markov_resident_chain(B, V, r, T, topk, wg, monkeypatch):
 ])
 def test_markov_topk_with_transposed_bm(B, V, r, T, topk):
     # the larger workspace turns on the transposed-Bm recompute of the top-k
-    # candidates; the smaller one keeps the strided recompute: both exact
+    # candidates (the copy stored by position 0's step kernel when no dump is
+    # asked for, else by the copy kernel); the smaller one keeps the strided
+    # recompute: all exact, and the same top-k
     dev = require_gpu()
     U, anchor, A, Bm = _markov_case(B, V, r, "bf16", seed=9)
     seeds = np.arange(B, dtype=np.uint64) * 31 + 5 if T > 0 else None
     small = bd.dspark_markov_propose_workspace(B, 7, V, topk)
     big = bd.dspark_markov_propose_workspace_bmt(bd.HEAD_LINEAR, B, 7, V, r, bd.BF16, topk)
     assert big >= small + r * V * 2
-    for n in (big, small):
+    ids = []
+    for n, dump in ((big, True), (big, False), (small, False)):
         ws = torch.zeros(n, dtype=torch.uint8, device=dev)
-        gpu = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=4, topk=topk, ws=ws)
+        gpu = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=4, topk=topk, ws=ws, dump=dump)
         check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"),
-                    temperature=T, seeds=seeds, offset=4, topk=topk)
+                    temperature=T, seeds=seeds, offset=4, topk=topk, check_logits=dump)
+        ids.append(gpu["topk_idx"])
+    # the same BmT either way: the same recompute, bit for bit
+    assert np.array_equal(ids[0], ids[1])
 
 
 def test_markov_workspace_is_left_ready_for_the_next_call(monkeypatch):
