@@ -901,7 +901,8 @@ __device__ float kth_largest(const float* vals, int n, int k, unsigned* kmin, in
 // BmT form, whose 70 registers let 7 workgroups per CU hold a 256 x 7 grid at
 // once, and 4 for the others (their register counts).  Without it the
 // compiler kept the argument block in over 100 scalar registers and spilled a
-// third of them into vector lanes inside the loops (C5: 20% slower).
+// third of them into vector lanes inside the loops (20% slower at B = 256,
+// V = 151936).
 template <typename WT, bool BMT = false>
 __global__ __launch_bounds__(kTopkThreads, BMT ? 7 : 4) void markov_topk(StepArgs a, int tile_cols) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
