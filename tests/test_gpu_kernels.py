@@ -255,6 +255,30 @@ def test_markov_nan_row_keeps_gathers_inside_the_table(B, V, r, topk):
     assert np.all((ids >= -1) & (ids < V))
 
 
+@pytest.mark.parametrize("gamma,B,V,r,T,topk,dump", [
+    (1, 40, 3000, 256, 0.0, 16, False),   # one position: the step that stores BmT is the whole chain
+    (3, 40, 2008, 64, 0.8, 8, True),      # sampled, ragged last tile, with the dump
+    (16, 20, 3000, 128, 0.0, 16, False),  # the longest block
+    (1, 2, 5000, 256, 0.0, 16, False),    # small batch (resident chain where it applies)
+    (16, 3, 5000, 256, 1.0, 0, True),
+])
+def test_markov_other_block_lengths(gamma, B, V, r, T, topk, dump, chain_path):
+    # blocks of other lengths than 7, through both chain paths and the
+    # transposed-Bm workspace
+    dev = require_gpu()
+    U = synth.base_logits(B, V, gamma=gamma, seed=31)
+    A = synth.normal((V, r), 0.25, 31, synth.TID_A, "bf16")
+    Bm = synth.normal((r, V), 0.25, 31, synth.TID_BM, "bf16")
+    anchor = synth.rng(31, synth.TID_ANCHOR).integers(0, V, size=B).astype(np.int32)
+    seeds = np.arange(B, dtype=np.uint64) * 5 + 2 if T > 0 else None
+    n = (bd.dspark_markov_propose_workspace_bmt(bd.HEAD_LINEAR, B, gamma, V, r, bd.BF16, topk) if topk
+         else bd.dspark_markov_propose_workspace(B, gamma, V, topk))
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+    gpu = _run_markov(U, anchor, A, Bm, "bf16", T=T, seeds=seeds, offset=1, topk=topk, dump=dump, ws=ws)
+    check_chain(gpu, U.astype(np.float64), anchor, o.to_f64(A, "bf16"), o.to_f64(Bm, "bf16"),
+                temperature=T, seeds=seeds, offset=1, topk=topk)
+
+
 @pytest.mark.parametrize("T", [0.0, 0.8])
 def test_markov_without_dump_matches_with_dump(T):
     # the per-position wide step has a variant that issues no U~ dump stores
