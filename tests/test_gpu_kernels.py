@@ -414,6 +414,38 @@ def test_overlap_dense_parity(sigma, N, V, resident, monkeypatch):
     assert got[1][-1] == 0.0                                   # padding block sentinel
 
 
+@pytest.mark.parametrize("gamma,N,V,mode", [
+    (1, 9, 5000, "dense"),        # one launch
+    (16, 3, 5000, "dense"),       # one launch, the longest block
+    (3, 40, 3000, "dense"),       # split rows
+    (16, 80, 2000, "dense"),      # many rows, each read once (1280 rows)
+    (1, 400, 3000, "candidates"),  # one workgroup per row, one position per block
+    (16, 30, 3000, "candidates"),  # one workgroup per row from 384 rows (480 rows)
+    (3, 10, 3000, "candidates"),  # one launch
+])
+def test_overlap_other_block_lengths(gamma, N, V, mode):
+    # tau, accept_rate@i and tau_mean over blocks of other lengths than 7, on
+    # every overlap path, with invalid slots and an all-invalid last block
+    teacher, draft = synth.overlap_inputs(N, V, 1.0, gamma=gamma, seed=8)
+    g = np.random.default_rng(8)
+    valid = (g.random((N, gamma)) > 0.2).astype(np.uint8)
+    valid[-1] = 0
+    t64 = teacher.astype(np.float64)
+    if mode == "dense":
+        got = _run_overlap(teacher, draft=draft, valid=valid)
+        a_raw, _ = o.overlap_dense(t64, draft.astype(np.float64))
+    else:
+        k = 16
+        teacher = teacher * 3.0
+        t64 = teacher.astype(np.float64)
+        idx = np.argsort(-t64, axis=-1)[..., :k].astype(np.int32)
+        _, prob = synth.candidates(N, V, k, gamma=gamma, seed=8)
+        got = _run_overlap(teacher.astype(np.float32), idx=idx, prob=prob, valid=valid)
+        a_raw = o.overlap_sparse(t64, idx, prob.astype(np.float64))
+    _check_tau(got, a_raw, valid)
+    assert got[1][-1] == 0.0                                   # all-invalid block sentinel
+
+
 def test_overlap_identical_rows_give_tau_eight():
     teacher, _ = synth.overlap_inputs(3, 4096, 1.0, seed=2)
     alpha, tau, acc, mean = _run_overlap(teacher, draft=teacher.copy())
