@@ -337,15 +337,17 @@ def test_lm_head_confidence_parity(B, gamma, H, V, wdtype):
 
 
 # ----------------------------------------------------------------------------- S5
-@pytest.mark.parametrize("B,H,r,wdtype,with_wm", [
-    (5, 2560, 256, "bf16", True),
-    (1, 256, 32, "f32", False),
-    (256, 2560, 256, "bf16", False),
-    (3, 100, 48, "f32", True),
+@pytest.mark.parametrize("B,H,r,wdtype,with_wm,gamma", [
+    (5, 2560, 256, "bf16", True, 7),
+    (1, 256, 32, "f32", False, 7),
+    (256, 2560, 256, "bf16", False, 7),
+    (3, 100, 48, "f32", True, 7),
+    (4, 2560, 256, "bf16", True, 1),     # one position per block
+    (9, 2560, 256, "bf16", False, 16),   # the longest block: survival over 16 slots
 ])
-def test_confidence_parity(B, H, r, wdtype, with_wm):
+def test_confidence_parity(B, H, r, wdtype, with_wm, gamma):
     dev = require_gpu()
-    gamma, V = 7, 777
+    V = 777
     h = synth.normal((B, gamma, H), 1.0, 2, synth.TID_H, wdtype)
     w_c = synth.normal((H,), 0.02, 2, synth.TID_WC, wdtype)
     w_m = synth.normal((r,), 0.5, 2, synth.TID_WM, wdtype) if with_wm else None
@@ -733,6 +735,26 @@ def test_compute_loss_parity(N, sigma, conf_decay):
     target = g.integers(0, V, (N, gamma)).astype(np.int32)
     conf = g.standard_normal((N, gamma)).astype(np.float32)
     valid = synth.validity(N, seed=3, trunc_frac=0.4, n_dummy=1 if N > 1 else 0)
+    per, losses = _run_loss(draft, teacher, target, conf, valid, conf_decay)
+    want_per, want_losses = o.compute_loss(draft.astype(np.float64), teacher.astype(np.float64), target,
+                                           conf.astype(np.float64), valid, conf_decay=conf_decay)
+    _check_loss(per, losses, want_per, want_losses)
+
+
+@pytest.mark.parametrize("gamma,N,conf_decay", [
+    (1, 9, False),      # 9 rows: the one-launch overlap path
+    (16, 5, True),      # 80 rows: chunked rows, decay weights over 16 positions
+    (16, 100, False),   # 1600 rows: many rows, each read once
+    (3, 30, True),
+])
+def test_compute_loss_other_block_lengths(gamma, N, conf_decay):
+    V = 3000
+    teacher, draft = synth.overlap_inputs(N, V, 1.0, gamma=gamma, seed=4)
+    g = np.random.default_rng([4, gamma])
+    target = g.integers(0, V, (N, gamma)).astype(np.int32)
+    conf = g.standard_normal((N, gamma)).astype(np.float32)
+    valid = (g.random((N, gamma)) > 0.25).astype(np.uint8)
+    valid[-1] = 0
     per, losses = _run_loss(draft, teacher, target, conf, valid, conf_decay)
     want_per, want_losses = o.compute_loss(draft.astype(np.float64), teacher.astype(np.float64), target,
                                            conf.astype(np.float64), valid, conf_decay=conf_decay)
