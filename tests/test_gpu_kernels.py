@@ -872,18 +872,21 @@ def test_verify_accepts_everything_when_draft_equals_target():
 
 
 # ----------------------------------------------------------------------------- sequential-head variants
-@pytest.mark.parametrize("head,B,V,r,wdtype,T,topk", [
-    ("silu", 1, 4000, 256, "bf16", 0.0, 16),     # narrow step (r split over waves), top-16
-    ("silu", 40, 3000, 256, "bf16", 1.0, 0),     # wide step, sampled
-    ("gated", 5, 3000, 128, "bf16", 0.0, 8),
-    ("gated", 33, 2008, 64, "bf16", 0.7, 16),    # wide step, sampled, top-16, ragged tile
-    ("gated", 3, 1000, 48, "f32", 0.0, 5),       # float32 tables
-    ("silu", 2, 1000, 32, "f32", 1.0, 0),
+@pytest.mark.parametrize("head,B,V,r,wdtype,T,topk,gamma", [
+    ("silu", 1, 4000, 256, "bf16", 0.0, 16, 7),     # narrow step (r split over waves), top-16
+    ("silu", 40, 3000, 256, "bf16", 1.0, 0, 7),     # wide step, sampled
+    ("gated", 5, 3000, 128, "bf16", 0.0, 8, 7),
+    ("gated", 33, 2008, 64, "bf16", 0.7, 16, 7),    # wide step, sampled, top-16, ragged tile
+    ("gated", 3, 1000, 48, "f32", 0.0, 5, 7),       # float32 tables
+    ("silu", 2, 1000, 32, "f32", 1.0, 0, 7),
+    ("gated", 20, 3000, 128, "bf16", 0.0, 16, 1),   # one position per block
+    ("silu", 3, 2000, 256, "bf16", 0.8, 8, 16),     # the longest block
 ])
-def test_markov_head_variants_parity(head, B, V, r, wdtype, T, topk):
+def test_markov_head_variants_parity(head, B, V, r, wdtype, T, topk, gamma):
     dev = require_gpu()
-    gamma, H, seed = 7, 96, 29
+    H, seed = 96, 29
     U, anchor, A, Bm = _markov_case(B, V, r, wdtype, seed=seed)
+    U = synth.base_logits(B, V, gamma=gamma, seed=seed)
     h = synth.normal((B, gamma, H), 1.0, seed, synth.TID_H, wdtype)
     W_g = synth.normal((r, H + r), 0.1, seed, synth.TID_WG, wdtype)
     seeds = np.arange(B, dtype=np.uint64) + np.uint64(11) if T > 0 else None
@@ -911,18 +914,21 @@ def test_markov_head_variants_parity(head, B, V, r, wdtype, T, topk):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("B,V,r,H,wdtype,T,topk", [
-    (5, 3000, 128, 96, "bf16", 0.0, 8),          # MFMA state and output kernels
-    (33, 2008, 64, 96, "bf16", 0.7, 16),         # wide step, sampled, top-16, ragged request block
-    (1, 4000, 256, 200, "bf16", 0.0, 16),        # one request, full rank
-    (3, 1000, 32, 90, "bf16", 0.0, 0),           # H % 8 != 0: one workgroup per request
-    (3, 1000, 48, 96, "f32", 0.0, 5),            # float32 tables
+@pytest.mark.parametrize("B,V,r,H,wdtype,T,topk,gamma", [
+    (5, 3000, 128, 96, "bf16", 0.0, 8, 7),          # MFMA state and output kernels
+    (33, 2008, 64, 96, "bf16", 0.7, 16, 7),         # wide step, sampled, top-16, ragged request block
+    (1, 4000, 256, 200, "bf16", 0.0, 16, 7),        # one request, full rank
+    (3, 1000, 32, 90, "bf16", 0.0, 0, 7),           # H % 8 != 0: one workgroup per request
+    (3, 1000, 48, 96, "f32", 0.0, 5, 7),            # float32 tables
+    (4, 3000, 128, 96, "bf16", 0.0, 8, 16),         # the state carried over 16 positions
+    (20, 2000, 64, 96, "bf16", 0.0, 16, 1),         # one position: the state starts at zero
 ])
-def test_markov_rnn_head_parity(B, V, r, H, wdtype, T, topk):
+def test_markov_rnn_head_parity(B, V, r, H, wdtype, T, topk, gamma):
     dev = require_gpu()
-    gamma, seed = 7, 31
-    print(f"rnn head B={B} V={V} r={r} H={H} {wdtype} T={T} topk={topk}", flush=True)
+    seed = 31
+    print(f"rnn head B={B} V={V} r={r} H={H} {wdtype} T={T} topk={topk} gamma={gamma}", flush=True)
     U, anchor, A, Bm = _markov_case(B, V, r, wdtype, seed=seed)
+    U = synth.base_logits(B, V, gamma=gamma, seed=seed)
     h = synth.normal((B, gamma, H), 1.0, seed, synth.TID_H, wdtype)
     W = synth.normal((3 * r, 2 * r + H), 0.1, seed, synth.TID_WG, wdtype)
     seeds = np.arange(B, dtype=np.uint64) + np.uint64(5) if T > 0 else None
