@@ -18,14 +18,27 @@ namespace dspark {
 // bytes per output than a square 256 one, and 475 x 7 tiles at V = 151936,
 // M = 1792 fill 13 whole rounds of the 256 CUs.)
 //
-// Operands move global -> LDS by DMA (global_load_lds_dwordx4: each wave
+// Operands move global -> LDS by DMA (buffer_load_dwordx4 ... lds: each wave
 // instruction fills 1 KB of LDS in lane order) into a ring of 2 stages of
 // 72 KB.  A stage holds 320 rows of W_lm and 256 rows of h, 128 bytes (one
 // whole cache line) per row; LDS lines of 256 bytes hold two rows, and 16-byte
 // chunk slots are XOR-swizzled by the line index mod 8, so that the DMA writes
 // stay contiguous and the MFMA operand reads (16 consecutive rows per 16
-// lanes) touch every bank once.  The DMA of stage st + 2 is issued right after
-// the barrier that ends stage st.
+// lanes) touch every bank once.  The DMA goes through buffer resources over
+// the tile's valid rows: a lane's offset is one of two per-lane values (even
+// and odd blocks) plus a uniform block and stage offset, and rows past V or M
+// read 0 (their outputs are never stored).
+//
+// A wave cannot issue past a DMA instruction until the memory pipeline takes
+// it, and a stage's 72 KB drain at the L2's pace (~1 KB per 20-35 cycles per
+// CU).  So waves 0-3 issue every DMA instruction of their SIMD (their own
+// blocks and those of wave w + 4), while waves 4-7 run their MFMAs from the
+// barrier on; the W_lm rows of stage st + 2 go out right after the barrier
+// that ends stage st, its h rows two MFMA groups into stage st + 1.  (With
+// every wave issuing its own 9 instructions after the barrier, the second
+// wave of each SIMD reached the barrier ~1,500 cycles after the first, and a
+// stage took ~4,400 cycles for 2,560 cycles of MFMA work per SIMD; split this
+// way it takes ~3,250.)
 //
 // Fragment reads are software-pipelined over two register sets: the reads of
 // 16-deep step ks + 1 are in flight while the MFMAs of step ks run.  They are
@@ -74,7 +87,7 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
   if (tile >= s1) return;                               // whole workgroup
   const int vt = tile / MT, mt = tile - vt * MT;
   const int v0 = vt * kGV, m0 = mt * kGM;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = w & 1, wm = w >> 1;                    // 2 x 4 waves
   const int l32 = lane & 31, hi = lane >> 5;
   const int nst = (H + kGK - 1) / kGK;
@@ -87,46 +100,75 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
   // to them (at most 320 rows, so 32 bits hold them)
   const uint16_t* const Wt = W + static_cast<size_t>(v0) * H;
   const uint16_t* const ht = h + static_cast<size_t>(m0) * H;
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(Wt, static_cast<size_t>(min(kGV, V - v0)) * H * 2);
+  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(ht, static_cast<size_t>(min(kGM, M - m0)) * H * 2);
 
-  // DMA: wave w fills 1 KB blocks kGNI w .. kGNI w + kGNI - 1 of the W_lm
-  // block (instructions q < kGNI) and blocks 4w .. 4w + 3 of the h block.
-  // Lane i of an instruction writes byte 16 i of its block, i.e. line
-  // 4 blk + i / 16, slot i % 16, and loads the (row, chunk) the swizzle places
-  // there.  Rows past V or M read the last valid row (their outputs are never
-  // stored); H % 8 == 0, so every chunk is whole, and chunks past H are
-  // clamped into the row and zeroed once landed.
-  auto block_of = [&](int q) __attribute__((always_inline)) { return q < kGNI ? w * kGNI + q : w * 4 + (q - kGNI); };
-  auto chunk8 = [&](int q) __attribute__((always_inline)) {
-    const int line = block_of(q) * 4 + (lane >> 4);
-    return 8 * (((lane & 15) ^ (line & 7)) & 7);
-  };
-  uint32_t ro[kGDma];                                   // element offset of the lane's (row, chunk)
+  // DMA: block b (1 KB) of the W_lm or h part of a stage holds rows
+  // 8b .. 8b + 7.  Lane i of its instruction writes byte 16 i of the block,
+  // i.e. line 4b + i / 16, slot i % 16, and loads the (row, chunk) the swizzle
+  // places there: row 8b + 2 (i / 16) + slot' / 8 and chunk slot' % 8 with
+  // slot' = (i % 16) ^ (line % 8), where line % 8 depends on b only through
+  // b % 2.  H % 8 == 0, so every chunk is whole; in a stage with a K tail,
+  // chunks past H are clamped into the row and zeroed once landed.
+  uint32_t vo[2];                                       // byte offset in an even / odd block
+  int c8[2];                                            // its first column in the stage
 #pragma unroll
-  for (int q = 0; q < kGDma; ++q) {
-    const bool isW = q < kGNI;
-    const int line = block_of(q) * 4 + (lane >> 4);
+  for (int p = 0; p < 2; ++p) {
+    const int line = 4 * p + (lane >> 4);
     const int slot = (lane & 15) ^ (line & 7);
-    const int row = min(line * 2 + (slot >> 3), (isW ? V - v0 : M - m0) - 1);
-    ro[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(H) + 8 * (slot & 7);
+    c8[p] = 8 * (slot & 7);
+    vo[p] = static_cast<uint32_t>(((2 * (lane >> 4) + (slot >> 3)) * H + c8[p]) * 2);
   }
-  auto dst_of = [&](unsigned char* base, int q) __attribute__((always_inline)) {
-    return base + (q < kGNI ? 0 : kGWBytes) + block_of(q) * 1024;
+  // the lane's byte offset of stage st in a block of parity p
+  auto stage_ofs = [&](int st, int p) __attribute__((always_inline)) {
+    const int k = st < nfull ? st * kGK : min(st * kGK + c8[p], H - 8) - c8[p];
+    return vo[p] + static_cast<uint32_t>(k * 2);
   };
-  auto issue = [&](int st) __attribute__((always_inline)) {
+  auto dma = [&](unsigned char* base, bool isW, int blk, uint32_t ofs) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        isW ? rw : rh, (__attribute__((address_space(3))) void*)(base + (isW ? 0 : kGWBytes) + blk * 1024), 16,
+        ofs + static_cast<uint32_t>(16 * blk * H), 0, 0, 0);
+  };
+  // waves 0-3 only: the blocks of wave w and of wave w + 4 (same parity)
+  auto issue_w = [&](int st) __attribute__((always_inline)) {
+    if (w >= 4) return;
     unsigned char* base = gsm + (st & 1) * kGStageBytes;
-    const bool full = st < nfull;
+    const uint32_t o0 = stage_ofs(st, 0), o1 = stage_ofs(st, 1);
+    const uint32_t oe = (w & 1) ? o1 : o0, od = (w & 1) ? o0 : o1;   // block w kGNI + q: parity (w + q) % 2
 #pragma unroll
-    for (int q = 0; q < kGDma; ++q) {
-      const uint32_t off = full ? ro[q] + st * kGK : ro[q] - chunk8(q) + min(st * kGK + chunk8(q), H - 8);
-      __builtin_amdgcn_global_load_lds((q < kGNI ? Wt : ht) + off, reinterpret_cast<void*>(dst_of(base, q)), 16, 0, 0);
-    }
+    for (int q = 0; q < kGNI; ++q) dma(base, true, w * kGNI + q, q & 1 ? od : oe);
+#pragma unroll
+    for (int q = 0; q < kGNI; ++q) dma(base, true, (w + 4) * kGNI + q, q & 1 ? od : oe);
+  };
+  auto issue_h = [&](int st) __attribute__((always_inline)) {
+    if (w >= 4) return;
+    unsigned char* base = gsm + (st & 1) * kGStageBytes;
+    const uint32_t o0 = stage_ofs(st, 0), o1 = stage_ofs(st, 1);  // block 4 w + q: parity q % 2
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma(base, false, w * 4 + q, q & 1 ? o1 : o0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma(base, false, (w + 4) * 4 + q, q & 1 ? o1 : o0);
   };
   auto zero_tail = [&](int st) __attribute__((always_inline)) {
-    if (st < nfull) return;
+    if (st < nfull || w >= 4) return;
     unsigned char* base = gsm + (st & 1) * kGStageBytes;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int q = 0; q < kGDma; ++q)
-      if (st * kGK + chunk8(q) >= H) *reinterpret_cast<u32x4*>(dst_of(base, q) + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < kGNI; ++q) {
+      const int b0 = w * kGNI + q, b1 = b0 + 4 * kGNI;    // same parity
+      if (st * kGK + c8[b0 & 1] >= H) {
+        *reinterpret_cast<u32x4*>(base + b0 * 1024 + lane * 16) = z;
+        *reinterpret_cast<u32x4*>(base + b1 * 1024 + lane * 16) = z;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b0 = w * 4 + q, b1 = b0 + 16;
+      if (st * kGK + c8[b0 & 1] >= H) {
+        *reinterpret_cast<u32x4*>(base + kGWBytes + b0 * 1024 + lane * 16) = z;
+        *reinterpret_cast<u32x4*>(base + kGWBytes + b1 * 1024 + lane * 16) = z;
+      }
+    }
   };
 
   f32x16 acc[kGNI][2];
@@ -172,11 +214,15 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
                                                              acc[i][jn], 0, 0, 0);
   };
 
-  issue(0);
+  issue_w(0);
+  issue_h(0);
   wait_vmcnt<0>();
   zero_tail(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (nst > 1) issue(1);
+  if (nst > 1) {
+    issue_w(1);
+    issue_h(1);
+  }
   load_frag(0, 0, 0);
   for (int st = 0; st < nst; ++st) {
     const uint32_t so = (st & 1) * kGStageBytes;
@@ -188,6 +234,8 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
     DSPARK_GEMM_WAIT_SET(1, kGNI + 2);
     mma(1);
     __builtin_amdgcn_sched_barrier(0);
+    // the h rows of stage st + 1 (its W_lm rows went out after the last barrier)
+    if (st >= 1 && st + 1 < nst) issue_h(st + 1);
     load_frag(1, so, 3);
     DSPARK_GEMM_WAIT_SET(0, kGNI + 2);
     mma(0);
@@ -199,7 +247,7 @@ __global__ __launch_bounds__(kGThreads, 1) void lm_head_gemm_bf16(
       wait_vmcnt<0>();
       zero_tail(st + 1);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (st + 2 < nst) issue(st + 2);
+      if (st + 2 < nst) issue_w(st + 2);
       load_frag(0, so ^ kGStageBytes, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
