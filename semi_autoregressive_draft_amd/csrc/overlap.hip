@@ -137,8 +137,12 @@ __device__ float candidate_overlap(const OverlapArgs& a, int row, float Lt, int 
 }
 
 // ---- one workgroup per row (many rows) ------------------------------------
-__global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
-  constexpr int NW = kOvThreads / kWave;
+// TR threads per row: 512, or 128 when there are enough rows for every CU to
+// hold several of them at once (one round of workgroups instead of ~1.75
+// rounds of 512-thread ones at 1,792 rows: ~3% off the pass)
+template <int TR>
+__global__ __launch_bounds__(TR) void overlap_rows(OverlapArgs a) {
+  constexpr int NW = TR / kWave;
   __shared__ LseState red_l[NW];
   __shared__ float red_f[NW];
   const int row = blockIdx.x, tid = threadIdx.x;
@@ -152,23 +156,23 @@ __global__ __launch_bounds__(kOvThreads) void overlap_rows(OverlapArgs a) {
   float total;
   if (a.draft) {
     const f32x4* dp = reinterpret_cast<const f32x4*>(a.draft + row * V);
-    const LseState lt = range_lse<false>(tp, tid, n4, kOvThreads);
-    const LseState ld = range_lse<false>(dp, tid, n4, kOvThreads);
+    const LseState lt = range_lse<false>(tp, tid, n4, TR);
+    const LseState ld = range_lse<false>(dp, tid, n4, TR);
     const LseState rt = block_lse_state<NW>(lt, red_l);
     const LseState rd = block_lse_state<NW>(ld, red_l);
     const float Lt = rt.m + logf(rt.s), Ld = rd.m + logf(rd.s);
     // second pass walks down, to reuse what the first touched last
-    const int last = (n4 - 1 - tid) >= 0 ? tid + ((n4 - 1 - tid) / kOvThreads) * kOvThreads : -1;
-    const float s = range_min_sum<true>(tp, dp, last, 0, n4, kOvThreads, Lt, Ld);
+    const int last = (n4 - 1 - tid) >= 0 ? tid + ((n4 - 1 - tid) / TR) * TR : -1;
+    const float s = range_min_sum<true>(tp, dp, last, 0, n4, TR, Lt, Ld);
     total = block_sum<NW>(s, red_f);
     if (tid == 0) {
       if (a.lse_draft) a.lse_draft[row] = Ld;
       if (a.ov_sum) a.ov_sum[row] = total;
     }
   } else {
-    const LseState lt = range_lse<true>(tp, tid, n4, kOvThreads);   // the row is read once
+    const LseState lt = range_lse<true>(tp, tid, n4, TR);   // the row is read once
     const LseState rt = block_lse_state<NW>(lt, red_l);
-    total = block_sum<NW>(candidate_overlap(a, row, rt.m + logf(rt.s), tid, kOvThreads), red_f);
+    total = block_sum<NW>(candidate_overlap(a, row, rt.m + logf(rt.s), tid, TR), red_f);
   }
   if (tid == 0) a.alpha[row] = fminf(fmaxf(total, 0.f), 1.f);
 }
@@ -962,7 +966,8 @@ hipError_t launch_overlap_tau(OverlapArgs a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(overlap_rows_resident_fold, dim3((rows + 255) / 256), dim3(256), 0, s, a);
   } else if (a.nchunk <= 1 || (!a.draft && rows >= kCandRowsPath)) {
-    hipLaunchKernelGGL(overlap_rows, dim3(rows), dim3(kOvThreads), 0, s, a);
+    if (rows >= 4 * device_info().cus) hipLaunchKernelGGL(overlap_rows<128>, dim3(rows), dim3(128), 0, s, a);
+    else hipLaunchKernelGGL(overlap_rows<kOvThreads>, dim3(rows), dim3(kOvThreads), 0, s, a);
   } else {
     const int n4 = a.V / 4;
     a.chunk4 = (n4 + a.nchunk - 1) / a.nchunk;
