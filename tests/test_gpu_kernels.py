@@ -30,6 +30,9 @@ pytestmark = pytest.mark.gpu
     # more tiles than compute units (several rounds of workgroups per XCD)
     (600, 136, 50000, "bf16"),    # 3 row tiles, K tail
     (300, 200, 40008, "bf16"),    # ragged M, K tail, vocabulary tail
+    # 8 row tiles (the last 208 rows), a K tail of 8 and a last vocabulary tile of 8 columns: the
+    # DMA of waves 0-3 (own and partner blocks), its tail zeroing and the range-checked rows at once
+    (2000, 264, 40008, "bf16"),
 ])
 def test_lm_head_parity(M, H, V, wdtype):
     dev = require_gpu()
